@@ -1,0 +1,447 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA fp32 recurrent-state decode step on one MI355X.
+
+Headline: single-token decode at B=64, H=32, dk=dv=128 (the batch-64 end of the
+pages' batch 1-64 decode, "Hyper Optimizing Kimi K3 in vLLM"), over a 256-slot
+fp32 state cache (512 MiB). Each step runs on the next of four disjoint
+64-slot tables, so a slot is revisited only after 384 MiB of other state has
+streamed through the 256 MB Infinity Cache: the state comes from HBM.
+
+Prints one JSON line on stdout:
+  value         decode steps per second (K steps bracketed by synchronizations)
+  roofline      HBM bytes the step must move per launch / the kernel's average
+                duration (HIP events around each launch, on its stream) vs 8 TB/s
+  cpu_baseline  the CPU oracle on this host's cores, on a bounded sample
+  breakdown     the batch sweep, the B=1 1024-step latency path (plain launches and
+                one captured HIP graph), the speculative verify + commit in both
+                buffer modes and the mixed gated batch, each with its own
+                algorithmic bytes and GB/s
+Progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "KDA decode steps/s + achieved HBM GB/s (fp32 state), B=1..64, H=32, dk=dv=128"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "kda_decode_b64_counters.txt")
+KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_98_amd", "csrc", "kda.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- bytes
+
+def decode_bytes(B, H, dk, dv):
+    """HBM bytes one single-token step must move: state read + write, inputs, output, slot ids."""
+    per_head = 2 * dk * dv * 4 + (2 * dk + dv) * 2 + dk * 4 + 4 + dv * 4
+    return B * H * per_head + B * 4
+
+
+def verify_bytes(n_tok, B, H, dk, dv, mode, T_max):
+    """Verify: state read once per row, per-token inputs and outputs, plus the replay copy
+    (REPLAY) or the per-token state writes (PER_POSITION)."""
+    state = B * H * dk * dv * 4
+    tok_in = n_tok * H * ((2 * dk + dv) * 2 + dk * 4 + 4)
+    tok_out = n_tok * H * dv * 4
+    meta = B * 4 + (B + 1) * 4
+    if mode == 0:
+        extra = n_tok * H * (dk * 2 + dv * 2 + dk * 4 + 4)
+    else:
+        extra = n_tok * H * dk * dv * 4
+    return state + tok_in + tok_out + meta + extra
+
+
+def mixed_verify_bytes(seqlens, H, dk, dv):
+    """Mixed batch with the output gate: single-token rows read and write their state in place;
+    longer rows read it once and copy their inputs to the replay buffer; every token reads its
+    inputs and gate and writes its output."""
+    seqlens = np.asarray(seqlens)
+    n_tok = int(seqlens.sum())
+    singles = int(np.sum(seqlens == 1))
+    multi = int(np.sum(seqlens > 1))
+    multi_tok = int(seqlens[seqlens > 1].sum())
+    state = (2 * singles + multi) * H * dk * dv * 4
+    per_tok = H * ((2 * dk + dv) * 2 + dk * 4 + 4 + dv * 2 + dv * 4)
+    replay = multi_tok * H * (dk * 2 + dv * 2 + dk * 4 + 4)
+    return state + n_tok * per_tok + replay + len(seqlens) * 8 + 4 + dv * 4
+
+
+def commit_bytes(accepted, H, dk, dv, mode):
+    live = int(np.count_nonzero(accepted))
+    state = live * H * dk * dv * 4
+    if mode == 0:
+        toks = int(np.sum(accepted)) * H * (dk * 2 + dv * 2 + dk * 4 + 4)
+        return 2 * state + toks + len(accepted) * 8
+    return 2 * state + len(accepted) * 8
+
+
+# ----------------------------------------------------------------------------- GPU helpers
+
+class Dev:
+    def __init__(self):
+        import torch
+
+        self.torch = torch
+        self.dev = torch.device("cuda", 0)
+
+    def bf(self, a):
+        t = self.torch
+        return t.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(self.dev).view(t.bfloat16)
+
+    def f(self, a):
+        return self.torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(self.dev)
+
+    def i(self, a):
+        return self.torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(self.dev)
+
+    def sync(self):
+        self.torch.cuda.synchronize()
+
+    def event(self):
+        return self.torch.cuda.Event(enable_timing=True)
+
+
+def timed_region(D, launch, n):
+    """Run launch(i) for i < n between two events; returns total ms."""
+    D.sync()
+    a, b = D.event(), D.event()
+    a.record()
+    for i in range(n):
+        launch(i)
+    b.record()
+    D.sync()
+    return a.elapsed_time(b)
+
+
+def per_launch_ms(D, launch, n):
+    """Average duration of one launch: an event pair around each launch on the launch stream."""
+    evs = [(D.event(), D.event()) for _ in range(n)]
+    D.sync()
+    for i in range(n):
+        evs[i][0].record()
+        launch(i)
+        evs[i][1].record()
+    D.sync()
+    return float(np.mean([s.elapsed_time(e) for s, e in evs]))
+
+
+# ----------------------------------------------------------------------------- workloads
+
+def decode_setup(D, K, synth, B, seed=0):
+    w = synth.make(B, 32, 128, 128, num_slots=256, state_std=0.02, seed=seed, name=f"decode_b{B}")
+    cache = D.f(w.cache)
+    tables = [D.i(t) for t in w.slot_tables]
+    x = dict(q=D.bf(w.q[0]), k=D.bf(w.k[0]), v=D.bf(w.v[0]), alpha=D.f(w.alpha[0]), beta=D.f(w.beta[0]))
+    out = D.torch.empty(B, 32, 128, device=D.dev)
+
+    def launch(i, hot=False):
+        K.kda_decode_step(cache, tables[0 if hot else i % len(tables)], x["q"], x["k"], x["v"], x["alpha"],
+                          x["beta"], out)
+
+    return w, launch, (cache, tables, x, out)
+
+
+def headline(D, K, synth, steps, warmup):
+    B = 64
+    w, launch, keep = decode_setup(D, K, synth, B)
+    nbytes = decode_bytes(B, 32, 128, 128)
+    log(f"headline: B={B} H=32 d=128, {len(w.slot_tables)} rotating slot tables, {steps} steps after {warmup} warmup")
+    for i in range(warmup):
+        launch(i)
+    D.sync()
+    total_ms = timed_region(D, launch, steps)
+    ms_step = total_ms / steps
+    kernel_ms = per_launch_ms(D, launch, steps)
+    hot_ms = per_launch_ms(D, lambda i: launch(i, hot=True), steps)
+    log(f"headline: {ms_step * 1e3:.2f} us/step, kernel {kernel_ms * 1e3:.2f} us, "
+        f"{nbytes / kernel_ms / 1e6:.1f} GB/s; same-table (cache-resident) kernel {hot_ms * 1e3:.2f} us")
+    return dict(w=w, ms_step=ms_step, kernel_ms=kernel_ms, hot_ms=hot_ms, bytes=nbytes,
+                tile=K.kda_query_variant(B, 32, 128, 128))
+
+
+def batch_sweep(D, K, synth, reps):
+    rows = []
+    for B in (1, 2, 4, 8, 16, 32, 64):
+        w, launch, keep = decode_setup(D, K, synth, B, seed=B)
+        for i in range(10):
+            launch(i)
+        ms = per_launch_ms(D, launch, reps)
+        total = timed_region(D, launch, reps) / reps
+        nb = decode_bytes(B, 32, 128, 128)
+        tw, th = K.kda_query_variant(B, 32, 128, 128)
+        rows.append(dict(B=B, tile_w=tw, threads=th, us_per_step=round(total * 1e3, 3),
+                         kernel_us=round(ms * 1e3, 3), steps_per_s=round(1e3 / total, 1),
+                         tokens_per_s=round(B * 1e3 / total, 1), algorithmic_bytes=nb,
+                         gbs=round(nb / ms / 1e6, 1), frac_of_peak=round(nb / ms / 1e6 / PEAK_HBM_GBS, 4)))
+        log(f"sweep B={B}: kernel {ms * 1e3:.2f} us, {nb / ms / 1e6:.0f} GB/s, step {total * 1e3:.2f} us")
+        del keep
+    return rows
+
+
+def b1_latency(D, K, synth):
+    torch = D.torch
+    w = synth.make_workload("b1_latency")
+    cache = D.f(w.cache)
+    slots = D.i(w.slot_ids)
+    q, k, v = D.bf(w.q), D.bf(w.k), D.bf(w.v)
+    al, be = D.f(w.alpha), D.f(w.beta)
+    out = torch.empty(w.steps, 1, 32, 128, device=D.dev)
+
+    def step(s):
+        K.kda_decode_step(cache, slots, q[s], k[s], v[s], al[s], be[s], out[s])
+
+    for s in range(16):
+        step(s)
+    D.sync()
+    plain_ms = timed_region(D, step, w.steps) / w.steps
+    kernel_ms = per_launch_ms(D, step, 256)
+    # the same 1024 launches captured once in a HIP graph and replayed
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            for s in range(w.steps):
+                step(s)
+    torch.cuda.current_stream().wait_stream(stream)
+    graph.replay()
+    D.sync()
+    a, b = D.event(), D.event()
+    a.record()
+    graph.replay()
+    b.record()
+    D.sync()
+    graph_ms = a.elapsed_time(b) / w.steps
+    log(f"b1_latency: plain {plain_ms * 1e3:.2f} us/step, kernel {kernel_ms * 1e3:.2f} us, "
+        f"graph {graph_ms * 1e3:.2f} us/step")
+    return dict(B=1, steps=w.steps, us_per_step_plain=round(plain_ms * 1e3, 3),
+                kernel_us=round(kernel_ms * 1e3, 3), us_per_step_graph=round(graph_ms * 1e3, 3),
+                tile_w=K.kda_query_variant(1, 32, 128, 128)[0])
+
+
+def spec_verify(D, K, synth, reps):
+    torch = D.torch
+    w = synth.make_workload("spec_verify")
+    cache = D.f(w.cache)
+    slots, cu, acc = D.i(w.slot_ids), D.i(w.cu_seqlens), D.i(w.accepted)
+    x = dict(q=D.bf(w.q[0]), k=D.bf(w.k[0]), v=D.bf(w.v[0]), alpha=D.f(w.alpha[0]), beta=D.f(w.beta[0]))
+    out = torch.empty(w.n_tok, 32, 128, device=D.dev)
+    H, d, T = 32, 128, w.T_max
+    rb = dict(k=torch.zeros(w.B, T, H, d, dtype=torch.bfloat16, device=D.dev),
+              v=torch.zeros(w.B, T, H, d, dtype=torch.bfloat16, device=D.dev),
+              alpha=torch.zeros(w.B, T, H, d, device=D.dev), beta=torch.zeros(w.B, T, H, device=D.dev))
+    draft = torch.zeros(w.B, T, H, d, d, device=D.dev)
+    res = {}
+    for mode, name in ((0, "replay"), (1, "per_position")):
+        # verify leaves the slots alone; the commit rewrites the accepted state, so each
+        # repetition starts from a fresh copy of the committed cache
+        base = cache.clone()
+
+        def verify(i):
+            K.kda_verify_chunk(cache, slots, cu, T, x["q"], x["k"], x["v"], x["alpha"], x["beta"], out,
+                               mode=mode, replay=rb if mode == 0 else None, draft=draft if mode == 1 else None)
+
+        def commit(i):
+            K.kda_replay_commit(cache, slots, cu, acc, T, w.n_tok, mode=mode,
+                                replay=rb if mode == 0 else None, draft=draft if mode == 1 else None)
+
+        for i in range(5):
+            verify(i)
+        v_ms = per_launch_ms(D, verify, reps)
+        c_times = []
+        for r in range(reps):
+            cache.copy_(base)
+            c_times.append(per_launch_ms(D, commit, 1))
+        c_ms = float(np.mean(c_times))
+        cache.copy_(base)
+        vb = verify_bytes(w.n_tok, w.B, H, d, d, mode, T)
+        cb = commit_bytes(w.accepted, H, d, d, mode)
+        res[name] = dict(verify_us=round(v_ms * 1e3, 3), verify_bytes=vb, verify_gbs=round(vb / v_ms / 1e6, 1),
+                         commit_us=round(c_ms * 1e3, 3), commit_bytes=cb, commit_gbs=round(cb / c_ms / 1e6, 1),
+                         total_us=round((v_ms + c_ms) * 1e3, 3), total_bytes=vb + cb)
+        log(f"spec_verify {name}: verify {v_ms * 1e3:.2f} us ({vb / v_ms / 1e6:.0f} GB/s), "
+            f"commit {c_ms * 1e3:.2f} us ({cb / c_ms / 1e6:.0f} GB/s)")
+    res["tile_w"] = K.kda_query_variant(w.B, H, d, d, T_max=T)[0]
+    return res
+
+
+def mixed(D, K, synth, reps):
+    torch = D.torch
+    w = synth.make_workload("mixed")
+    cache = D.f(w.cache)
+    base = cache.clone()
+    slots, cu, acc = D.i(w.slot_ids), D.i(w.cu_seqlens), D.i(w.accepted)
+    x = dict(q=D.bf(w.q[0]), k=D.bf(w.k[0]), v=D.bf(w.v[0]), alpha=D.f(w.alpha[0]), beta=D.f(w.beta[0]),
+             gate=D.bf(w.gate[0]))
+    out = torch.empty(w.n_tok, 32, 128, device=D.dev)
+    H, d, T = 32, 128, w.T_max
+    rb = dict(k=torch.zeros(w.B, T, H, d, dtype=torch.bfloat16, device=D.dev),
+              v=torch.zeros(w.B, T, H, d, dtype=torch.bfloat16, device=D.dev),
+              alpha=torch.zeros(w.B, T, H, d, device=D.dev), beta=torch.zeros(w.B, T, H, device=D.dev))
+
+    def verify(i):
+        K.kda_verify_chunk(cache, slots, cu, T, x["q"], x["k"], x["v"], x["alpha"], x["beta"], out,
+                           mode=0, t1_inplace=True, replay=rb, gate=x["gate"], eps=1e-6)
+
+    def commit(i):
+        K.kda_replay_commit(cache, slots, cu, acc, T, w.n_tok, mode=0, replay=rb)
+
+    for i in range(3):
+        verify(i)
+    v_ms = per_launch_ms(D, verify, reps)
+    c_times = []
+    for r in range(reps):
+        cache.copy_(base)
+        verify(0)
+        c_times.append(per_launch_ms(D, commit, 1))
+    c_ms = float(np.mean(c_times))
+    vb = mixed_verify_bytes(w.seqlens, H, d, d)
+    cb = commit_bytes(w.accepted, H, d, d, 0)
+    log(f"mixed: verify {v_ms * 1e3:.2f} us ({vb / v_ms / 1e6:.0f} GB/s), commit {c_ms * 1e3:.2f} us")
+    return dict(verify_us=round(v_ms * 1e3, 3), verify_bytes=vb, verify_gbs=round(vb / v_ms / 1e6, 1),
+                commit_us=round(c_ms * 1e3, 3), commit_bytes=cb, commit_gbs=round(cb / c_ms / 1e6, 1))
+
+
+def copy_calibration(D, nbytes=256 << 20, reps=5):
+    """A plain device copy of known size (for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)."""
+    src = D.torch.empty(nbytes // 4, dtype=D.torch.float32, device=D.dev).normal_()
+    dst = D.torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    D.sync()
+    log(f"copy calibration: {reps} copies of {nbytes} bytes")
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(w, budget_s=12.0, max_steps=2000):
+    """The CPU oracle (as it stands) on the headline workload, rotating the same slot tables."""
+    import oracle
+
+    threads = max(1, min(len(os.sched_getaffinity(0)), 16))
+    cache = w.cache.copy()
+    n = 0
+    t0 = time.perf_counter()
+    while n < max_steps:
+        table = w.slot_tables[n % len(w.slot_tables)]
+        oracle.decode(cache, table, w.q[0], w.k[0], w.v[0], w.alpha[0], w.beta[0], nthreads=threads)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    log(f"cpu baseline: {n} oracle steps in {el:.1f} s on {threads} threads")
+    return dict(value=round(n / el, 3), unit="steps/s", cores=threads, kind="oracle",
+                sample=f"{n} single-token steps of the B=64 H=32 d=128 workload (4 rotating slot tables), "
+                       f"{el:.1f} s wall; fp64 arithmetic with fp32 state")
+
+
+# ----------------------------------------------------------------------------- counters
+
+def stored_traffic(launch_bytes):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel source."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    fields = {}
+    for line in open(COUNTERS_FILE):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            fields[key.strip()] = val.strip()
+    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if fields.get("kernel_source_sha256") != src_hash:
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+# ----------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--no-breakdown", action="store_true", help="headline only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run plain device copies of 256 MiB (for counter scaling)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the KDA state step is independent per (sequence, head), "
+              "so a multi-GPU run is this kernel on each GPU's share with no exchange; "
+              "run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_delta_rule_98_amd as K
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    K.load_library()
+    D = Dev()
+    log(f"device: {torch.cuda.get_device_name(0)}; library {K.LIB_PATH}")
+
+    h = headline(D, K, synth, args.steps, args.warmup)
+    breakdown = None
+    if not args.no_breakdown:
+        breakdown = dict(
+            decode_batch_sweep=batch_sweep(D, K, synth, reps=200),
+            b1_latency_1024_steps=b1_latency(D, K, synth),
+            spec_verify_b16_t8=spec_verify(D, K, synth, reps=50),
+            mixed_b64_gated=mixed(D, K, synth, reps=30),
+            headline_same_table_kernel_us=round(h["hot_ms"] * 1e3, 3),
+        )
+    if args.copy_calibration:
+        copy_calibration(D)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(h["w"])
+
+    achieved = h["bytes"] / h["kernel_ms"] / 1e6
+    line = {
+        "metric": METRIC,
+        "value": round(1e3 / h["ms_step"], 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(h["ms_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "single-token KDA decode, B=64, H=32, dk=dv=128, fp32 state in a 256-slot "
+                               "cache, 4 rotating disjoint slot tables",
+                   "global_batch": 64, "heads": 32, "dk": 128, "dv": 128, "tile_w": h["tile"][0],
+                   "threads": h["tile"][1], "tokens_per_s": round(64 * 1e3 / h["ms_step"], 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": stored_traffic(h["bytes"]),
+                     "algorithmic_bytes_per_launch": h["bytes"],
+                     "kernel_us": round(h["kernel_ms"] * 1e3, 3)},
+        "cpu_baseline": cpu,
+        "breakdown": breakdown,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

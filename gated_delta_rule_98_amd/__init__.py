@@ -1,0 +1,27 @@
+"""KDA fp32 recurrent-state decode, speculative verify and replay commit on MI355X.
+
+The computation lives in hand-written HIP kernels for gfx950 behind the C ABI
+of include/kda.h (libkda.so, built in this directory). This package is the thin
+torch-facing binding of that library.
+"""
+
+from .kda import (  # noqa: F401
+    KDA_DEVERR_ACCEPTED,
+    KDA_DEVERR_SEQLEN,
+    KDA_DEVERR_SLOT,
+    KDA_ERR_ALIGN,
+    KDA_ERR_HIP,
+    KDA_ERR_INVALID,
+    KDA_ERR_UNSUPPORTED,
+    KDA_OK,
+    KDA_PER_POSITION,
+    KDA_REPLAY,
+    LIB_PATH,
+    KdaError,
+    kda_decode_step,
+    kda_query_variant,
+    kda_replay_commit,
+    kda_status_str,
+    kda_verify_chunk,
+    load_library,
+)

@@ -1,0 +1,48 @@
+"""Build the HIP library for gfx950: gated_delta_rule_98_amd/libkda.so.
+
+One translation unit (csrc/kda.hip) holds the kernels and the C ABI of
+include/kda.h. Flags:
+  -ffp-contract=off   no implicit FMA contraction: every FMA is written out, so
+                      all kernels round identically
+  -Xclang -target-feature -Xclang -packed-fp32-ops
+                      no packed fp32 instructions (the host pass warns that it
+                      does not know the feature; that is expected)
+"""
+
+from __future__ import annotations
+
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "kda.hip")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libkda.so")
+ARCH = "gfx950"
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off", "-fno-fast-math",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unknown-warning-option",
+]
+
+
+def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
+    """Compile the library (always recompiles); return its path."""
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, *extra, f"-I{INCLUDE}", SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose and (r.stdout or r.stderr):
+        print(r.stdout, r.stderr)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

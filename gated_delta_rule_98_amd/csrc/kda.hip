@@ -1,0 +1,783 @@
+// kda.hip - HIP kernels for gfx950 and the C ABI declared in include/kda.h.
+//
+// The KDA recurrent-state step (taken as the gated delta rule with per-channel
+// decay; the pages name the KDA recurrent state and its FP32 SSM cache in
+// "Kimi K3 performance optimization in vLLM" and "Kimi K3 vLLM optimization:
+// NVIDIA decode speed-up 1.68x", but do not write the update): per head,
+//     S <- Diag(alpha) S ;  S <- S + beta k (v - S^T k)^T ;  o = S^T q .
+//
+// Work decomposition. One workgroup per (row, head, tile of W value columns).
+// The cache stores each value column's dk key channels contiguously, so a tile
+// is one contiguous span of W * dk floats. A column is owned by 16 lanes (one
+// DPP row): lane r holds key channels 4r..4r+3 and, for dk = 128, also
+// 64+4r..64+4r+3, as float4 registers. S^T k and S^T q are therefore a
+// per-lane partial followed by a 16-lane DPP butterfly that leaves the same
+// bits in every lane, and the rank-1 write needs no exchange at all. A wave
+// covers 4 columns per slab; a lane holds C slabs, so W = 4 * waves * C.
+//
+// Bit-exactness. Every kernel runs the same column engine (token_update /
+// token_readout) with explicit FMAs, the build disables contraction, and the
+// reduction tree depends only on the lane's position in its row. The state
+// after a token is therefore identical bit for bit across decode, verify,
+// both commit modes and every tile width.
+//
+// Memory. At one token per row the step moves 2 * dk * dv * 4 bytes of state
+// per head and ~1.3 KB of inputs, so it is HBM-bound: loads and stores are
+// 128-bit and fully coalesced (each 16-lane row reads 256 contiguous bytes),
+// and all of a lane's state loads are issued before the first use.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "kda.h"
+
+namespace {
+
+constexpr int kMaxT = 16;
+
+struct Args {
+  float *cache;
+  int64_t num_slots, slot_stride;
+  const int32_t *slot_ids;
+  const int32_t *cu;       // packed row offsets [B + 1] (verify; commit may pass NULL)
+  const int32_t *accepted; // commit
+  const uint16_t *q, *k, *v, *gate;
+  const float *alpha, *beta, *weight;
+  float *out;
+  int32_t *dev_err;
+  uint16_t *rk, *rv;
+  float *ralpha, *rbeta, *draft;
+  float eps;
+  int32_t B, H, dv, T_max, n_tok, ntile, mode, t1_inplace;
+};
+
+// ----------------------------------------------------------------------------
+// Column engine
+// ----------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
+
+__device__ __forceinline__ float4 unpack_bf16x4(uint2 u) {
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row. Each stage adds two partial sums that are
+// the same pair in every lane (only the operand order differs), so all 16
+// lanes end with identical bits.
+__device__ __forceinline__ float row16_sum(float x) {
+  x = x + dpp_f32<0xB1>(x);   // quad_perm(1,0,3,2): partner lane ^ 1
+  x = x + dpp_f32<0x4E>(x);   // quad_perm(2,3,0,1): partner lane ^ 2
+  x = x + dpp_f32<0x141>(x);  // row_half_mirror: the other quad of the half-row
+  x = x + dpp_f32<0x140>(x);  // row_mirror: the other half of the row
+  return x;
+}
+
+// This lane's share of dot(s, x) over its key channels, in a fixed order.
+template <int NV>
+__device__ __forceinline__ float lane_dot(const float4 (&s)[NV], const float4 (&x)[NV]) {
+  float p = s[0].x * x[0].x;
+  p = __builtin_fmaf(s[0].y, x[0].y, p);
+  p = __builtin_fmaf(s[0].z, x[0].z, p);
+  p = __builtin_fmaf(s[0].w, x[0].w, p);
+#pragma unroll
+  for (int e = 1; e < NV; ++e) {
+    p = __builtin_fmaf(s[e].x, x[e].x, p);
+    p = __builtin_fmaf(s[e].y, x[e].y, p);
+    p = __builtin_fmaf(s[e].z, x[e].z, p);
+    p = __builtin_fmaf(s[e].w, x[e].w, p);
+  }
+  return p;
+}
+
+// One token on C columns: decay rows by alpha, u = S^T k, S += k * beta (v - u).
+template <int NV, int C>
+__device__ __forceinline__ void token_update(float4 (&s)[C][NV], const float4 (&a)[NV],
+                                             const float4 (&k)[NV], const float (&vj)[C],
+                                             float beta) {
+  float u[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      s[c][e].x = s[c][e].x * a[e].x;
+      s[c][e].y = s[c][e].y * a[e].y;
+      s[c][e].z = s[c][e].z * a[e].z;
+      s[c][e].w = s[c][e].w * a[e].w;
+    }
+    u[c] = lane_dot<NV>(s[c], k);
+  }
+#pragma unroll
+  for (int c = 0; c < C; ++c) u[c] = row16_sum(u[c]);
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const float d = beta * (vj[c] - u[c]);
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      s[c][e].x = __builtin_fmaf(k[e].x, d, s[c][e].x);
+      s[c][e].y = __builtin_fmaf(k[e].y, d, s[c][e].y);
+      s[c][e].z = __builtin_fmaf(k[e].z, d, s[c][e].z);
+      s[c][e].w = __builtin_fmaf(k[e].w, d, s[c][e].w);
+    }
+  }
+}
+
+// Read-out on the updated state: o = S^T q, in every lane of the column's row.
+template <int NV, int C>
+__device__ __forceinline__ void token_readout(const float4 (&s)[C][NV], const float4 (&q)[NV],
+                                              float (&o)[C]) {
+#pragma unroll
+  for (int c = 0; c < C; ++c) o[c] = lane_dot<NV>(s[c], q);
+#pragma unroll
+  for (int c = 0; c < C; ++c) o[c] = row16_sum(o[c]);
+}
+
+// ----------------------------------------------------------------------------
+// Work decomposition
+// ----------------------------------------------------------------------------
+
+struct Unit {
+  int b, h, tile;
+};
+
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup n runs on
+// XCD n % 8). Renumber them so each XCD gets a contiguous range of units: the
+// tiles of one head then share their L2 for the head's k, q, alpha and beta.
+__device__ __forceinline__ Unit unit_of_block(int ntile, int H) {
+  const int n = blockIdx.x, N = gridDim.x;
+  const int xcd = n & 7, local = n >> 3, per = N >> 3, rem = N & 7;
+  const int u = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+  Unit r;
+  r.tile = u % ntile;
+  const int bh = u / ntile;
+  r.h = bh % H;
+  r.b = bh / H;
+  return r;
+}
+
+struct Lane {
+  int r;     // position in the 16-lane row: key channels 4r..4r+3 (+ 64)
+  int col0;  // tile-local value column of slab 0
+  int slab;  // columns per slab = 4 * waves; slab c holds column col0 + c * slab
+};
+
+__device__ __forceinline__ Lane lane_geometry() {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  Lane L;
+  L.r = lane & 15;
+  L.col0 = wave * 4 + (lane >> 4);
+  L.slab = (blockDim.x >> 6) * 4;
+  return L;
+}
+
+__device__ __forceinline__ void report(int32_t *dev_err, const Unit &u, int bit) {
+  if (dev_err && u.tile == 0 && u.h == 0 && threadIdx.x == 0) atomicOr(dev_err, bit);
+}
+
+__device__ __forceinline__ bool row_range(const Args &a, int b, int64_t &row0, int &Tb) {
+  const int32_t c0 = a.cu[b], c1 = a.cu[b + 1];
+  if (c0 < 0 || c1 < c0 || c1 > a.n_tok || c1 - c0 > a.T_max) return false;
+  row0 = c0;
+  Tb = c1 - c0;
+  return true;
+}
+
+template <int DK, int C>
+__device__ __forceinline__ void load_tile(float4 (&s)[C][DK / 64], const float *base, const Lane &L) {
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int e = 0; e < DK / 64; ++e)
+      s[c][e] = *reinterpret_cast<const float4 *>(base + (int64_t)(L.col0 + c * L.slab) * DK + 4 * L.r + 64 * e);
+}
+
+template <int DK, int C>
+__device__ __forceinline__ void store_tile(float *base, const float4 (&s)[C][DK / 64], const Lane &L) {
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int e = 0; e < DK / 64; ++e)
+      *reinterpret_cast<float4 *>(base + (int64_t)(L.col0 + c * L.slab) * DK + 4 * L.r + 64 * e) = s[c][e];
+}
+
+// Output gate over the head's whole value vector (the tile spans all of dv):
+// o <- o / sqrt(mean(o^2) + eps) * weight * sigmoid(gate). part: LDS, >= slab floats.
+template <int C>
+__device__ __forceinline__ void output_gate(const Args &a, float (&o)[C], int64_t gbase,
+                                            const Lane &L, float *part) {
+  float ss = o[0] * o[0];
+#pragma unroll
+  for (int c = 1; c < C; ++c) ss = __builtin_fmaf(o[c], o[c], ss);
+  if (L.r == 0) part[L.col0] = ss;
+  __syncthreads();
+  float tot = part[0];
+  for (int i = 1; i < L.slab; ++i) tot += part[i];
+  __syncthreads();
+  const float inv_rms = 1.0f / sqrtf(tot / (float)a.dv + a.eps);
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int j = L.col0 + c * L.slab;
+    const float g = bf16_to_f32(a.gate[gbase + j]);
+    const float w = a.weight ? a.weight[j] : 1.0f;
+    o[c] = o[c] * inv_rms * w * (1.0f / (1.0f + expf(-g)));
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Kernels
+// ----------------------------------------------------------------------------
+
+// Single-token step, in place. Inputs go straight to registers: a lane's key
+// channels are fixed, so it loads exactly the k, q, alpha it uses.
+template <int DK, int C, bool GATE>
+__global__ __launch_bounds__(256) void decode_kernel(Args a) {
+  constexpr int NV = DK / 64;
+  const Unit u = unit_of_block(a.ntile, a.H);
+  const int32_t slot = a.slot_ids[u.b];
+  if (slot < 0) return;
+  if (slot >= a.num_slots) {
+    report(a.dev_err, u, KDA_DEVERR_SLOT);
+    return;
+  }
+  const Lane L = lane_geometry();
+  const int W = C * L.slab;
+  const int64_t th = (int64_t)u.b * a.H + u.h;
+  float *S = a.cache + (int64_t)slot * a.slot_stride + ((int64_t)u.h * a.dv + (int64_t)u.tile * W) * DK;
+
+  float4 s[C][NV];
+  load_tile<DK, C>(s, S, L);
+  float4 kk[NV], qq[NV], aa[NV];
+#pragma unroll
+  for (int e = 0; e < NV; ++e) {
+    const int64_t off = th * DK + 4 * L.r + 64 * e;
+    kk[e] = unpack_bf16x4(*reinterpret_cast<const uint2 *>(a.k + off));
+    qq[e] = unpack_bf16x4(*reinterpret_cast<const uint2 *>(a.q + off));
+    aa[e] = *reinterpret_cast<const float4 *>(a.alpha + off);
+  }
+  const int64_t vbase = th * a.dv + (int64_t)u.tile * W;
+  float vj[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) vj[c] = bf16_to_f32(a.v[vbase + L.col0 + c * L.slab]);
+  const float beta = a.beta[th];
+
+  token_update<NV, C>(s, aa, kk, vj, beta);
+  float o[C];
+  token_readout<NV, C>(s, qq, o);
+  store_tile<DK, C>(S, s, L);
+  if constexpr (GATE) {
+    __shared__ float part[16];
+    output_gate<C>(a, o, vbase, L, part);
+  }
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+    if (L.r == c) a.out[vbase + L.col0 + c * L.slab] = o[c];
+}
+
+// LDS staging for a chunk of tokens: k, q, alpha as float [T_max][DK], the
+// tile's v as float [T_max][W], beta [T_max].
+template <int DK>
+struct Staged {
+  float *k, *q, *a, *v, *beta;
+  __device__ Staged(float *base, int T_max, int W) {
+    k = base;
+    q = k + T_max * DK;
+    a = q + T_max * DK;
+    v = a + T_max * DK;
+    beta = v + T_max * W;
+  }
+};
+
+// Dynamic LDS bytes for Staged<dk>, rounded up to 16.
+inline size_t staged_bytes(int dk, int T_max, int W) {
+  return ((size_t)T_max * (3 * dk + W + 1) * sizeof(float) + 15) / 16 * 16;
+}
+
+// Speculative verify over a packed chunk: T_b tokens with the state in
+// registers; outputs per token; the committed slot stays untouched unless the
+// row is a single in-place token.
+template <int DK, int C, bool GATE>
+__global__ __launch_bounds__(256) void verify_kernel(Args a) {
+  constexpr int NV = DK / 64;
+  extern __shared__ float4 lds_dyn[];
+  const Unit u = unit_of_block(a.ntile, a.H);
+  const int32_t slot = a.slot_ids[u.b];
+  if (slot < 0) return;
+  if (slot >= a.num_slots) {
+    report(a.dev_err, u, KDA_DEVERR_SLOT);
+    return;
+  }
+  int64_t row0;
+  int Tb;
+  if (!row_range(a, u.b, row0, Tb)) {
+    report(a.dev_err, u, KDA_DEVERR_SEQLEN);
+    return;
+  }
+  if (Tb == 0) return;
+  const bool inplace = Tb == 1 && a.t1_inplace;
+  const bool replay = !inplace && a.mode == KDA_REPLAY;
+  const bool perpos = !inplace && a.mode == KDA_PER_POSITION;
+  const Lane L = lane_geometry();
+  const int W = C * L.slab;
+  Staged<DK> st(reinterpret_cast<float *>(lds_dyn), a.T_max, W);
+
+  // stage the chunk's inputs; in replay mode also copy them to the buffer
+  for (int idx = threadIdx.x; idx < Tb * (DK / 4); idx += blockDim.x) {
+    const int t = idx / (DK / 4), i = (idx % (DK / 4)) * 4;
+    const int64_t off = ((row0 + t) * a.H + u.h) * DK + i;
+    const uint2 kb = *reinterpret_cast<const uint2 *>(a.k + off);
+    const uint2 qb = *reinterpret_cast<const uint2 *>(a.q + off);
+    const float4 al = *reinterpret_cast<const float4 *>(a.alpha + off);
+    *reinterpret_cast<float4 *>(st.k + t * DK + i) = unpack_bf16x4(kb);
+    *reinterpret_cast<float4 *>(st.q + t * DK + i) = unpack_bf16x4(qb);
+    *reinterpret_cast<float4 *>(st.a + t * DK + i) = al;
+    if (replay && u.tile == 0) {
+      const int64_t d = (((int64_t)u.b * a.T_max + t) * a.H + u.h) * DK + i;
+      *reinterpret_cast<uint2 *>(a.rk + d) = kb;
+      *reinterpret_cast<float4 *>(a.ralpha + d) = al;
+    }
+  }
+  for (int idx = threadIdx.x; idx < Tb * W; idx += blockDim.x) {
+    const int t = idx / W, jj = idx % W;
+    const uint16_t vb = a.v[((row0 + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj];
+    st.v[t * W + jj] = bf16_to_f32(vb);
+    if (replay) a.rv[(((int64_t)u.b * a.T_max + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj] = vb;
+  }
+  if ((int)threadIdx.x < Tb) {
+    const float bt = a.beta[(row0 + threadIdx.x) * a.H + u.h];
+    st.beta[threadIdx.x] = bt;
+    if (replay && u.tile == 0) a.rbeta[((int64_t)u.b * a.T_max + threadIdx.x) * a.H + u.h] = bt;
+  }
+  __syncthreads();
+
+  float *S = a.cache + (int64_t)slot * a.slot_stride + ((int64_t)u.h * a.dv + (int64_t)u.tile * W) * DK;
+  float4 s[C][NV];
+  load_tile<DK, C>(s, S, L);
+  __shared__ float part[16];
+
+  for (int t = 0; t < Tb; ++t) {
+    float4 kk[NV], qq[NV], aa[NV];
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      const int i = t * DK + 4 * L.r + 64 * e;
+      kk[e] = *reinterpret_cast<const float4 *>(st.k + i);
+      qq[e] = *reinterpret_cast<const float4 *>(st.q + i);
+      aa[e] = *reinterpret_cast<const float4 *>(st.a + i);
+    }
+    float vj[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) vj[c] = st.v[t * W + L.col0 + c * L.slab];
+    token_update<NV, C>(s, aa, kk, vj, st.beta[t]);
+    float o[C];
+    token_readout<NV, C>(s, qq, o);
+    const int64_t obase = ((row0 + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W;
+    if constexpr (GATE) output_gate<C>(a, o, obase, L, part);
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+      if (L.r == c) a.out[obase + L.col0 + c * L.slab] = o[c];
+    if (perpos) {
+      float *D = a.draft + ((((int64_t)u.b * a.T_max + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W) * DK;
+      store_tile<DK, C>(D, s, L);
+    }
+  }
+  if (inplace) store_tile<DK, C>(S, s, L);
+}
+
+// Row checks shared by the commit kernels; returns the accepted length, or -1
+// when the row does not run.
+__device__ __forceinline__ int commit_row(const Args &a, const Unit &u, int32_t &slot) {
+  slot = a.slot_ids[u.b];
+  if (slot < 0) return -1;
+  if (slot >= a.num_slots) {
+    report(a.dev_err, u, KDA_DEVERR_SLOT);
+    return -1;
+  }
+  int Tb = a.T_max;
+  if (a.cu) {
+    int64_t row0;
+    if (!row_range(a, u.b, row0, Tb)) {
+      report(a.dev_err, u, KDA_DEVERR_SEQLEN);
+      return -1;
+    }
+  }
+  const int n = a.accepted[u.b];
+  if (n < 0 || n > Tb) {
+    report(a.dev_err, u, KDA_DEVERR_ACCEPTED);
+    return -1;
+  }
+  return n;
+}
+
+// ReplaySSM commit: reload the committed state, replay the first n buffered
+// tokens with the same column engine, store once.
+template <int DK, int C>
+__global__ __launch_bounds__(256) void commit_replay_kernel(Args a) {
+  constexpr int NV = DK / 64;
+  extern __shared__ float4 lds_dyn[];
+  const Unit u = unit_of_block(a.ntile, a.H);
+  int32_t slot;
+  const int n = commit_row(a, u, slot);
+  if (n <= 0) return;
+  const Lane L = lane_geometry();
+  const int W = C * L.slab;
+  Staged<DK> st(reinterpret_cast<float *>(lds_dyn), a.T_max, W);
+  for (int idx = threadIdx.x; idx < n * (DK / 4); idx += blockDim.x) {
+    const int t = idx / (DK / 4), i = (idx % (DK / 4)) * 4;
+    const int64_t d = (((int64_t)u.b * a.T_max + t) * a.H + u.h) * DK + i;
+    *reinterpret_cast<float4 *>(st.k + t * DK + i) = unpack_bf16x4(*reinterpret_cast<const uint2 *>(a.rk + d));
+    *reinterpret_cast<float4 *>(st.a + t * DK + i) = *reinterpret_cast<const float4 *>(a.ralpha + d);
+  }
+  for (int idx = threadIdx.x; idx < n * W; idx += blockDim.x) {
+    const int t = idx / W, jj = idx % W;
+    st.v[t * W + jj] = bf16_to_f32(a.rv[(((int64_t)u.b * a.T_max + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj]);
+  }
+  if ((int)threadIdx.x < n) st.beta[threadIdx.x] = a.rbeta[((int64_t)u.b * a.T_max + threadIdx.x) * a.H + u.h];
+  __syncthreads();
+
+  float *S = a.cache + (int64_t)slot * a.slot_stride + ((int64_t)u.h * a.dv + (int64_t)u.tile * W) * DK;
+  float4 s[C][NV];
+  load_tile<DK, C>(s, S, L);
+  for (int t = 0; t < n; ++t) {
+    float4 kk[NV], aa[NV];
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      const int i = t * DK + 4 * L.r + 64 * e;
+      kk[e] = *reinterpret_cast<const float4 *>(st.k + i);
+      aa[e] = *reinterpret_cast<const float4 *>(st.a + i);
+    }
+    float vj[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) vj[c] = st.v[t * W + L.col0 + c * L.slab];
+    token_update<NV, C>(s, aa, kk, vj, st.beta[t]);
+  }
+  store_tile<DK, C>(S, s, L);
+}
+
+// Per-position commit: copy the state saved after the last accepted token.
+template <int DK, int C>
+__global__ __launch_bounds__(256) void commit_copy_kernel(Args a) {
+  constexpr int NV = DK / 64;
+  const Unit u = unit_of_block(a.ntile, a.H);
+  int32_t slot;
+  const int n = commit_row(a, u, slot);
+  if (n <= 0) return;
+  const Lane L = lane_geometry();
+  const int W = C * L.slab;
+  const float *D = a.draft + ((((int64_t)u.b * a.T_max + (n - 1)) * a.H + u.h) * a.dv + (int64_t)u.tile * W) * DK;
+  float *S = a.cache + (int64_t)slot * a.slot_stride + ((int64_t)u.h * a.dv + (int64_t)u.tile * W) * DK;
+  float4 s[C][NV];
+  load_tile<DK, C>(s, D, L);
+  store_tile<DK, C>(S, s, L);
+}
+
+// ----------------------------------------------------------------------------
+// Host side: checks, launch shape, dispatch
+// ----------------------------------------------------------------------------
+
+enum Kind { KIND_DECODE, KIND_VERIFY, KIND_COMMIT_REPLAY, KIND_COMMIT_COPY };
+
+template <int DK, int C>
+const void *kernel_for(Kind kind, bool gate) {
+  switch (kind) {
+    case KIND_DECODE:
+      return gate ? (const void *)decode_kernel<DK, C, true> : (const void *)decode_kernel<DK, C, false>;
+    case KIND_VERIFY:
+      return gate ? (const void *)verify_kernel<DK, C, true> : (const void *)verify_kernel<DK, C, false>;
+    case KIND_COMMIT_REPLAY:
+      return (const void *)commit_replay_kernel<DK, C>;
+    case KIND_COMMIT_COPY:
+      return (const void *)commit_copy_kernel<DK, C>;
+  }
+  return nullptr;
+}
+
+template <int DK>
+const void *kernel_for_c(Kind kind, bool gate, int C) {
+  switch (C) {
+    case 1: return kernel_for<DK, 1>(kind, gate);
+    case 2: return kernel_for<DK, 2>(kind, gate);
+    case 4: return kernel_for<DK, 4>(kind, gate);
+    case 8: return kernel_for<DK, 8>(kind, gate);
+  }
+  return nullptr;
+}
+
+struct Launch {
+  int W, waves, C;
+};
+
+// Legal tile widths and their (waves, slabs per lane).
+bool launch_of_width(int W, Launch *l) {
+  switch (W) {
+    case 4: *l = {4, 1, 1}; return true;
+    case 8: *l = {8, 2, 1}; return true;
+    case 16: *l = {16, 4, 1}; return true;
+    case 32: *l = {32, 4, 2}; return true;
+    case 64: *l = {64, 4, 4}; return true;
+    case 128: *l = {128, 4, 8}; return true;
+  }
+  return false;
+}
+
+bool dims_supported(int dk, int dv) { return (dk == 64 || dk == 128) && (dv == 64 || dv == 128); }
+
+// Launch shape from the batch size and the per-GPU head count: the widest tile
+// that still gives every CU several workgroups; at small B*H fall back to
+// narrow tiles so the state is spread over as many CUs as possible.
+int choose_width(int64_t rows, int H, int dv, bool gate, int requested, int T_max, Launch *l) {
+  if (gate) {
+    if (requested != 0 && requested != dv) return KDA_ERR_UNSUPPORTED;
+    return launch_of_width(dv, l) ? KDA_OK : KDA_ERR_UNSUPPORTED;
+  }
+  if (requested != 0) {
+    if (requested > dv || dv % requested != 0 || !launch_of_width(requested, l)) return KDA_ERR_UNSUPPORTED;
+    return KDA_OK;
+  }
+  const int64_t heads = rows * H;
+  const int64_t target = 2048;
+  int W = 4;
+  for (int cand : {64, 32, 16, 8}) {
+    if (cand <= dv && heads * (dv / cand) >= target) {
+      W = cand;
+      break;
+    }
+  }
+  (void)T_max;
+  return launch_of_width(W, l) ? KDA_OK : KDA_ERR_UNSUPPORTED;
+}
+
+bool aligned(const void *p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
+
+int launch(Kind kind, bool gate, int dk, const Launch &l, int64_t units, size_t shmem, Args &a,
+           void *stream) {
+  if (units > 0x7fffffff) return KDA_ERR_UNSUPPORTED;
+  const void *fn = dk == 64 ? kernel_for_c<64>(kind, gate, l.C) : kernel_for_c<128>(kind, gate, l.C);
+  if (!fn) return KDA_ERR_UNSUPPORTED;
+  void *args[] = {&a};
+  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)units), dim3(64 * l.waves), args, shmem,
+                                       (hipStream_t)stream);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int check_cache(const float *cache, int64_t num_slots, int64_t slot_stride, int H, int dk, int dv) {
+  if (!cache || num_slots < 0) return KDA_ERR_INVALID;
+  if (slot_stride < (int64_t)H * dv * dk) return KDA_ERR_INVALID;
+  if (!aligned(cache, 16) || slot_stride % 4 != 0) return KDA_ERR_ALIGN;
+  return KDA_OK;
+}
+
+int check_inputs(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *alpha,
+                 const float *beta, float *out, bool need_q) {
+  if ((need_q && !q) || !k || !v || !alpha || !beta || (need_q && !out)) return KDA_ERR_INVALID;
+  if ((q && !aligned(q, 8)) || !aligned(k, 8) || !aligned(v, 8) || !aligned(alpha, 16) ||
+      !aligned(beta, 4) || (out && !aligned(out, 4)))
+    return KDA_ERR_ALIGN;
+  return KDA_OK;
+}
+
+int check_gate(const kda_epilogue *epi) {
+  if (!epi) return KDA_OK;
+  if (!epi->gate || !(epi->eps >= 0.0f) || epi->eps > 3.0e38f) return KDA_ERR_INVALID;
+  if (!aligned(epi->gate, 8) || (epi->weight && !aligned(epi->weight, 4))) return KDA_ERR_ALIGN;
+  return KDA_OK;
+}
+
+int check_replay_buf(const kda_replay_buf *rb) {
+  if (!rb || !rb->k || !rb->v || !rb->alpha || !rb->beta) return KDA_ERR_INVALID;
+  if (!aligned(rb->k, 8) || !aligned(rb->v, 8) || !aligned(rb->alpha, 16) || !aligned(rb->beta, 4))
+    return KDA_ERR_ALIGN;
+  return KDA_OK;
+}
+
+#define KDA_TRY(expr)          \
+  do {                         \
+    const int rc_ = (expr);    \
+    if (rc_ != KDA_OK) return rc_; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int kda_decode_step(float *cache, int64_t num_slots, int64_t slot_stride, const int32_t *slot_ids,
+                    int32_t B, int32_t H, int32_t dk, int32_t dv, const uint16_t *q,
+                    const uint16_t *k, const uint16_t *v, const float *alpha, const float *beta,
+                    float *out, const kda_epilogue *epi, int32_t *dev_err,
+                    const kda_options *opts, void *stream) {
+  if (B < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID;
+  if (!dims_supported(dk, dv)) return KDA_ERR_UNSUPPORTED;
+  if (B == 0) return KDA_OK;
+  if (!slot_ids) return KDA_ERR_INVALID;
+  KDA_TRY(check_cache(cache, num_slots, slot_stride, H, dk, dv));
+  KDA_TRY(check_inputs(q, k, v, alpha, beta, out, true));
+  KDA_TRY(check_gate(epi));
+  if (dev_err && !aligned(dev_err, 4)) return KDA_ERR_ALIGN;
+  Launch l;
+  KDA_TRY(choose_width(B, H, dv, epi != nullptr, opts ? opts->tile_w : 0, 1, &l));
+
+  Args a;
+  memset(&a, 0, sizeof a);
+  a.cache = cache;
+  a.num_slots = num_slots;
+  a.slot_stride = slot_stride;
+  a.slot_ids = slot_ids;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.out = out;
+  a.gate = epi ? epi->gate : nullptr;
+  a.weight = epi ? epi->weight : nullptr;
+  a.eps = epi ? epi->eps : 0.0f;
+  a.dev_err = dev_err;
+  a.B = B;
+  a.H = H;
+  a.dv = dv;
+  a.T_max = 1;
+  a.n_tok = B;
+  a.ntile = dv / l.W;
+  return launch(KIND_DECODE, epi != nullptr, dk, l, (int64_t)B * H * a.ntile, 0, a, stream);
+}
+
+int kda_verify_chunk(float *cache, int64_t num_slots, int64_t slot_stride, const int32_t *slot_ids,
+                     const int32_t *cu_seqlens, int32_t B, int32_t T_max, int32_t n_tok, int32_t H,
+                     int32_t dk, int32_t dv, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                     const float *alpha, const float *beta, float *out, const kda_epilogue *epi,
+                     int32_t mode, int32_t t1_inplace, const kda_replay_buf *rb, float *draft,
+                     int32_t *dev_err, const kda_options *opts, void *stream) {
+  if (B < 0 || H <= 0 || dk <= 0 || dv <= 0 || n_tok < 0) return KDA_ERR_INVALID;
+  if (mode != KDA_REPLAY && mode != KDA_PER_POSITION) return KDA_ERR_INVALID;
+  if (!dims_supported(dk, dv) || T_max < 1 || T_max > kMaxT) return KDA_ERR_UNSUPPORTED;
+  if (B == 0 || n_tok == 0) return KDA_OK;  // no tokens: nothing to read or write
+  if (!slot_ids || !cu_seqlens) return KDA_ERR_INVALID;
+  KDA_TRY(check_cache(cache, num_slots, slot_stride, H, dk, dv));
+  KDA_TRY(check_inputs(q, k, v, alpha, beta, out, true));
+  KDA_TRY(check_gate(epi));
+  if (mode == KDA_REPLAY) KDA_TRY(check_replay_buf(rb));
+  if (mode == KDA_PER_POSITION) {
+    if (!draft) return KDA_ERR_INVALID;
+    if (!aligned(draft, 16)) return KDA_ERR_ALIGN;
+  }
+  if (dev_err && !aligned(dev_err, 4)) return KDA_ERR_ALIGN;
+  Launch l;
+  KDA_TRY(choose_width(B, H, dv, epi != nullptr, opts ? opts->tile_w : 0, T_max, &l));
+
+  Args a;
+  memset(&a, 0, sizeof a);
+  a.cache = cache;
+  a.num_slots = num_slots;
+  a.slot_stride = slot_stride;
+  a.slot_ids = slot_ids;
+  a.cu = cu_seqlens;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.out = out;
+  a.gate = epi ? epi->gate : nullptr;
+  a.weight = epi ? epi->weight : nullptr;
+  a.eps = epi ? epi->eps : 0.0f;
+  a.dev_err = dev_err;
+  if (mode == KDA_REPLAY) {
+    a.rk = rb->k;
+    a.rv = rb->v;
+    a.ralpha = rb->alpha;
+    a.rbeta = rb->beta;
+  } else {
+    a.draft = draft;
+  }
+  a.B = B;
+  a.H = H;
+  a.dv = dv;
+  a.T_max = T_max;
+  a.n_tok = n_tok;
+  a.ntile = dv / l.W;
+  a.mode = mode;
+  a.t1_inplace = t1_inplace ? 1 : 0;
+  return launch(KIND_VERIFY, epi != nullptr, dk, l, (int64_t)B * H * a.ntile, staged_bytes(dk, T_max, l.W), a,
+                stream);
+}
+
+int kda_replay_commit(float *cache, int64_t num_slots, int64_t slot_stride, const int32_t *slot_ids,
+                      const int32_t *cu_seqlens, const int32_t *accepted_len, int32_t B,
+                      int32_t T_max, int32_t n_tok, int32_t H, int32_t dk, int32_t dv, int32_t mode,
+                      const kda_replay_buf *rb, const float *draft, int32_t *dev_err,
+                      const kda_options *opts, void *stream) {
+  if (B < 0 || H <= 0 || dk <= 0 || dv <= 0 || n_tok < 0) return KDA_ERR_INVALID;
+  if (mode != KDA_REPLAY && mode != KDA_PER_POSITION) return KDA_ERR_INVALID;
+  if (!dims_supported(dk, dv) || T_max < 1 || T_max > kMaxT) return KDA_ERR_UNSUPPORTED;
+  if (B == 0) return KDA_OK;
+  if (!slot_ids || !accepted_len) return KDA_ERR_INVALID;
+  KDA_TRY(check_cache(cache, num_slots, slot_stride, H, dk, dv));
+  if (mode == KDA_REPLAY) KDA_TRY(check_replay_buf(rb));
+  if (mode == KDA_PER_POSITION) {
+    if (!draft) return KDA_ERR_INVALID;
+    if (!aligned(draft, 16)) return KDA_ERR_ALIGN;
+  }
+  if (!aligned(accepted_len, 4) || (cu_seqlens && !aligned(cu_seqlens, 4)) ||
+      (dev_err && !aligned(dev_err, 4)))
+    return KDA_ERR_ALIGN;
+  Launch l;
+  KDA_TRY(choose_width(B, H, dv, false, opts ? opts->tile_w : 0, T_max, &l));
+
+  Args a;
+  memset(&a, 0, sizeof a);
+  a.cache = cache;
+  a.num_slots = num_slots;
+  a.slot_stride = slot_stride;
+  a.slot_ids = slot_ids;
+  a.cu = cu_seqlens;
+  a.accepted = accepted_len;
+  a.dev_err = dev_err;
+  if (mode == KDA_REPLAY) {
+    a.rk = rb->k;
+    a.rv = rb->v;
+    a.ralpha = rb->alpha;
+    a.rbeta = rb->beta;
+  } else {
+    a.draft = const_cast<float *>(draft);
+  }
+  a.B = B;
+  a.H = H;
+  a.dv = dv;
+  a.T_max = T_max;
+  a.n_tok = n_tok;
+  a.ntile = dv / l.W;
+  a.mode = mode;
+  if (mode == KDA_REPLAY) {
+    return launch(KIND_COMMIT_REPLAY, false, dk, l, (int64_t)B * H * a.ntile, staged_bytes(dk, T_max, l.W), a,
+                  stream);
+  }
+  return launch(KIND_COMMIT_COPY, false, dk, l, (int64_t)B * H * a.ntile, 0, a, stream);
+}
+
+int kda_query_variant(int32_t B, int32_t H, int32_t dk, int32_t dv, int32_t T_max, int32_t epilogue,
+                      int32_t requested_tile_w, int32_t *tile_w, int32_t *threads) {
+  if (B < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID;
+  if (!dims_supported(dk, dv) || T_max < 1 || T_max > kMaxT) return KDA_ERR_UNSUPPORTED;
+  Launch l;
+  KDA_TRY(choose_width(B, H, dv, epilogue != 0, requested_tile_w, T_max, &l));
+  if (tile_w) *tile_w = l.W;
+  if (threads) *threads = 64 * l.waves;
+  return KDA_OK;
+}
+
+const char *kda_status_str(int32_t status) {
+  switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_INVALID: return "invalid argument";
+    case KDA_ERR_UNSUPPORTED: return "unsupported shape or launch width";
+    case KDA_ERR_ALIGN: return "misaligned pointer or stride";
+    case KDA_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,266 @@
+"""Python binding of the KDA C ABI (include/kda.h): argument marshalling only.
+
+Each function has the name of the C entry point it calls, takes torch tensors
+that already live on the GPU, passes their device pointers and the current
+HIP stream, and raises KdaError on a non-zero status. Every step of the
+computation runs in the HIP kernels of libkda.so; there is no other path. If
+the library is missing, importing the package still works but the first call
+raises, naming the build command.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+
+KDA_OK = 0
+KDA_ERR_INVALID = -1
+KDA_ERR_UNSUPPORTED = -2
+KDA_ERR_ALIGN = -3
+KDA_ERR_HIP = -4
+
+KDA_REPLAY = 0
+KDA_PER_POSITION = 1
+
+KDA_DEVERR_SLOT = 1
+KDA_DEVERR_SEQLEN = 2
+KDA_DEVERR_ACCEPTED = 4
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {kda_status_str(status)} ({status})")
+        self.status = status
+
+
+class kda_epilogue(ctypes.Structure):
+    _fields_ = [("gate", ctypes.c_void_p), ("weight", ctypes.c_void_p), ("eps", ctypes.c_float)]
+
+
+class kda_replay_buf(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("alpha", ctypes.c_void_p),
+                ("beta", ctypes.c_void_p)]
+
+
+class kda_options(ctypes.Structure):
+    _fields_ = [("tile_w", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libkda.so (once). Raises FileNotFoundError when it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python gated_delta_rule_98_amd/build.py`")
+    lib = ctypes.CDLL(path)
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.kda_decode_step.argtypes = [P, i64, i64, P, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
+    lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_verify_chunk.argtypes = [P, i64, i64, P, P, i32, i32, i32, i32, i32, i32,
+                                     P, P, P, P, P, P, P, i32, i32, P, P, P, P, P]
+    lib.kda_verify_chunk.restype = ctypes.c_int
+    lib.kda_replay_commit.argtypes = [P, i64, i64, P, P, P, i32, i32, i32, i32, i32, i32, i32,
+                                      P, P, P, P, P]
+    lib.kda_replay_commit.restype = ctypes.c_int
+    lib.kda_query_variant.argtypes = [i32, i32, i32, i32, i32, i32, i32,
+                                      ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.kda_query_variant.restype = ctypes.c_int
+    lib.kda_status_str.argtypes = [i32]
+    lib.kda_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def kda_status_str(status: int) -> str:
+    return load_library().kda_status_str(int(status)).decode()
+
+
+def kda_query_variant(B: int, H: int, dk: int, dv: int, T_max: int = 1, epilogue: bool = False,
+                      tile_w: int = 0) -> Tuple[int, int]:
+    """(tile width, threads per workgroup) that a call of this shape launches."""
+    w, t = ctypes.c_int32(0), ctypes.c_int32(0)
+    rc = load_library().kda_query_variant(B, H, dk, dv, T_max, int(bool(epilogue)), tile_w,
+                                          ctypes.byref(w), ctypes.byref(t))
+    if rc != KDA_OK:
+        raise KdaError(rc, "kda_query_variant")
+    return w.value, t.value
+
+
+# ------------------------------------------------------------------ marshalling
+
+_BF16_TYPES = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str, dtypes, ndim: Optional[int] = None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _shape(t: Optional[torch.Tensor], name: str, shape) -> None:
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _replay(replay: Optional[dict], B: int, T_max: int, H: int, dk: int, dv: int):
+    if replay is None:
+        return None
+    for key, d, shape in (("k", _BF16_TYPES, (B, T_max, H, dk)), ("v", _BF16_TYPES, (B, T_max, H, dv)),
+                          ("alpha", (torch.float32,), (B, T_max, H, dk)),
+                          ("beta", (torch.float32,), (B, T_max, H))):
+        _dev(replay[key], f"replay {key}", d)
+        _shape(replay[key], f"replay {key}", shape)
+    return kda_replay_buf(replay["k"].data_ptr(), replay["v"].data_ptr(), replay["alpha"].data_ptr(),
+                          replay["beta"].data_ptr())
+
+
+def _cache(cache: torch.Tensor):
+    """cache: float32 [num_slots, H, dv, dk]; each slot contiguous, slots at stride(0)."""
+    if cache.device.type != "cuda" or cache.dtype != torch.float32 or cache.dim() != 4:
+        raise ValueError("cache must be a float32 GPU tensor [num_slots, H, dv, dk]")
+    ns, H, dv, dk = cache.shape
+    if cache.stride()[1:] != (dv * dk, dk, 1):
+        raise ValueError("each cache slot must be contiguous [H, dv, dk]")
+    return ns, cache.stride(0), H, dv, dk
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _epilogue(gate, weight, eps):
+    if gate is None:
+        return None
+    _dev(gate, "gate", _BF16_TYPES)
+    if weight is not None:
+        _dev(weight, "weight", (torch.float32,), 1)
+    return kda_epilogue(gate.data_ptr(), _ptr(weight), float(eps))
+
+
+def _opts(tile_w: int):
+    return kda_options(int(tile_w)) if tile_w else None
+
+
+def _ref(x):
+    return None if x is None else ctypes.byref(x)
+
+
+def kda_decode_step(cache: torch.Tensor, slot_ids: torch.Tensor, q, k, v, alpha, beta,
+                    out: torch.Tensor, *, gate=None, weight=None, eps: float = 1e-6,
+                    dev_err: Optional[torch.Tensor] = None, tile_w: int = 0, stream=None) -> None:
+    """One token per row, state updated in place.
+
+    cache float32 [num_slots, H, dv, dk]; slot_ids int32 [B]; q, k bf16 [B, H, dk];
+    v bf16 [B, H, dv]; alpha float32 [B, H, dk]; beta float32 [B, H]; out float32
+    [B, H, dv]; gate bf16 [B, H, dv] (optional output gate), weight float32 [dv].
+    """
+    ns, stride, H, dv, dk = _cache(cache)
+    _dev(slot_ids, "slot_ids", (torch.int32,), 1)
+    B = slot_ids.shape[0]
+    for name, t, d in (("q", q, _BF16_TYPES), ("k", k, _BF16_TYPES), ("v", v, _BF16_TYPES),
+                       ("alpha", alpha, (torch.float32,)), ("beta", beta, (torch.float32,)),
+                       ("out", out, (torch.float32,))):
+        _dev(t, name, d)
+    for name, t, shape in (("q", q, (B, H, dk)), ("k", k, (B, H, dk)), ("v", v, (B, H, dv)),
+                           ("alpha", alpha, (B, H, dk)), ("beta", beta, (B, H)), ("out", out, (B, H, dv)),
+                           ("gate", gate, (B, H, dv)), ("weight", weight, (dv,))):
+        _shape(t, name, shape)
+    if dev_err is not None:
+        _dev(dev_err, "dev_err", (torch.int32,))
+    epi = _epilogue(gate, weight, eps)
+    rc = load_library().kda_decode_step(
+        cache.data_ptr(), ns, stride, slot_ids.data_ptr(), B, H, dk, dv,
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(), beta.data_ptr(), out.data_ptr(),
+        _ref(epi), _ptr(dev_err), _ref(_opts(tile_w)), _stream(stream))
+    if rc != KDA_OK:
+        raise KdaError(rc, "kda_decode_step")
+
+
+def kda_verify_chunk(cache: torch.Tensor, slot_ids: torch.Tensor, cu_seqlens: torch.Tensor,
+                     T_max: int, q, k, v, alpha, beta, out: torch.Tensor, *, mode: int = KDA_REPLAY,
+                     t1_inplace: bool = False, replay: Optional[dict] = None,
+                     draft: Optional[torch.Tensor] = None, gate=None, weight=None, eps: float = 1e-6,
+                     dev_err: Optional[torch.Tensor] = None, tile_w: int = 0, stream=None) -> None:
+    """Packed speculative chunk; token arrays are [n_tok, H, .], row b owns tokens
+    [cu[b], cu[b+1]). replay = dict(k, v, alpha, beta) with shapes [B, T_max, H, .]
+    (mode KDA_REPLAY); draft float32 [B, T_max, H, dv, dk] (mode KDA_PER_POSITION)."""
+    ns, stride, H, dv, dk = _cache(cache)
+    _dev(slot_ids, "slot_ids", (torch.int32,), 1)
+    _dev(cu_seqlens, "cu_seqlens", (torch.int32,), 1)
+    B = slot_ids.shape[0]
+    if cu_seqlens.shape[0] != B + 1:
+        raise ValueError("cu_seqlens must have B + 1 entries")
+    for name, t, d in (("q", q, _BF16_TYPES), ("k", k, _BF16_TYPES), ("v", v, _BF16_TYPES),
+                       ("alpha", alpha, (torch.float32,)), ("beta", beta, (torch.float32,)),
+                       ("out", out, (torch.float32,))):
+        _dev(t, name, d)
+    n_tok = k.shape[0]
+    for name, t, shape in (("q", q, (n_tok, H, dk)), ("k", k, (n_tok, H, dk)), ("v", v, (n_tok, H, dv)),
+                           ("alpha", alpha, (n_tok, H, dk)), ("beta", beta, (n_tok, H)),
+                           ("out", out, (n_tok, H, dv)), ("gate", gate, (n_tok, H, dv)),
+                           ("weight", weight, (dv,)), ("draft", draft, (B, T_max, H, dv, dk))):
+        _shape(t, name, shape)
+    rb = _replay(replay, B, T_max, H, dk, dv)
+    if draft is not None:
+        _dev(draft, "draft", (torch.float32,))
+    if dev_err is not None:
+        _dev(dev_err, "dev_err", (torch.int32,))
+    epi = _epilogue(gate, weight, eps)
+    rc = load_library().kda_verify_chunk(
+        cache.data_ptr(), ns, stride, slot_ids.data_ptr(), cu_seqlens.data_ptr(), B, int(T_max),
+        n_tok, H, dk, dv, q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(), beta.data_ptr(),
+        out.data_ptr(), _ref(epi), int(mode), int(bool(t1_inplace)), _ref(rb), _ptr(draft),
+        _ptr(dev_err), _ref(_opts(tile_w)), _stream(stream))
+    if rc != KDA_OK:
+        raise KdaError(rc, "kda_verify_chunk")
+
+
+def kda_replay_commit(cache: torch.Tensor, slot_ids: torch.Tensor, cu_seqlens: Optional[torch.Tensor],
+                      accepted_len: torch.Tensor, T_max: int, n_tok: int, *, mode: int = KDA_REPLAY,
+                      replay: Optional[dict] = None, draft: Optional[torch.Tensor] = None,
+                      dev_err: Optional[torch.Tensor] = None, tile_w: int = 0, stream=None) -> None:
+    """Slot of row b <- state after the first accepted_len[b] tokens of its verified chunk."""
+    ns, stride, H, dv, dk = _cache(cache)
+    _dev(slot_ids, "slot_ids", (torch.int32,), 1)
+    _dev(accepted_len, "accepted_len", (torch.int32,), 1)
+    B = slot_ids.shape[0]
+    if cu_seqlens is not None:
+        _dev(cu_seqlens, "cu_seqlens", (torch.int32,), 1)
+        _shape(cu_seqlens, "cu_seqlens", (B + 1,))
+    rb = _replay(replay, B, T_max, H, dk, dv)
+    if draft is not None:
+        _dev(draft, "draft", (torch.float32,))
+        _shape(draft, "draft", (B, T_max, H, dv, dk))
+    if dev_err is not None:
+        _dev(dev_err, "dev_err", (torch.int32,))
+    rc = load_library().kda_replay_commit(
+        cache.data_ptr(), ns, stride, slot_ids.data_ptr(), _ptr(cu_seqlens), accepted_len.data_ptr(),
+        B, int(T_max), int(n_tok), H, dk, dv, int(mode), _ref(rb), _ptr(draft), _ptr(dev_err),
+        _ref(_opts(tile_w)), _stream(stream))
+    if rc != KDA_OK:
+        raise KdaError(rc, "kda_replay_commit")

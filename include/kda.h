@@ -1,0 +1,182 @@
+/*
+ * kda.h - C ABI of the KDA recurrent-state library for MI355X (gfx950).
+ *
+ * The operation. Kimi K3's small-batch decode carries, per layer and per
+ * attention head, a KDA recurrent state held in an FP32 SSM cache ("Kimi K3
+ * vLLM optimization: NVIDIA decode speed-up 1.68x", section "What the upstream
+ * tests actually show"; "Kimi K3 performance optimization in vLLM", opening
+ * paragraph). The pages do not write the update out; this library takes KDA to
+ * be the gated delta rule with per-channel decay. Per head, with the state S a
+ * dk x dv matrix (row i = key channel, column j = value channel), one token
+ * applies
+ *     S <- Diag(alpha) S ;   S <- S + beta k (v - S^T k)^T ;   o = S^T q .
+ * Speculative verify and commit follow ReplaySSM ("Kimi K3 performance
+ * optimization in vLLM", section "ReplaySSM for state reconstruction"): the
+ * draft tokens are evaluated without writing the committed state, their inputs
+ * are buffered, and the commit rebuilds only the accepted state. Mixed batches
+ * are packed contiguously and outputs are written straight to each row's
+ * offset (same page, section "Zero-copy mixed KDA batching"). The launch shape
+ * is chosen from the batch size and the per-GPU head count ("Hyper Optimizing
+ * Kimi K3 in vLLM", section "Finding time between operators").
+ *
+ * Layouts. All arrays are contiguous, row-major, in device memory unless
+ * marked "host". bf16 arrays hold raw bfloat16 bit patterns (uint16_t).
+ *   cache   float  slot s at cache + s * slot_stride, laid out [H][dv][dk]:
+ *                  element (i, j) of head h is cache[s*slot_stride + (h*dv + j)*dk + i]
+ *                  (each value column's dk key channels are contiguous)
+ *   q, k    bf16   [rows][H][dk]   (q is used as given: any 1/sqrt(dk) scale is the caller's)
+ *   v       bf16   [rows][H][dv]
+ *   alpha   float  [rows][H][dk]   decay per key channel
+ *   beta    float  [rows][H]       write strength per head
+ *   out     float  [rows][H][dv]
+ * where rows is B for kda_decode_step and n_tok for kda_verify_chunk.
+ *
+ * Supported shapes: dk, dv in {64, 128}; 1 <= T_max <= 16.
+ *
+ * Ownership and ordering. The caller allocates and frees every buffer. The
+ * library allocates no device memory, keeps no state between calls and never
+ * synchronizes: each call validates its arguments on the host, enqueues its
+ * kernels on `stream` (a hipStream_t; NULL = the null stream) and returns.
+ * Buffers must stay valid until the stream has passed the call. Calls are
+ * reentrant. Within one call, slot ids must be distinct, and no output buffer
+ * may overlap an input or another output.
+ *
+ * Rows and slots. slot_ids[b] < 0 marks a padding row: nothing is read or
+ * written for it (its output rows keep their contents). A slot id >=
+ * num_slots is a device-side error (below).
+ *
+ * Errors. Every entry point returns KDA_OK or a negative KDA_ERR_* code. The
+ * host checks run before anything is enqueued; on an error nothing is
+ * enqueued. Device-side errors are OR-ed into *dev_err (optional, int32 in
+ * device memory, which the caller zeroes) and the offending row is skipped in
+ * full while the other rows proceed:
+ *   KDA_DEVERR_SLOT      slot id >= num_slots
+ *   KDA_DEVERR_SEQLEN    row b's token range [cu[b], cu[b+1]) is decreasing, leaves
+ *                        [0, n_tok] or is longer than T_max
+ *   KDA_DEVERR_ACCEPTED  accepted_len[b] outside [0, T_b]
+ * The library never falls back to another path: an unsupported shape is
+ * reported (KDA_ERR_UNSUPPORTED) and left to the caller.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_INVALID = -1,     /* null required pointer, negative size, bad mode, slot_stride too small */
+    KDA_ERR_UNSUPPORTED = -2, /* dk or dv not in {64, 128}, T_max outside [1, 16], illegal tile width,
+                                 grid too large */
+    KDA_ERR_ALIGN = -3,       /* cache / alpha / draft / replay alpha not 16-byte aligned, slot_stride
+                                 not a multiple of 4, bf16 arrays not 8-byte aligned, out / beta not
+                                 4-byte aligned */
+    KDA_ERR_HIP = -4          /* the HIP runtime rejected a launch */
+};
+
+enum kda_mode { KDA_REPLAY = 0, KDA_PER_POSITION = 1 };
+
+enum kda_device_error { KDA_DEVERR_SLOT = 1, KDA_DEVERR_SEQLEN = 2, KDA_DEVERR_ACCEPTED = 4 };
+
+/* Output gate fused into the read-out, per (token, head) over the whole value
+ * vector: y = o / sqrt(mean_j o_j^2 + eps) * weight * sigmoid(gate). It is the
+ * gating fused at the output of "Hyper Optimizing Kimi K3 in vLLM", section
+ * "Finding time between operators". Host struct; pointers are device memory. */
+typedef struct kda_epilogue {
+    const uint16_t *gate; /* bf16 [rows][H][dv], required */
+    const float *weight;  /* [dv], or NULL for all ones */
+    float eps;            /* >= 0 */
+} kda_epilogue;
+
+/* ReplaySSM input buffer, indexed by batch row b and draft position t.
+ * Host struct; pointers are device memory. The caller keeps the batch order
+ * between kda_verify_chunk and kda_replay_commit. */
+typedef struct kda_replay_buf {
+    uint16_t *k;  /* bf16 [B][T_max][H][dk] */
+    uint16_t *v;  /* bf16 [B][T_max][H][dv] */
+    float *alpha; /* [B][T_max][H][dk] */
+    float *beta;  /* [B][T_max][H] */
+} kda_replay_buf;
+
+/* Launch options (host struct, may be NULL). */
+typedef struct kda_options {
+    int32_t tile_w; /* value columns per workgroup: 0 = chosen from (B, H); otherwise one of
+                       4, 8, 16, 32, 64, 128 with tile_w <= dv (and tile_w == dv with the gate).
+                       Results are bit-identical for every legal width. */
+} kda_options;
+
+/*
+ * Single-token decode step for B rows. Row b reads token b of q, k, v, alpha,
+ * beta, updates the state of slot slot_ids[b] in place (all H heads) and
+ * writes out[b] (the gated y when epi != NULL).
+ */
+int kda_decode_step(float *cache, int64_t num_slots, int64_t slot_stride,
+                    const int32_t *slot_ids, int32_t B, int32_t H, int32_t dk, int32_t dv,
+                    const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                    const float *alpha, const float *beta, float *out,
+                    const kda_epilogue *epi, int32_t *dev_err,
+                    const kda_options *opts, void *stream);
+
+/*
+ * Speculative verify over a packed chunk ("ReplaySSM for state
+ * reconstruction"; "Zero-copy mixed KDA batching"). Row b owns tokens
+ * [cu_seqlens[b], cu_seqlens[b+1]) of the packed [n_tok] arrays; its T_b tokens
+ * run in order from the slot's committed state and out[cu_seqlens[b] + t] gets
+ * token t's read-out. The committed slot is not written, except that rows with
+ * T_b == 1 are updated in place when t1_inplace != 0 (the non-speculative
+ * members of a mixed batch).
+ *   mode KDA_REPLAY:       token t's k, v, alpha, beta are copied bit for bit to
+ *                          rb at [b][t] (rb required, draft ignored)
+ *   mode KDA_PER_POSITION: the state after token t is written to draft at [b][t],
+ *                          float [B][T_max][H][dv][dk] (draft required, rb ignored)
+ * In-place rows write neither. Positions t >= T_b are left untouched. With
+ * B == 0 or n_tok == 0 nothing is enqueued.
+ */
+int kda_verify_chunk(float *cache, int64_t num_slots, int64_t slot_stride,
+                     const int32_t *slot_ids, const int32_t *cu_seqlens,
+                     int32_t B, int32_t T_max, int32_t n_tok, int32_t H, int32_t dk, int32_t dv,
+                     const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                     const float *alpha, const float *beta, float *out,
+                     const kda_epilogue *epi, int32_t mode, int32_t t1_inplace,
+                     const kda_replay_buf *rb, float *draft, int32_t *dev_err,
+                     const kda_options *opts, void *stream);
+
+/*
+ * Commit the accepted prefix ("ReplaySSM for state reconstruction"): the slot
+ * of row b becomes the state after the first accepted_len[b] tokens of the
+ * chunk that kda_verify_chunk evaluated for row b. accepted_len[b] == 0 leaves
+ * the slot unchanged (use it for rows already updated in place).
+ *   mode KDA_REPLAY:       reload the slot, replay the buffered inputs of rb, store once
+ *   mode KDA_PER_POSITION: copy draft[b][accepted_len[b] - 1] into the slot
+ * Both modes leave bit-identical slots, equal bit for bit to accepted_len[b]
+ * successive kda_decode_step calls. cu_seqlens (may be NULL: then T_b = T_max)
+ * bounds accepted_len.
+ */
+int kda_replay_commit(float *cache, int64_t num_slots, int64_t slot_stride,
+                      const int32_t *slot_ids, const int32_t *cu_seqlens,
+                      const int32_t *accepted_len, int32_t B, int32_t T_max, int32_t n_tok,
+                      int32_t H, int32_t dk, int32_t dv, int32_t mode,
+                      const kda_replay_buf *rb, const float *draft, int32_t *dev_err,
+                      const kda_options *opts, void *stream);
+
+/*
+ * Host only. Reports the launch shape a call with these sizes would use
+ * (tile_w value columns per workgroup, threads per workgroup), choosing it
+ * from the batch size and head count when requested_tile_w == 0. Returns
+ * KDA_ERR_UNSUPPORTED for shapes the library does not run.
+ */
+int kda_query_variant(int32_t B, int32_t H, int32_t dk, int32_t dv, int32_t T_max,
+                      int32_t epilogue, int32_t requested_tile_w,
+                      int32_t *tile_w, int32_t *threads);
+
+/* Host only. Static message text for a kda_status code. */
+const char *kda_status_str(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -85,7 +85,12 @@ def _c(a, dtype):
 
 
 def default_threads() -> int:
-    return max(1, min(os.cpu_count() or 1, 64))
+    """Threads for the batch drivers: the CPUs this process may use, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
 
 
 def unit(S0, q, k, v, alpha, beta, *, state_fp32: bool = True, lib=None):

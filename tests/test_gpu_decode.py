@@ -1,0 +1,248 @@
+"""GPU parity of kda_decode_step against the CPU oracle, through the C ABI.
+
+Tolerances: each step's output (all rows and heads) within 1e-4 relative L2 of
+the oracle's, the state within 1e-3 relative Frobenius after the whole run.
+Slot, row and index handling is compared bit for bit.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_98_amd as K
+import oracle
+import synth
+from gpu_util import SENTINEL_BITS, bits, dev, f32, i32, log, rel_l2, sentinel, step_inputs
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 1e-4
+STATE_TOL = 1e-3
+
+
+def _sequential(w, tile_w=0):
+    """Run w.steps single-token steps on the GPU and in the oracle, each from its own state."""
+    cache_d = f32(w.cache)
+    slots_d = i32(w.slot_ids)
+    outs = torch.empty(w.steps, w.B, w.H, w.dv, device=dev())
+    log(f"{w.name}: {w.steps} sequential decode steps B={w.B} H={w.H} dk={w.dk} dv={w.dv} tile_w={tile_w}")
+    for s in range(w.steps):
+        x = step_inputs(w, s)
+        K.kda_decode_step(cache_d, slots_d, x["q"], x["k"], x["v"], x["alpha"], x["beta"], outs[s],
+                          tile_w=tile_w)
+    torch.cuda.synchronize()
+    outs_h = outs.cpu().numpy()
+    cache_h = w.cache.copy()
+    worst = 0.0
+    for s in range(w.steps):
+        ref, rc = oracle.decode(cache_h, w.slot_ids, w.q[s], w.k[s], w.v[s], w.alpha[s], w.beta[s])
+        assert rc == 0
+        worst = max(worst, rel_l2(outs_h[s], ref))
+    got = cache_d.cpu().numpy()
+    state_err = rel_l2(got[w.slot_ids], cache_h[w.slot_ids])
+    return worst, state_err, got, cache_h
+
+
+def test_tiny_256_steps():
+    w = synth.make_workload("tiny")
+    worst, state_err, _, _ = _sequential(w)
+    log(f"tiny: worst step rel-L2 {worst:.3e}, state rel-Frobenius {state_err:.3e}")
+    assert worst <= OUT_TOL and state_err <= STATE_TOL
+
+
+def test_b1_latency_1024_steps():
+    w = synth.make_workload("b1_latency")
+    worst, state_err, _, _ = _sequential(w)
+    log(f"b1_latency: worst step rel-L2 {worst:.3e}, state rel-Frobenius after 1024 steps {state_err:.3e}")
+    assert worst <= OUT_TOL and state_err <= STATE_TOL
+
+
+def test_b64_bandwidth_all_rotation_tables():
+    """The bench's launch: B=64, H=32, d=128, each of the 4 disjoint slot tables once."""
+    w = synth.make_workload("b64_bandwidth")
+    cache_d = f32(w.cache)
+    cache_h = w.cache.copy()
+    x = step_inputs(w, 0)
+    touched = []
+    for t, table in enumerate(w.slot_tables):
+        out = sentinel((w.B, w.H, w.dv))
+        log(f"b64_bandwidth: table {t}")
+        K.kda_decode_step(cache_d, i32(table), x["q"], x["k"], x["v"], x["alpha"], x["beta"], out)
+        torch.cuda.synchronize()
+        ref, rc = oracle.decode(cache_h, table, w.q[0], w.k[0], w.v[0], w.alpha[0], w.beta[0])
+        assert rc == 0
+        err = rel_l2(out.cpu().numpy(), ref)
+        got = cache_d.cpu().numpy()
+        serr = rel_l2(got[table], cache_h[table])
+        log(f"  out rel-L2 {err:.3e}, state rel-Frobenius {serr:.3e}")
+        assert err <= OUT_TOL and serr <= STATE_TOL
+        touched.extend(table.tolist())
+        untouched = np.setdiff1d(np.arange(w.num_slots), touched)
+        assert np.array_equal(got[untouched].view(np.uint32), w.cache[untouched].view(np.uint32))
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (64, 128), (128, 64)])
+def test_tile_widths_are_bit_identical(dk, dv):
+    w = synth.make(5, 3, dk, dv, num_slots=9, state_std=0.1, seed=21)
+    x = step_inputs(w, 0)
+    ref, rc = oracle.decode(w.cache.copy(), w.slot_ids, w.q[0], w.k[0], w.v[0], w.alpha[0], w.beta[0])
+    cache_ref = w.cache.copy()
+    oracle.decode(cache_ref, w.slot_ids, w.q[0], w.k[0], w.v[0], w.alpha[0], w.beta[0])
+    first = None
+    for tw in (4, 8, 16, 32, 64, 128):
+        if tw > dv:
+            continue
+        cache_d = f32(w.cache)
+        out = sentinel((w.B, w.H, dv))
+        log(f"tile widths dk={dk} dv={dv}: W={tw}")
+        K.kda_decode_step(cache_d, i32(w.slot_ids), x["q"], x["k"], x["v"], x["alpha"], x["beta"], out,
+                          tile_w=tw)
+        torch.cuda.synchronize()
+        got = (bits(cache_d), bits(out))
+        if first is None:
+            first = got
+            assert rel_l2(out.cpu().numpy(), ref) <= OUT_TOL
+            c = cache_d.cpu().numpy()
+            assert rel_l2(c[w.slot_ids], cache_ref[w.slot_ids]) <= STATE_TOL
+        else:
+            assert np.array_equal(got[0], first[0]) and np.array_equal(got[1], first[1]), tw
+
+
+def test_padding_and_out_of_range_slot():
+    w = synth.make(7, 4, 128, 128, num_slots=12, state_std=0.05, seed=22)
+    slots = w.slot_ids.copy()
+    slots[2] = -1                     # padding row
+    slots[5] = w.num_slots            # past the cache: device error, row skipped
+    x = step_inputs(w, 0)
+    cache_d = f32(w.cache)
+    out = sentinel((w.B, w.H, w.dv))
+    err = torch.zeros(1, dtype=torch.int32, device=dev())
+    log("padding and out-of-range slot")
+    K.kda_decode_step(cache_d, i32(slots), x["q"], x["k"], x["v"], x["alpha"], x["beta"], out, dev_err=err)
+    torch.cuda.synchronize()
+    cache_h = w.cache.copy()
+    ref = np.full((w.B, w.H, w.dv), np.nan, np.float32)
+    ref.view(np.uint32)[:] = SENTINEL_BITS
+    ref, rc = oracle.decode(cache_h, slots, w.q[0], w.k[0], w.v[0], w.alpha[0], w.beta[0], out=ref)
+    assert int(err.item()) == rc == K.KDA_DEVERR_SLOT
+    ob = bits(out)
+    assert np.all(ob[2] == SENTINEL_BITS) and np.all(ob[5] == SENTINEL_BITS)
+    live = [0, 1, 3, 4, 6]
+    assert rel_l2(out.cpu().numpy()[live], ref[live]) <= OUT_TOL
+    got = cache_d.cpu().numpy()
+    # the set of written slots is the oracle's, bit for bit on every slot left alone
+    changed_gpu = {s for s in range(w.num_slots) if not np.array_equal(got[s], w.cache[s])}
+    changed_ref = {s for s in range(w.num_slots) if not np.array_equal(cache_h[s], w.cache[s])}
+    assert changed_gpu == changed_ref == set(slots[live].tolist())
+    assert rel_l2(got[slots[live]], cache_h[slots[live]]) <= STATE_TOL
+
+
+def test_row_permutation_is_equivariant():
+    w = synth.make(9, 4, 128, 128, num_slots=16, state_std=0.05, seed=23)
+    p = np.random.Generator(np.random.PCG64(24)).permutation(w.B)
+    x = step_inputs(w, 0)
+    runs = []
+    for perm in (np.arange(w.B), p):
+        cache_d = f32(w.cache)
+        out = torch.empty(w.B, w.H, w.dv, device=dev())
+        log(f"permutation run {len(runs)}")
+        K.kda_decode_step(cache_d, i32(w.slot_ids[perm]), x["q"][perm].contiguous(), x["k"][perm].contiguous(),
+                          x["v"][perm].contiguous(), x["alpha"][perm].contiguous(), x["beta"][perm].contiguous(), out)
+        torch.cuda.synchronize()
+        runs.append((bits(cache_d), bits(out)))
+    assert np.array_equal(runs[0][0], runs[1][0])
+    assert np.array_equal(runs[0][1][p], runs[1][1])
+
+
+def test_repeat_runs_are_bit_identical():
+    w = synth.make(16, 32, 128, 128, num_slots=16, state_std=0.02, seed=25)
+    x = step_inputs(w, 0)
+    runs = []
+    for r in range(2):
+        cache_d = f32(w.cache)
+        out = torch.empty(w.B, w.H, w.dv, device=dev())
+        log(f"determinism run {r}")
+        K.kda_decode_step(cache_d, i32(w.slot_ids), x["q"], x["k"], x["v"], x["alpha"], x["beta"], out)
+        torch.cuda.synchronize()
+        runs.append((bits(cache_d), bits(out)))
+    assert np.array_equal(runs[0][0], runs[1][0]) and np.array_equal(runs[0][1], runs[1][1])
+
+
+def test_slot_offsets_beyond_2_pow_31_floats():
+    """A cache of 4100 slots of 2 MiB (8.6 GB): slot 4099 starts past 2^31 floats."""
+    w = synth.make(2, 32, 128, 128, num_slots=2, state_std=0.05, seed=26)
+    big = torch.empty(4100, 32, 128, 128, dtype=torch.float32, device=dev())
+    far = [4099, 3]
+    for b, s in enumerate(far):
+        big[s] = f32(w.cache[w.slot_ids[b]])
+    x = step_inputs(w, 0)
+    out = torch.empty(w.B, w.H, w.dv, device=dev())
+    log("slot offsets beyond 2^31 floats")
+    K.kda_decode_step(big, i32(far), x["q"], x["k"], x["v"], x["alpha"], x["beta"], out)
+    torch.cuda.synchronize()
+    cache_h = w.cache.copy()
+    ref, rc = oracle.decode(cache_h, w.slot_ids, w.q[0], w.k[0], w.v[0], w.alpha[0], w.beta[0])
+    assert rel_l2(out.cpu().numpy(), ref) <= OUT_TOL
+    for b, s in enumerate(far):
+        assert rel_l2(big[s].cpu().numpy(), cache_h[w.slot_ids[b]]) <= STATE_TOL
+    del big
+    torch.cuda.empty_cache()
+
+
+def test_empty_batch_is_a_no_op():
+    cache = torch.zeros(2, 1, 64, 64, device=dev())
+    e16 = torch.empty(0, 1, 64, dtype=torch.bfloat16, device=dev())
+    log("empty batch")
+    K.kda_decode_step(cache, torch.empty(0, dtype=torch.int32, device=dev()), e16, e16, e16,
+                      torch.empty(0, 1, 64, device=dev()), torch.empty(0, 1, device=dev()),
+                      torch.empty(0, 1, 64, device=dev()))
+    torch.cuda.synchronize()
+    assert float(cache.abs().sum()) == 0.0
+
+
+@pytest.mark.parametrize("dv", [128, 64])
+def test_output_gate_in_decode(dv):
+    w = synth.make(6, 4, 128, dv, num_slots=8, state_std=0.05, gate=True, seed=27)
+    weight = np.random.Generator(np.random.PCG64(28)).uniform(0.5, 2.0, dv).astype(np.float32)
+    x = step_inputs(w, 0)
+    for wt in (None, weight):
+        cache_d = f32(w.cache)
+        out = torch.empty(w.B, w.H, dv, device=dev())
+        log(f"output gate dv={dv} weight={'yes' if wt is not None else 'no'}")
+        K.kda_decode_step(cache_d, i32(w.slot_ids), x["q"], x["k"], x["v"], x["alpha"], x["beta"], out,
+                          gate=x["gate"], weight=None if wt is None else f32(wt), eps=1e-6)
+        torch.cuda.synchronize()
+        cache_h = w.cache.copy()
+        ref, _ = oracle.decode(cache_h, w.slot_ids, w.q[0], w.k[0], w.v[0], w.alpha[0], w.beta[0],
+                               gate=w.gate[0], weight=wt, eps=1e-6)
+        assert rel_l2(out.cpu().numpy(), ref) <= OUT_TOL
+        assert rel_l2(cache_d.cpu().numpy()[w.slot_ids], cache_h[w.slot_ids]) <= STATE_TOL
+
+
+def test_write_then_read_one_hot_key():
+    """beta = 1, alpha = 1, k = e_i: row i of the state becomes v (to 3 ulp) and S^T k reads it back."""
+    rng = np.random.Generator(np.random.PCG64(29))
+    H, d = 4, 128
+    cache0 = (rng.standard_normal((1, H, d, d)) * 0.02).astype(np.float32)
+    idx = [0, 17, 64, 127]
+    k = np.zeros((1, H, d), np.float32)
+    for h, i in enumerate(idx):
+        k[0, h, i] = 1.0
+    v = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(rng.standard_normal((1, H, d)).astype(np.float32)))
+    kb = synth.f32_to_bf16_bits(k)
+    cache_d = f32(cache0)
+    out = torch.empty(1, H, d, device=dev())
+    from gpu_util import bf16
+    log("write-then-read")
+    K.kda_decode_step(cache_d, i32([0]), bf16(kb), bf16(kb), bf16(synth.f32_to_bf16_bits(v)),
+                      f32(np.ones((1, H, d))), f32(np.ones((1, H))), out)
+    torch.cuda.synchronize()
+    got = cache_d.cpu().numpy()
+    o = out.cpu().numpy()
+    for h, i in enumerate(idx):
+        row = got[0, h, :, i]
+        ulp = np.spacing(np.maximum(np.abs(cache0[0, h, :, i]), np.abs(v[0, h])).astype(np.float32))
+        assert np.all(np.abs(row - v[0, h]) <= 3 * ulp)
+        assert np.array_equal(o[0, h], row)                  # reading with q = e_i returns row i
+        others = np.arange(d) != i
+        assert np.array_equal(got[0, h][:, others], cache0[0, h][:, others])
