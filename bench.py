@@ -139,6 +139,28 @@ def per_launch_ms(D, launch, n):
     return float(np.mean([s.elapsed_time(e) for s, e in evs]))
 
 
+def graph_ms(D, launch, n, replays=3):
+    """Average GPU time per launch: n launches captured once in a HIP graph, replayed."""
+    torch = D.torch
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(n):
+                launch(i)
+    torch.cuda.current_stream().wait_stream(stream)
+    graph.replay()
+    D.sync()
+    a, b = D.event(), D.event()
+    a.record()
+    for _ in range(replays):
+        graph.replay()
+    b.record()
+    D.sync()
+    return a.elapsed_time(b) / (n * replays)
+
+
 # ----------------------------------------------------------------------------- workloads
 
 def decode_setup(D, K, synth, B, seed=0):
@@ -165,11 +187,14 @@ def headline(D, K, synth, steps, warmup):
     D.sync()
     total_ms = timed_region(D, launch, steps)
     ms_step = total_ms / steps
-    kernel_ms = per_launch_ms(D, launch, steps)
-    hot_ms = per_launch_ms(D, lambda i: launch(i, hot=True), steps)
-    log(f"headline: {ms_step * 1e3:.2f} us/step, kernel {kernel_ms * 1e3:.2f} us, "
-        f"{nbytes / kernel_ms / 1e6:.1f} GB/s; same-table (cache-resident) kernel {hot_ms * 1e3:.2f} us")
-    return dict(w=w, ms_step=ms_step, kernel_ms=kernel_ms, hot_ms=hot_ms, bytes=nbytes,
+    # the K launches above run back to back on one stream with no other work, so the
+    # region's average is the kernel's average duration (rocprofv3 agrees to ~1%)
+    kernel_ms = ms_step
+    pairs_ms = per_launch_ms(D, launch, min(steps, 200))
+    hot_ms = timed_region(D, lambda i: launch(i, hot=True), min(steps, 200)) / min(steps, 200)
+    log(f"headline: {ms_step * 1e3:.2f} us/step ({nbytes / kernel_ms / 1e6:.1f} GB/s); "
+        f"event pair per launch {pairs_ms * 1e3:.2f} us; same table every step (cache-resident) {hot_ms * 1e3:.2f} us")
+    return dict(w=w, ms_step=ms_step, kernel_ms=kernel_ms, pairs_ms=pairs_ms, hot_ms=hot_ms, bytes=nbytes,
                 tile=K.kda_query_variant(B, 32, 128, 128))
 
 
@@ -179,20 +204,23 @@ def batch_sweep(D, K, synth, reps):
         w, launch, keep = decode_setup(D, K, synth, B, seed=B)
         for i in range(10):
             launch(i)
-        ms = per_launch_ms(D, launch, reps)
-        total = timed_region(D, launch, reps) / reps
+        ms = graph_ms(D, launch, reps)
+        eager = timed_region(D, launch, reps) / reps
         nb = decode_bytes(B, 32, 128, 128)
         tw, th = K.kda_query_variant(B, 32, 128, 128)
-        rows.append(dict(B=B, tile_w=tw, threads=th, us_per_step=round(total * 1e3, 3),
-                         kernel_us=round(ms * 1e3, 3), steps_per_s=round(1e3 / total, 1),
-                         tokens_per_s=round(B * 1e3 / total, 1), algorithmic_bytes=nb,
+        rows.append(dict(B=B, tile_w=tw, threads=th, us_per_step=round(ms * 1e3, 3),
+                         us_per_step_eager_python=round(eager * 1e3, 3), steps_per_s=round(1e3 / ms, 1),
+                         tokens_per_s=round(B * 1e3 / ms, 1), algorithmic_bytes=nb,
                          gbs=round(nb / ms / 1e6, 1), frac_of_peak=round(nb / ms / 1e6 / PEAK_HBM_GBS, 4)))
-        log(f"sweep B={B}: kernel {ms * 1e3:.2f} us, {nb / ms / 1e6:.0f} GB/s, step {total * 1e3:.2f} us")
+        log(f"sweep B={B}: {ms * 1e3:.2f} us/step in a HIP graph ({nb / ms / 1e6:.0f} GB/s), "
+            f"{eager * 1e3:.2f} us/step launched eagerly from Python")
         del keep
     return rows
 
 
 def b1_latency(D, K, synth):
+    """B=1, H=32, d=128: 1024 sequential single-token steps, each on the state the previous
+    step wrote. Launched eagerly from Python, and as one captured HIP graph."""
     torch = D.torch
     w = synth.make_workload("b1_latency")
     cache = D.f(w.cache)
@@ -208,112 +236,99 @@ def b1_latency(D, K, synth):
         step(s)
     D.sync()
     plain_ms = timed_region(D, step, w.steps) / w.steps
-    kernel_ms = per_launch_ms(D, step, 256)
-    # the same 1024 launches captured once in a HIP graph and replayed
-    stream = torch.cuda.Stream()
-    stream.wait_stream(torch.cuda.current_stream())
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        with torch.cuda.graph(graph, stream=stream):
-            for s in range(w.steps):
-                step(s)
-    torch.cuda.current_stream().wait_stream(stream)
-    graph.replay()
-    D.sync()
-    a, b = D.event(), D.event()
-    a.record()
-    graph.replay()
-    b.record()
-    D.sync()
-    graph_ms = a.elapsed_time(b) / w.steps
-    log(f"b1_latency: plain {plain_ms * 1e3:.2f} us/step, kernel {kernel_ms * 1e3:.2f} us, "
-        f"graph {graph_ms * 1e3:.2f} us/step")
-    return dict(B=1, steps=w.steps, us_per_step_plain=round(plain_ms * 1e3, 3),
-                kernel_us=round(kernel_ms * 1e3, 3), us_per_step_graph=round(graph_ms * 1e3, 3),
-                tile_w=K.kda_query_variant(1, 32, 128, 128)[0])
+    g_ms = graph_ms(D, step, w.steps, replays=2)
+    log(f"b1_latency: {plain_ms * 1e3:.2f} us/step launched from Python, {g_ms * 1e3:.2f} us/step in a HIP graph")
+    return dict(B=1, steps=w.steps, us_per_step_eager_python=round(plain_ms * 1e3, 3),
+                us_per_step_graph=round(g_ms * 1e3, 3), tile_w=K.kda_query_variant(1, 32, 128, 128)[0])
+
+
+def _replay_bufs(torch, dev, B, T, H, dk, dv):
+    return dict(k=torch.zeros(B, T, H, dk, dtype=torch.bfloat16, device=dev),
+                v=torch.zeros(B, T, H, dv, dtype=torch.bfloat16, device=dev),
+                alpha=torch.zeros(B, T, H, dk, device=dev), beta=torch.zeros(B, T, H, device=dev))
 
 
 def spec_verify(D, K, synth, reps):
+    """B=16 rows of 8 draft tokens. Each launch takes the next of 16 disjoint slot tables
+    (and of 4 replay / 2 per-position buffers), so state and buffers come from HBM."""
     torch = D.torch
     w = synth.make_workload("spec_verify")
-    cache = D.f(w.cache)
-    slots, cu, acc = D.i(w.slot_ids), D.i(w.cu_seqlens), D.i(w.accepted)
-    x = dict(q=D.bf(w.q[0]), k=D.bf(w.k[0]), v=D.bf(w.v[0]), alpha=D.f(w.alpha[0]), beta=D.f(w.beta[0]))
-    out = torch.empty(w.n_tok, 32, 128, device=D.dev)
     H, d, T = 32, 128, w.T_max
-    rb = dict(k=torch.zeros(w.B, T, H, d, dtype=torch.bfloat16, device=D.dev),
-              v=torch.zeros(w.B, T, H, d, dtype=torch.bfloat16, device=D.dev),
-              alpha=torch.zeros(w.B, T, H, d, device=D.dev), beta=torch.zeros(w.B, T, H, device=D.dev))
-    draft = torch.zeros(w.B, T, H, d, d, device=D.dev)
+    cache = D.f(w.cache)
+    tables = [D.i(t) for t in w.slot_tables]
+    cu, acc = D.i(w.cu_seqlens), D.i(w.accepted)
+    x = dict(q=D.bf(w.q[0]), k=D.bf(w.k[0]), v=D.bf(w.v[0]), alpha=D.f(w.alpha[0]), beta=D.f(w.beta[0]))
+    out = torch.empty(w.n_tok, H, d, device=D.dev)
+    rbs = [_replay_bufs(torch, D.dev, w.B, T, H, d, d) for _ in range(4)]
+    drafts = [torch.zeros(w.B, T, H, d, d, device=D.dev) for _ in range(2)]
     res = {}
     for mode, name in ((0, "replay"), (1, "per_position")):
-        # verify leaves the slots alone; the commit rewrites the accepted state, so each
-        # repetition starts from a fresh copy of the committed cache
-        base = cache.clone()
-
         def verify(i):
-            K.kda_verify_chunk(cache, slots, cu, T, x["q"], x["k"], x["v"], x["alpha"], x["beta"], out,
-                               mode=mode, replay=rb if mode == 0 else None, draft=draft if mode == 1 else None)
+            K.kda_verify_chunk(cache, tables[i % len(tables)], cu, T, x["q"], x["k"], x["v"], x["alpha"], x["beta"],
+                               out, mode=mode, replay=rbs[i % 4] if mode == 0 else None,
+                               draft=drafts[i % 2] if mode == 1 else None)
 
         def commit(i):
-            K.kda_replay_commit(cache, slots, cu, acc, T, w.n_tok, mode=mode,
-                                replay=rb if mode == 0 else None, draft=draft if mode == 1 else None)
+            K.kda_replay_commit(cache, tables[i % len(tables)], cu, acc, T, w.n_tok, mode=mode,
+                                replay=rbs[i % 4] if mode == 0 else None, draft=drafts[i % 2] if mode == 1 else None)
 
-        for i in range(5):
+        def pair(i):
             verify(i)
-        v_ms = per_launch_ms(D, verify, reps)
-        c_times = []
-        for r in range(reps):
-            cache.copy_(base)
-            c_times.append(per_launch_ms(D, commit, 1))
-        c_ms = float(np.mean(c_times))
-        cache.copy_(base)
+            commit(i)
+
+        for i in range(8):
+            pair(i)
+        v_ms = timed_region(D, verify, reps) / reps
+        c_ms = timed_region(D, commit, reps) / reps
+        p_ms = timed_region(D, pair, reps) / reps
         vb = verify_bytes(w.n_tok, w.B, H, d, d, mode, T)
         cb = commit_bytes(w.accepted, H, d, d, mode)
         res[name] = dict(verify_us=round(v_ms * 1e3, 3), verify_bytes=vb, verify_gbs=round(vb / v_ms / 1e6, 1),
                          commit_us=round(c_ms * 1e3, 3), commit_bytes=cb, commit_gbs=round(cb / c_ms / 1e6, 1),
-                         total_us=round((v_ms + c_ms) * 1e3, 3), total_bytes=vb + cb)
+                         verify_plus_commit_us=round(p_ms * 1e3, 3), total_bytes=vb + cb,
+                         tile_w=K.kda_query_variant(w.B, H, d, d, T_max=T, op=K.KDA_OP_VERIFY)[0])
         log(f"spec_verify {name}: verify {v_ms * 1e3:.2f} us ({vb / v_ms / 1e6:.0f} GB/s), "
-            f"commit {c_ms * 1e3:.2f} us ({cb / c_ms / 1e6:.0f} GB/s)")
-    res["tile_w"] = K.kda_query_variant(w.B, H, d, d, T_max=T)[0]
+            f"commit {c_ms * 1e3:.2f} us ({cb / c_ms / 1e6:.0f} GB/s), verify+commit {p_ms * 1e3:.2f} us")
     return res
 
 
 def mixed(D, K, synth, reps):
+    """40 single-token rows (in place) + 24 rows of 4 verified tokens, output gate, then the
+    commit of the 24; 8 disjoint slot tables over the 512-slot cache, 2 replay buffers."""
     torch = D.torch
     w = synth.make_workload("mixed")
+    H, d, T = 32, 128, w.T_max
     cache = D.f(w.cache)
-    base = cache.clone()
-    slots, cu, acc = D.i(w.slot_ids), D.i(w.cu_seqlens), D.i(w.accepted)
+    tables = [D.i(t) for t in w.slot_tables]
+    cu, acc = D.i(w.cu_seqlens), D.i(w.accepted)
     x = dict(q=D.bf(w.q[0]), k=D.bf(w.k[0]), v=D.bf(w.v[0]), alpha=D.f(w.alpha[0]), beta=D.f(w.beta[0]),
              gate=D.bf(w.gate[0]))
-    out = torch.empty(w.n_tok, 32, 128, device=D.dev)
-    H, d, T = 32, 128, w.T_max
-    rb = dict(k=torch.zeros(w.B, T, H, d, dtype=torch.bfloat16, device=D.dev),
-              v=torch.zeros(w.B, T, H, d, dtype=torch.bfloat16, device=D.dev),
-              alpha=torch.zeros(w.B, T, H, d, device=D.dev), beta=torch.zeros(w.B, T, H, device=D.dev))
+    out = torch.empty(w.n_tok, H, d, device=D.dev)
+    rbs = [_replay_bufs(torch, D.dev, w.B, T, H, d, d) for _ in range(2)]
 
     def verify(i):
-        K.kda_verify_chunk(cache, slots, cu, T, x["q"], x["k"], x["v"], x["alpha"], x["beta"], out,
-                           mode=0, t1_inplace=True, replay=rb, gate=x["gate"], eps=1e-6)
+        K.kda_verify_chunk(cache, tables[i % len(tables)], cu, T, x["q"], x["k"], x["v"], x["alpha"], x["beta"], out,
+                           mode=0, t1_inplace=True, replay=rbs[i % 2], gate=x["gate"], eps=1e-6)
 
     def commit(i):
-        K.kda_replay_commit(cache, slots, cu, acc, T, w.n_tok, mode=0, replay=rb)
+        K.kda_replay_commit(cache, tables[i % len(tables)], cu, acc, T, w.n_tok, mode=0, replay=rbs[i % 2])
 
-    for i in range(3):
+    def pair(i):
         verify(i)
-    v_ms = per_launch_ms(D, verify, reps)
-    c_times = []
-    for r in range(reps):
-        cache.copy_(base)
-        verify(0)
-        c_times.append(per_launch_ms(D, commit, 1))
-    c_ms = float(np.mean(c_times))
+        commit(i)
+
+    for i in range(8):
+        pair(i)
+    v_ms = timed_region(D, verify, reps) / reps
+    c_ms = timed_region(D, commit, reps) / reps
+    p_ms = timed_region(D, pair, reps) / reps
     vb = mixed_verify_bytes(w.seqlens, H, d, d)
     cb = commit_bytes(w.accepted, H, d, d, 0)
-    log(f"mixed: verify {v_ms * 1e3:.2f} us ({vb / v_ms / 1e6:.0f} GB/s), commit {c_ms * 1e3:.2f} us")
+    log(f"mixed: verify {v_ms * 1e3:.2f} us ({vb / v_ms / 1e6:.0f} GB/s), commit {c_ms * 1e3:.2f} us "
+        f"({cb / c_ms / 1e6:.0f} GB/s), verify+commit {p_ms * 1e3:.2f} us")
     return dict(verify_us=round(v_ms * 1e3, 3), verify_bytes=vb, verify_gbs=round(vb / v_ms / 1e6, 1),
-                commit_us=round(c_ms * 1e3, 3), commit_bytes=cb, commit_gbs=round(cb / c_ms / 1e6, 1))
+                commit_us=round(c_ms * 1e3, 3), commit_bytes=cb, commit_gbs=round(cb / c_ms / 1e6, 1),
+                verify_plus_commit_us=round(p_ms * 1e3, 3))
 
 
 def copy_calibration(D, nbytes=256 << 20, reps=5):
@@ -405,10 +420,10 @@ def main():
     breakdown = None
     if not args.no_breakdown:
         breakdown = dict(
-            decode_batch_sweep=batch_sweep(D, K, synth, reps=200),
+            decode_batch_sweep=batch_sweep(D, K, synth, reps=256),
             b1_latency_1024_steps=b1_latency(D, K, synth),
-            spec_verify_b16_t8=spec_verify(D, K, synth, reps=50),
-            mixed_b64_gated=mixed(D, K, synth, reps=30),
+            spec_verify_b16_t8=spec_verify(D, K, synth, reps=200),
+            mixed_b64_gated=mixed(D, K, synth, reps=200),
             headline_same_table_kernel_us=round(h["hot_ms"] * 1e3, 3),
         )
     if args.copy_calibration:
@@ -436,7 +451,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": stored_traffic(h["bytes"]),
                      "algorithmic_bytes_per_launch": h["bytes"],
-                     "kernel_us": round(h["kernel_ms"] * 1e3, 3)},
+                     "kernel_us": round(h["kernel_ms"] * 1e3, 3),
+                     "kernel_us_event_pair_per_launch": round(h["pairs_ms"] * 1e3, 3)},
         "cpu_baseline": cpu,
         "breakdown": breakdown,
     }

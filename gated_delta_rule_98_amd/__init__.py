@@ -14,6 +14,10 @@ from .kda import (  # noqa: F401
     KDA_ERR_INVALID,
     KDA_ERR_UNSUPPORTED,
     KDA_OK,
+    KDA_OP_COMMIT_COPY,
+    KDA_OP_COMMIT_REPLAY,
+    KDA_OP_DECODE,
+    KDA_OP_VERIFY,
     KDA_PER_POSITION,
     KDA_REPLAY,
     LIB_PATH,

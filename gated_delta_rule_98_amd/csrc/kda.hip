@@ -188,23 +188,59 @@ __device__ __forceinline__ bool row_range(const Args &a, int b, int64_t &row0, i
   return true;
 }
 
-template <int DK, int C>
+// 128-bit state accesses. STREAM marks an access that should not be kept in
+// the caches (the "nt" hint): each state tile is touched once per call, and on
+// MI355X streaming both the read and the write-back of the state measurably
+// raises the sustained HBM rate of the single-token step.
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+template <bool STREAM>
+__device__ __forceinline__ float4 ld4(const float *p) {
+  if constexpr (STREAM) {
+    const v4f t = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(p));
+    return make_float4(t.x, t.y, t.z, t.w);
+  } else {
+    return *reinterpret_cast<const float4 *>(p);
+  }
+}
+
+template <bool STREAM>
+__device__ __forceinline__ void st4(float *p, const float4 &x) {
+  if constexpr (STREAM) {
+    const v4f t = {x.x, x.y, x.z, x.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<v4f *>(p));
+  } else {
+    *reinterpret_cast<float4 *>(p) = x;
+  }
+}
+
+template <int DK, int C, bool STREAM>
 __device__ __forceinline__ void load_tile(float4 (&s)[C][DK / 64], const float *base, const Lane &L) {
 #pragma unroll
   for (int c = 0; c < C; ++c)
 #pragma unroll
     for (int e = 0; e < DK / 64; ++e)
-      s[c][e] = *reinterpret_cast<const float4 *>(base + (int64_t)(L.col0 + c * L.slab) * DK + 4 * L.r + 64 * e);
+      s[c][e] = ld4<STREAM>(base + (int64_t)(L.col0 + c * L.slab) * DK + 4 * L.r + 64 * e);
 }
 
-template <int DK, int C>
+template <int DK, int C, bool STREAM>
 __device__ __forceinline__ void store_tile(float *base, const float4 (&s)[C][DK / 64], const Lane &L) {
 #pragma unroll
   for (int c = 0; c < C; ++c)
 #pragma unroll
     for (int e = 0; e < DK / 64; ++e)
-      *reinterpret_cast<float4 *>(base + (int64_t)(L.col0 + c * L.slab) * DK + 4 * L.r + 64 * e) = s[c][e];
+      st4<STREAM>(base + (int64_t)(L.col0 + c * L.slab) * DK + 4 * L.r + 64 * e, s[c][e]);
 }
+
+// Cache policy of each state stream (measured on MI355X).
+constexpr bool kDecodeLoadStream = true;    // slot state read by the single-token step
+constexpr bool kDecodeStoreStream = true;   // slot state written back by it
+constexpr bool kVerifyLoadStream = true;    // committed state read by verify
+constexpr bool kVerifyStoreStream = true;   // per-position states and in-place rows written by verify
+constexpr bool kCommitLoadStream = true;    // committed state reloaded by the replay commit
+constexpr bool kCommitStoreStream = true;   // rebuilt state written by the replay commit
+constexpr bool kCopyLoadStream = false;     // per-position state read by the copy commit
+constexpr bool kCopyStoreStream = false;    // committed state written by the copy commit
 
 // Output gate over the head's whole value vector (the tile spans all of dv):
 // o <- o / sqrt(mean(o^2) + eps) * weight * sigmoid(gate). part: LDS, >= slab floats.
@@ -251,7 +287,7 @@ __global__ __launch_bounds__(256) void decode_kernel(Args a) {
   float *S = a.cache + (int64_t)slot * a.slot_stride + ((int64_t)u.h * a.dv + (int64_t)u.tile * W) * DK;
 
   float4 s[C][NV];
-  load_tile<DK, C>(s, S, L);
+  load_tile<DK, C, kDecodeLoadStream>(s, S, L);
   float4 kk[NV], qq[NV], aa[NV];
 #pragma unroll
   for (int e = 0; e < NV; ++e) {
@@ -269,7 +305,7 @@ __global__ __launch_bounds__(256) void decode_kernel(Args a) {
   token_update<NV, C>(s, aa, kk, vj, beta);
   float o[C];
   token_readout<NV, C>(s, qq, o);
-  store_tile<DK, C>(S, s, L);
+  store_tile<DK, C, kDecodeStoreStream>(S, s, L);
   if constexpr (GATE) {
     __shared__ float part[16];
     output_gate<C>(a, o, vbase, L, part);
@@ -357,7 +393,7 @@ __global__ __launch_bounds__(256) void verify_kernel(Args a) {
 
   float *S = a.cache + (int64_t)slot * a.slot_stride + ((int64_t)u.h * a.dv + (int64_t)u.tile * W) * DK;
   float4 s[C][NV];
-  load_tile<DK, C>(s, S, L);
+  load_tile<DK, C, kVerifyLoadStream>(s, S, L);
   __shared__ float part[16];
 
   for (int t = 0; t < Tb; ++t) {
@@ -382,10 +418,10 @@ __global__ __launch_bounds__(256) void verify_kernel(Args a) {
       if (L.r == c) a.out[obase + L.col0 + c * L.slab] = o[c];
     if (perpos) {
       float *D = a.draft + ((((int64_t)u.b * a.T_max + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W) * DK;
-      store_tile<DK, C>(D, s, L);
+      store_tile<DK, C, kVerifyStoreStream>(D, s, L);
     }
   }
-  if (inplace) store_tile<DK, C>(S, s, L);
+  if (inplace) store_tile<DK, C, kVerifyStoreStream>(S, s, L);
 }
 
 // Row checks shared by the commit kernels; returns the accepted length, or -1
@@ -441,7 +477,7 @@ __global__ __launch_bounds__(256) void commit_replay_kernel(Args a) {
 
   float *S = a.cache + (int64_t)slot * a.slot_stride + ((int64_t)u.h * a.dv + (int64_t)u.tile * W) * DK;
   float4 s[C][NV];
-  load_tile<DK, C>(s, S, L);
+  load_tile<DK, C, kCommitLoadStream>(s, S, L);
   for (int t = 0; t < n; ++t) {
     float4 kk[NV], aa[NV];
 #pragma unroll
@@ -455,7 +491,7 @@ __global__ __launch_bounds__(256) void commit_replay_kernel(Args a) {
     for (int c = 0; c < C; ++c) vj[c] = st.v[t * W + L.col0 + c * L.slab];
     token_update<NV, C>(s, aa, kk, vj, st.beta[t]);
   }
-  store_tile<DK, C>(S, s, L);
+  store_tile<DK, C, kCommitStoreStream>(S, s, L);
 }
 
 // Per-position commit: copy the state saved after the last accepted token.
@@ -471,8 +507,8 @@ __global__ __launch_bounds__(256) void commit_copy_kernel(Args a) {
   const float *D = a.draft + ((((int64_t)u.b * a.T_max + (n - 1)) * a.H + u.h) * a.dv + (int64_t)u.tile * W) * DK;
   float *S = a.cache + (int64_t)slot * a.slot_stride + ((int64_t)u.h * a.dv + (int64_t)u.tile * W) * DK;
   float4 s[C][NV];
-  load_tile<DK, C>(s, D, L);
-  store_tile<DK, C>(S, s, L);
+  load_tile<DK, C, kCopyLoadStream>(s, D, L);
+  store_tile<DK, C, kCopyStoreStream>(S, s, L);
 }
 
 // ----------------------------------------------------------------------------
@@ -526,10 +562,16 @@ bool launch_of_width(int W, Launch *l) {
 
 bool dims_supported(int dk, int dv) { return (dk == 64 || dk == 128) && (dv == 64 || dv == 128); }
 
-// Launch shape from the batch size and the per-GPU head count: the widest tile
-// that still gives every CU several workgroups; at small B*H fall back to
-// narrow tiles so the state is spread over as many CUs as possible.
-int choose_width(int64_t rows, int H, int dv, bool gate, int requested, int T_max, Launch *l) {
+// Launch shape from the batch size and the per-GPU head count. Measured on
+// MI355X with cold state (fp32, d = 128, H = 32):
+//  * single-token step: the widest tile (64, 32 or 16 columns) that still gives
+//    at least 256 workgroups, i.e. one per CU, so a small batch spreads its state
+//    over the whole chip; once that would exceed 1024 workgroups the step is a
+//    pure stream and one-wave workgroups of 4 columns sustain the highest rate;
+//  * verify and replay commit (T tokens per row, VALU-heavy): 32 columns while
+//    that gives at least 512 workgroups, narrower tiles below that;
+//  * per-position copy commit: 16 columns.
+int choose_width(Kind kind, int64_t rows, int H, int dv, bool gate, int requested, Launch *l) {
   if (gate) {
     if (requested != 0 && requested != dv) return KDA_ERR_UNSUPPORTED;
     return launch_of_width(dv, l) ? KDA_OK : KDA_ERR_UNSUPPORTED;
@@ -539,15 +581,31 @@ int choose_width(int64_t rows, int H, int dv, bool gate, int requested, int T_ma
     return KDA_OK;
   }
   const int64_t heads = rows * H;
-  const int64_t target = 2048;
-  int W = 4;
-  for (int cand : {64, 32, 16, 8}) {
-    if (cand <= dv && heads * (dv / cand) >= target) {
-      W = cand;
+  int W = 16;
+  switch (kind) {
+    case KIND_DECODE:
+      for (int cand : {64, 32, 16}) {
+        if (cand <= dv && heads * (dv / cand) >= 256) {
+          W = cand;
+          break;
+        }
+      }
+      if (heads * (dv / W) > 1024) W = 4;
       break;
-    }
+    case KIND_VERIFY:
+    case KIND_COMMIT_REPLAY:
+      W = 8;
+      for (int cand : {32, 16}) {
+        if (cand <= dv && heads * (dv / cand) >= 512) {
+          W = cand;
+          break;
+        }
+      }
+      break;
+    case KIND_COMMIT_COPY:
+      W = 16;
+      break;
   }
-  (void)T_max;
   return launch_of_width(W, l) ? KDA_OK : KDA_ERR_UNSUPPORTED;
 }
 
@@ -618,7 +676,7 @@ int kda_decode_step(float *cache, int64_t num_slots, int64_t slot_stride, const 
   KDA_TRY(check_gate(epi));
   if (dev_err && !aligned(dev_err, 4)) return KDA_ERR_ALIGN;
   Launch l;
-  KDA_TRY(choose_width(B, H, dv, epi != nullptr, opts ? opts->tile_w : 0, 1, &l));
+  KDA_TRY(choose_width(KIND_DECODE, B, H, dv, epi != nullptr, opts ? opts->tile_w : 0, &l));
 
   Args a;
   memset(&a, 0, sizeof a);
@@ -666,7 +724,7 @@ int kda_verify_chunk(float *cache, int64_t num_slots, int64_t slot_stride, const
   }
   if (dev_err && !aligned(dev_err, 4)) return KDA_ERR_ALIGN;
   Launch l;
-  KDA_TRY(choose_width(B, H, dv, epi != nullptr, opts ? opts->tile_w : 0, T_max, &l));
+  KDA_TRY(choose_width(KIND_VERIFY, B, H, dv, epi != nullptr, opts ? opts->tile_w : 0, &l));
 
   Args a;
   memset(&a, 0, sizeof a);
@@ -725,7 +783,8 @@ int kda_replay_commit(float *cache, int64_t num_slots, int64_t slot_stride, cons
       (dev_err && !aligned(dev_err, 4)))
     return KDA_ERR_ALIGN;
   Launch l;
-  KDA_TRY(choose_width(B, H, dv, false, opts ? opts->tile_w : 0, T_max, &l));
+  KDA_TRY(choose_width(mode == KDA_REPLAY ? KIND_COMMIT_REPLAY : KIND_COMMIT_COPY, B, H, dv, false,
+                       opts ? opts->tile_w : 0, &l));
 
   Args a;
   memset(&a, 0, sizeof a);
@@ -758,12 +817,21 @@ int kda_replay_commit(float *cache, int64_t num_slots, int64_t slot_stride, cons
   return launch(KIND_COMMIT_COPY, false, dk, l, (int64_t)B * H * a.ntile, 0, a, stream);
 }
 
-int kda_query_variant(int32_t B, int32_t H, int32_t dk, int32_t dv, int32_t T_max, int32_t epilogue,
-                      int32_t requested_tile_w, int32_t *tile_w, int32_t *threads) {
+int kda_query_variant(int32_t op, int32_t B, int32_t H, int32_t dk, int32_t dv, int32_t T_max,
+                      int32_t epilogue, int32_t requested_tile_w, int32_t *tile_w, int32_t *threads) {
   if (B < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID;
+  Kind kind;
+  switch (op) {
+    case KDA_OP_DECODE: kind = KIND_DECODE; break;
+    case KDA_OP_VERIFY: kind = KIND_VERIFY; break;
+    case KDA_OP_COMMIT_REPLAY: kind = KIND_COMMIT_REPLAY; break;
+    case KDA_OP_COMMIT_COPY: kind = KIND_COMMIT_COPY; break;
+    default: return KDA_ERR_INVALID;
+  }
   if (!dims_supported(dk, dv) || T_max < 1 || T_max > kMaxT) return KDA_ERR_UNSUPPORTED;
+  if (epilogue && kind != KIND_DECODE && kind != KIND_VERIFY) return KDA_ERR_INVALID;
   Launch l;
-  KDA_TRY(choose_width(B, H, dv, epilogue != 0, requested_tile_w, T_max, &l));
+  KDA_TRY(choose_width(kind, B, H, dv, epilogue != 0, requested_tile_w, &l));
   if (tile_w) *tile_w = l.W;
   if (threads) *threads = 64 * l.waves;
   return KDA_OK;

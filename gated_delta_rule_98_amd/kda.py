@@ -27,6 +27,11 @@ KDA_ERR_HIP = -4
 KDA_REPLAY = 0
 KDA_PER_POSITION = 1
 
+KDA_OP_DECODE = 0
+KDA_OP_VERIFY = 1
+KDA_OP_COMMIT_REPLAY = 2
+KDA_OP_COMMIT_COPY = 3
+
 KDA_DEVERR_SLOT = 1
 KDA_DEVERR_SEQLEN = 2
 KDA_DEVERR_ACCEPTED = 4
@@ -73,7 +78,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_replay_commit.argtypes = [P, i64, i64, P, P, P, i32, i32, i32, i32, i32, i32, i32,
                                       P, P, P, P, P]
     lib.kda_replay_commit.restype = ctypes.c_int
-    lib.kda_query_variant.argtypes = [i32, i32, i32, i32, i32, i32, i32,
+    lib.kda_query_variant.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32,
                                       ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.kda_query_variant.restype = ctypes.c_int
     lib.kda_status_str.argtypes = [i32]
@@ -87,10 +92,10 @@ def kda_status_str(status: int) -> str:
 
 
 def kda_query_variant(B: int, H: int, dk: int, dv: int, T_max: int = 1, epilogue: bool = False,
-                      tile_w: int = 0) -> Tuple[int, int]:
-    """(tile width, threads per workgroup) that a call of this shape launches."""
+                      tile_w: int = 0, op: int = KDA_OP_DECODE) -> Tuple[int, int]:
+    """(tile width, threads per workgroup) that operation ``op`` launches for this shape."""
     w, t = ctypes.c_int32(0), ctypes.c_int32(0)
-    rc = load_library().kda_query_variant(B, H, dk, dv, T_max, int(bool(epilogue)), tile_w,
+    rc = load_library().kda_query_variant(op, B, H, dk, dv, T_max, int(bool(epilogue)), tile_w,
                                           ctypes.byref(w), ctypes.byref(t))
     if rc != KDA_OK:
         raise KdaError(rc, "kda_query_variant")

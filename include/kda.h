@@ -81,6 +81,14 @@ enum kda_mode { KDA_REPLAY = 0, KDA_PER_POSITION = 1 };
 
 enum kda_device_error { KDA_DEVERR_SLOT = 1, KDA_DEVERR_SEQLEN = 2, KDA_DEVERR_ACCEPTED = 4 };
 
+/* Operations, for kda_query_variant. */
+enum kda_op {
+    KDA_OP_DECODE = 0,        /* kda_decode_step */
+    KDA_OP_VERIFY = 1,        /* kda_verify_chunk */
+    KDA_OP_COMMIT_REPLAY = 2, /* kda_replay_commit, mode KDA_REPLAY */
+    KDA_OP_COMMIT_COPY = 3    /* kda_replay_commit, mode KDA_PER_POSITION */
+};
+
 /* Output gate fused into the read-out, per (token, head) over the whole value
  * vector: y = o / sqrt(mean_j o_j^2 + eps) * weight * sigmoid(gate). It is the
  * gating fused at the output of "Hyper Optimizing Kimi K3 in vLLM", section
@@ -163,12 +171,15 @@ int kda_replay_commit(float *cache, int64_t num_slots, int64_t slot_stride,
                       const kda_options *opts, void *stream);
 
 /*
- * Host only. Reports the launch shape a call with these sizes would use
- * (tile_w value columns per workgroup, threads per workgroup), choosing it
- * from the batch size and head count when requested_tile_w == 0. Returns
- * KDA_ERR_UNSUPPORTED for shapes the library does not run.
+ * Host only. Reports the launch shape operation op (a kda_op) would use for
+ * these sizes (tile_w value columns per workgroup, threads per workgroup),
+ * chosen from the batch size and head count when requested_tile_w == 0 (the
+ * scheduling by batch size and per-GPU head count of "Hyper Optimizing Kimi K3
+ * in vLLM", section "Finding time between operators"). Returns
+ * KDA_ERR_UNSUPPORTED for shapes the library does not run, KDA_ERR_INVALID for
+ * an unknown op or non-positive sizes.
  */
-int kda_query_variant(int32_t B, int32_t H, int32_t dk, int32_t dv, int32_t T_max,
+int kda_query_variant(int32_t op, int32_t B, int32_t H, int32_t dk, int32_t dv, int32_t T_max,
                       int32_t epilogue, int32_t requested_tile_w,
                       int32_t *tile_w, int32_t *threads);
 

@@ -46,11 +46,24 @@ def test_python_binding_has_the_same_names():
 
 def test_query_variant_launch_shapes():
     q = kda.kda_query_variant
-    assert q(64, 32, 128, 128) == (64, 256)        # 4096 workgroups of 64 columns
-    assert q(16, 32, 128, 128, T_max=8) == (32, 256)
-    assert q(1, 32, 128, 128) == (4, 64)            # spread B=1 over 1024 workgroups
-    assert q(1, 4, 64, 64) == (4, 64)
-    assert q(64, 32, 128, 128, epilogue=True) == (128, 256)   # the gate needs the whole head
+    D, V, CR, CC = kda.KDA_OP_DECODE, kda.KDA_OP_VERIFY, kda.KDA_OP_COMMIT_REPLAY, kda.KDA_OP_COMMIT_COPY
+    # single-token step: widest tile with >= 256 workgroups; a pure stream past 1024
+    assert q(1, 32, 128, 128) == (16, 256)          # 256 workgroups
+    assert q(2, 32, 128, 128) == (32, 256)
+    assert q(4, 32, 128, 128) == (64, 256)
+    assert q(16, 32, 128, 128) == (64, 256)         # 1024 workgroups
+    assert q(32, 32, 128, 128) == (4, 64)
+    assert q(64, 32, 128, 128) == (4, 64)           # 32768 one-wave workgroups
+    assert q(1, 4, 64, 64) == (16, 256)
+    # verify / replay commit: 32 columns while >= 512 workgroups
+    assert q(16, 32, 128, 128, T_max=8, op=V) == (32, 256)
+    assert q(16, 32, 128, 128, T_max=8, op=CR) == (32, 256)
+    assert q(2, 32, 128, 128, T_max=8, op=V) == (16, 256)
+    assert q(1, 4, 128, 128, T_max=8, op=V) == (8, 128)
+    assert q(16, 32, 128, 128, T_max=8, op=CC) == (16, 256)
+    # the output gate needs the whole head in one workgroup
+    assert q(64, 32, 128, 128, epilogue=True) == (128, 256)
+    assert q(64, 32, 128, 128, T_max=4, epilogue=True, op=V) == (128, 256)
     assert q(64, 32, 128, 64, epilogue=True) == (64, 256)
     for w, threads in ((4, 64), (8, 128), (16, 256), (32, 256), (64, 256), (128, 256)):
         assert q(3, 5, 128, 128, tile_w=w) == (w, threads)
@@ -67,9 +80,12 @@ def test_query_variant_launch_shapes():
         with pytest.raises(kda.KdaError) as e:
             q(**args)
         assert e.value.status == kda.KDA_ERR_UNSUPPORTED
-    with pytest.raises(kda.KdaError) as e:
-        q(2, 0, 128, 128)
-    assert e.value.status == kda.KDA_ERR_INVALID
+    for bad in (dict(H=0), dict(op=7), dict(op=CC, epilogue=True)):
+        args = dict(B=2, H=2, dk=128, dv=128)
+        args.update(bad)
+        with pytest.raises(kda.KdaError) as e:
+            q(**args)
+        assert e.value.status == kda.KDA_ERR_INVALID
 
 
 def test_status_strings():
