@@ -35,6 +35,12 @@
 namespace {
 
 constexpr int kMaxT = 16;
+constexpr int kMaxWaves = 16;  // waves in the largest (1024-thread) workgroup
+constexpr int kMaxDv = 128;
+// Slabs per lane when the output gate makes one workgroup own all dv columns
+// (waves = dv / (4 * slabs)); measured on MI355X.
+constexpr int kGateSlabsDecode = 2;
+constexpr int kGateSlabsVerify = 4;
 
 struct Args {
   float *cache;
@@ -242,27 +248,42 @@ constexpr bool kCommitStoreStream = true;   // rebuilt state written by the repl
 constexpr bool kCopyLoadStream = false;     // per-position state read by the copy commit
 constexpr bool kCopyStoreStream = false;    // committed state written by the copy commit
 
-// Output gate over the head's whole value vector (the tile spans all of dv):
-// o <- o / sqrt(mean(o^2) + eps) * weight * sigmoid(gate). part: LDS, >= slab floats.
+__device__ __forceinline__ float readlane_f32(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+// Output gate over the head's whole value vector (the workgroup spans all of dv):
+// y = o / sqrt(mean(o^2) + eps) * weight * sigmoid(gate).
+//
+// gate_partial: the wave's sum of squares of its columns' outputs (its four
+// column groups in a fixed order), written to part[wave] by lane 0.
 template <int C>
-__device__ __forceinline__ void output_gate(const Args &a, float (&o)[C], int64_t gbase,
-                                            const Lane &L, float *part) {
+__device__ __forceinline__ void gate_partial(const float (&o)[C], float *part) {
   float ss = o[0] * o[0];
 #pragma unroll
   for (int c = 1; c < C; ++c) ss = __builtin_fmaf(o[c], o[c], ss);
-  if (L.r == 0) part[L.col0] = ss;
-  __syncthreads();
+  const float wave_ss = (readlane_f32(ss, 0) + readlane_f32(ss, 16)) + (readlane_f32(ss, 32) + readlane_f32(ss, 48));
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = wave_ss;
+}
+
+// gate_apply: after a barrier, y for one column from the head's wave partials
+// (summed over the waves in a fixed order), its raw output oc, its gate g and
+// its weight w.
+__device__ __forceinline__ float gate_apply(const Args &a, const float *part, float oc, float g, float w) {
+  const int waves = blockDim.x >> 6;
   float tot = part[0];
-  for (int i = 1; i < L.slab; ++i) tot += part[i];
-  __syncthreads();
+  for (int i = 1; i < waves; ++i) tot += part[i];
   const float inv_rms = 1.0f / sqrtf(tot / (float)a.dv + a.eps);
+  return oc * inv_rms * w * (1.0f / (1.0f + expf(-g)));
+}
+
+// Writes the C column outputs of each 16-lane row to dst[col0 + c * slab]: lane
+// r == c stores column c (every lane of the row holds all C values).
+template <int C>
+__device__ __forceinline__ void store_cols(float *dst, const Lane &L, const float (&o)[C]) {
 #pragma unroll
-  for (int c = 0; c < C; ++c) {
-    const int j = L.col0 + c * L.slab;
-    const float g = bf16_to_f32(a.gate[gbase + j]);
-    const float w = a.weight ? a.weight[j] : 1.0f;
-    o[c] = o[c] * inv_rms * w * (1.0f / (1.0f + expf(-g)));
-  }
+  for (int c = 0; c < C; ++c)
+    if (L.r == c) dst[L.col0 + c * L.slab] = o[c];
 }
 
 // ----------------------------------------------------------------------------
@@ -272,7 +293,7 @@ __device__ __forceinline__ void output_gate(const Args &a, float (&o)[C], int64_
 // Single-token step, in place. Inputs go straight to registers: a lane's key
 // channels are fixed, so it loads exactly the k, q, alpha it uses.
 template <int DK, int C, bool GATE>
-__global__ __launch_bounds__(256) void decode_kernel(Args a) {
+__global__ __launch_bounds__(GATE ? 1024 : 256) void decode_kernel(Args a) {
   constexpr int NV = DK / 64;
   const Unit u = unit_of_block(a.ntile, a.H);
   const int32_t slot = a.slot_ids[u.b];
@@ -301,44 +322,58 @@ __global__ __launch_bounds__(256) void decode_kernel(Args a) {
 #pragma unroll
   for (int c = 0; c < C; ++c) vj[c] = bf16_to_f32(a.v[vbase + L.col0 + c * L.slab]);
   const float beta = a.beta[th];
+  float gj = 0.0f, wj = 1.0f;
+  if constexpr (GATE) {
+    const int j = L.col0 + (L.r < C ? L.r : 0) * L.slab;
+    gj = bf16_to_f32(a.gate[vbase + j]);
+    if (a.weight) wj = a.weight[j];
+  }
 
   token_update<NV, C>(s, aa, kk, vj, beta);
   float o[C];
   token_readout<NV, C>(s, qq, o);
   store_tile<DK, C, kDecodeStoreStream>(S, s, L);
   if constexpr (GATE) {
-    __shared__ float part[16];
-    output_gate<C>(a, o, vbase, L, part);
+    __shared__ float part[kMaxWaves];
+    __shared__ float raw[kMaxDv];
+    store_cols<C>(raw, L, o);
+    gate_partial<C>(o, part);
+    __syncthreads();
+    if (L.r < C) {
+      const int j = L.col0 + L.r * L.slab;
+      a.out[vbase + j] = gate_apply(a, part, raw[j], gj, wj);
+    }
+  } else {
+    store_cols<C>(a.out + vbase, L, o);
   }
-#pragma unroll
-  for (int c = 0; c < C; ++c)
-    if (L.r == c) a.out[vbase + L.col0 + c * L.slab] = o[c];
 }
 
 // LDS staging for a chunk of tokens: k, q, alpha as float [T_max][DK], the
-// tile's v as float [T_max][W], beta [T_max].
+// tile's v as float [T_max][W], beta [T_max], and with the output gate the
+// tile's gate as float [T_max][W].
 template <int DK>
 struct Staged {
-  float *k, *q, *a, *v, *beta;
+  float *k, *q, *a, *v, *beta, *g;
   __device__ Staged(float *base, int T_max, int W) {
     k = base;
     q = k + T_max * DK;
     a = q + T_max * DK;
     v = a + T_max * DK;
     beta = v + T_max * W;
+    g = beta + T_max;
   }
 };
 
 // Dynamic LDS bytes for Staged<dk>, rounded up to 16.
-inline size_t staged_bytes(int dk, int T_max, int W) {
-  return ((size_t)T_max * (3 * dk + W + 1) * sizeof(float) + 15) / 16 * 16;
+inline size_t staged_bytes(int dk, int T_max, int W, bool gate) {
+  return ((size_t)T_max * (3 * dk + W + 1 + (gate ? W : 0)) * sizeof(float) + 15) / 16 * 16;
 }
 
 // Speculative verify over a packed chunk: T_b tokens with the state in
 // registers; outputs per token; the committed slot stays untouched unless the
 // row is a single in-place token.
 template <int DK, int C, bool GATE>
-__global__ __launch_bounds__(256) void verify_kernel(Args a) {
+__global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
   constexpr int NV = DK / 64;
   extern __shared__ float4 lds_dyn[];
   const Unit u = unit_of_block(a.ntile, a.H);
@@ -383,6 +418,7 @@ __global__ __launch_bounds__(256) void verify_kernel(Args a) {
     const uint16_t vb = a.v[((row0 + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj];
     st.v[t * W + jj] = bf16_to_f32(vb);
     if (replay) a.rv[(((int64_t)u.b * a.T_max + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj] = vb;
+    if constexpr (GATE) st.g[t * W + jj] = bf16_to_f32(a.gate[((row0 + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj]);
   }
   if ((int)threadIdx.x < Tb) {
     const float bt = a.beta[(row0 + threadIdx.x) * a.H + u.h];
@@ -394,7 +430,8 @@ __global__ __launch_bounds__(256) void verify_kernel(Args a) {
   float *S = a.cache + (int64_t)slot * a.slot_stride + ((int64_t)u.h * a.dv + (int64_t)u.tile * W) * DK;
   float4 s[C][NV];
   load_tile<DK, C, kVerifyLoadStream>(s, S, L);
-  __shared__ float part[16];
+  __shared__ float part[GATE ? kMaxT * kMaxWaves : 1];
+  __shared__ float raw[GATE ? kMaxT * kMaxDv : 1];
 
   for (int t = 0; t < Tb; ++t) {
     float4 kk[NV], qq[NV], aa[NV];
@@ -412,16 +449,31 @@ __global__ __launch_bounds__(256) void verify_kernel(Args a) {
     float o[C];
     token_readout<NV, C>(s, qq, o);
     const int64_t obase = ((row0 + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W;
-    if constexpr (GATE) output_gate<C>(a, o, obase, L, part);
-#pragma unroll
-    for (int c = 0; c < C; ++c)
-      if (L.r == c) a.out[obase + L.col0 + c * L.slab] = o[c];
+    if constexpr (GATE) {
+      // keep the raw read-out in LDS; the whole chunk is normalized after the loop
+      store_cols<C>(raw + t * kMaxDv, L, o);
+      gate_partial<C>(o, part + t * kMaxWaves);
+    } else {
+      store_cols<C>(a.out + obase, L, o);
+    }
     if (perpos) {
       float *D = a.draft + ((((int64_t)u.b * a.T_max + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W) * DK;
       store_tile<DK, C, kVerifyStoreStream>(D, s, L);
     }
   }
   if (inplace) store_tile<DK, C, kVerifyStoreStream>(S, s, L);
+  if constexpr (GATE) {
+    // one barrier for the whole chunk, then each lane finishes its column per token
+    __syncthreads();
+    if (L.r < C) {
+      const int j = L.col0 + L.r * L.slab;
+      const float wj = a.weight ? a.weight[j] : 1.0f;
+      for (int t = 0; t < Tb; ++t) {
+        const int64_t obase = ((row0 + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W;
+        a.out[obase + j] = gate_apply(a, part + t * kMaxWaves, raw[t * kMaxDv + j], st.g[t * W + j], wj);
+      }
+    }
+  }
 }
 
 // Row checks shared by the commit kernels; returns the accepted length, or -1
@@ -517,13 +569,20 @@ __global__ __launch_bounds__(256) void commit_copy_kernel(Args a) {
 
 enum Kind { KIND_DECODE, KIND_VERIFY, KIND_COMMIT_REPLAY, KIND_COMMIT_COPY };
 
+// Gated launches use a fixed number of slabs per lane for each op (see
+// choose_width); only those are instantiated with the gate.
 template <int DK, int C>
 const void *kernel_for(Kind kind, bool gate) {
+  if constexpr (C == kGateSlabsDecode)
+    if (gate && kind == KIND_DECODE) return (const void *)decode_kernel<DK, C, true>;
+  if constexpr (C == kGateSlabsVerify)
+    if (gate && kind == KIND_VERIFY) return (const void *)verify_kernel<DK, C, true>;
+  if (gate) return nullptr;
   switch (kind) {
     case KIND_DECODE:
-      return gate ? (const void *)decode_kernel<DK, C, true> : (const void *)decode_kernel<DK, C, false>;
+      return (const void *)decode_kernel<DK, C, false>;
     case KIND_VERIFY:
-      return gate ? (const void *)verify_kernel<DK, C, true> : (const void *)verify_kernel<DK, C, false>;
+      return (const void *)verify_kernel<DK, C, false>;
     case KIND_COMMIT_REPLAY:
       return (const void *)commit_replay_kernel<DK, C>;
     case KIND_COMMIT_COPY:
@@ -573,8 +632,13 @@ bool dims_supported(int dk, int dv) { return (dk == 64 || dk == 128) && (dv == 6
 //  * per-position copy commit: 16 columns.
 int choose_width(Kind kind, int64_t rows, int H, int dv, bool gate, int requested, Launch *l) {
   if (gate) {
+    // the gate's RMS norm spans the whole head: one workgroup owns all dv columns,
+    // with two slabs per lane (1024 threads at dv = 128) to keep registers low
     if (requested != 0 && requested != dv) return KDA_ERR_UNSUPPORTED;
-    return launch_of_width(dv, l) ? KDA_OK : KDA_ERR_UNSUPPORTED;
+    if (dv != 64 && dv != 128) return KDA_ERR_UNSUPPORTED;
+    const int C = kind == KIND_DECODE ? kGateSlabsDecode : kGateSlabsVerify;
+    *l = {dv, dv / (4 * C), C};
+    return KDA_OK;
   }
   if (requested != 0) {
     if (requested > dv || dv % requested != 0 || !launch_of_width(requested, l)) return KDA_ERR_UNSUPPORTED;
@@ -759,8 +823,8 @@ int kda_verify_chunk(float *cache, int64_t num_slots, int64_t slot_stride, const
   a.ntile = dv / l.W;
   a.mode = mode;
   a.t1_inplace = t1_inplace ? 1 : 0;
-  return launch(KIND_VERIFY, epi != nullptr, dk, l, (int64_t)B * H * a.ntile, staged_bytes(dk, T_max, l.W), a,
-                stream);
+  return launch(KIND_VERIFY, epi != nullptr, dk, l, (int64_t)B * H * a.ntile, staged_bytes(dk, T_max, l.W, epi != nullptr),
+                a, stream);
 }
 
 int kda_replay_commit(float *cache, int64_t num_slots, int64_t slot_stride, const int32_t *slot_ids,
@@ -811,7 +875,7 @@ int kda_replay_commit(float *cache, int64_t num_slots, int64_t slot_stride, cons
   a.ntile = dv / l.W;
   a.mode = mode;
   if (mode == KDA_REPLAY) {
-    return launch(KIND_COMMIT_REPLAY, false, dk, l, (int64_t)B * H * a.ntile, staged_bytes(dk, T_max, l.W), a,
+    return launch(KIND_COMMIT_REPLAY, false, dk, l, (int64_t)B * H * a.ntile, staged_bytes(dk, T_max, l.W, false), a,
                   stream);
   }
   return launch(KIND_COMMIT_COPY, false, dk, l, (int64_t)B * H * a.ntile, 0, a, stream);
