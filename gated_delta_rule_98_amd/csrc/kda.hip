@@ -675,15 +675,19 @@ int choose_width(Kind kind, int64_t rows, int H, int dv, bool gate, int requeste
 
 bool aligned(const void *p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
 
+int launch_fn(const void *fn, int64_t blocks, int threads, size_t shmem, Args &a, void *stream) {
+  if (!fn) return KDA_ERR_UNSUPPORTED;
+  void *args[] = {&a};
+  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(threads), args, shmem,
+                                       (hipStream_t)stream);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 int launch(Kind kind, bool gate, int dk, const Launch &l, int64_t units, size_t shmem, Args &a,
            void *stream) {
   if (units > 0x7fffffff) return KDA_ERR_UNSUPPORTED;
   const void *fn = dk == 64 ? kernel_for_c<64>(kind, gate, l.C) : kernel_for_c<128>(kind, gate, l.C);
-  if (!fn) return KDA_ERR_UNSUPPORTED;
-  void *args[] = {&a};
-  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)units), dim3(64 * l.waves), args, shmem,
-                                       (hipStream_t)stream);
-  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  return launch_fn(fn, units, 64 * l.waves, shmem, a, stream);
 }
 
 int check_cache(const float *cache, int64_t num_slots, int64_t slot_stride, int H, int dk, int dv) {
@@ -764,7 +768,9 @@ int kda_decode_step(float *cache, int64_t num_slots, int64_t slot_stride, const 
   a.T_max = 1;
   a.n_tok = B;
   a.ntile = dv / l.W;
-  return launch(KIND_DECODE, epi != nullptr, dk, l, (int64_t)B * H * a.ntile, 0, a, stream);
+  const int64_t units = (int64_t)B * H * a.ntile;
+  if (units > 0x7fffffff) return KDA_ERR_UNSUPPORTED;
+  return launch(KIND_DECODE, epi != nullptr, dk, l, units, 0, a, stream);
 }
 
 int kda_verify_chunk(float *cache, int64_t num_slots, int64_t slot_stride, const int32_t *slot_ids,

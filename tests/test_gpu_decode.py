@@ -108,7 +108,9 @@ def test_tile_widths_are_bit_identical(dk, dv):
             assert np.array_equal(got[0], first[0]) and np.array_equal(got[1], first[1]), tw
 
 
-def test_padding_and_out_of_range_slot():
+@pytest.mark.parametrize("tile_w", [0, 4])
+def test_padding_and_out_of_range_slot(tile_w):
+    """Padding rows and a slot past the cache; tile_w=4 is the one-wave large-batch launch."""
     w = synth.make(7, 4, 128, 128, num_slots=12, state_std=0.05, seed=22)
     slots = w.slot_ids.copy()
     slots[2] = -1                     # padding row
@@ -117,8 +119,9 @@ def test_padding_and_out_of_range_slot():
     cache_d = f32(w.cache)
     out = sentinel((w.B, w.H, w.dv))
     err = torch.zeros(1, dtype=torch.int32, device=dev())
-    log("padding and out-of-range slot")
-    K.kda_decode_step(cache_d, i32(slots), x["q"], x["k"], x["v"], x["alpha"], x["beta"], out, dev_err=err)
+    log(f"padding and out-of-range slot, tile_w={tile_w}")
+    K.kda_decode_step(cache_d, i32(slots), x["q"], x["k"], x["v"], x["alpha"], x["beta"], out, dev_err=err,
+                      tile_w=tile_w)
     torch.cuda.synchronize()
     cache_h = w.cache.copy()
     ref = np.full((w.B, w.H, w.dv), np.nan, np.float32)
