@@ -289,6 +289,18 @@ def spec_verify(D, K, synth, reps):
                          tile_w=K.kda_query_variant(w.B, H, d, d, T_max=T, op=K.KDA_OP_VERIFY)[0])
         log(f"spec_verify {name}: verify {v_ms * 1e3:.2f} us ({vb / v_ms / 1e6:.0f} GB/s), "
             f"commit {c_ms * 1e3:.2f} us ({cb / c_ms / 1e6:.0f} GB/s), verify+commit {p_ms * 1e3:.2f} us")
+
+    # the replay-mode verify in chunk form (MFMA products with the committed state), for comparison
+    def verify_chunked(i):
+        K.kda_verify_chunk(cache, tables[i % len(tables)], cu, T, x["q"], x["k"], x["v"], x["alpha"], x["beta"],
+                           out, mode=0, replay=rbs[i % 4], verify_form=K.KDA_VERIFY_CHUNKED)
+
+    for i in range(8):
+        verify_chunked(i)
+    ch_ms = timed_region(D, verify_chunked, reps) / reps
+    vb = verify_bytes(w.n_tok, w.B, H, d, d, 0, T)
+    res["replay_chunked_form"] = dict(verify_us=round(ch_ms * 1e3, 3), verify_gbs=round(vb / ch_ms / 1e6, 1))
+    log(f"spec_verify replay, chunk form: verify {ch_ms * 1e3:.2f} us")
     return res
 
 

@@ -20,6 +20,9 @@ from .kda import (  # noqa: F401
     KDA_OP_VERIFY,
     KDA_PER_POSITION,
     KDA_REPLAY,
+    KDA_VERIFY_AUTO,
+    KDA_VERIFY_CHUNKED,
+    KDA_VERIFY_RECURRENT,
     LIB_PATH,
     KdaError,
     kda_decode_step,

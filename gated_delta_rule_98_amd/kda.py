@@ -32,6 +32,10 @@ KDA_OP_VERIFY = 1
 KDA_OP_COMMIT_REPLAY = 2
 KDA_OP_COMMIT_COPY = 3
 
+KDA_VERIFY_AUTO = 0
+KDA_VERIFY_RECURRENT = 1
+KDA_VERIFY_CHUNKED = 2
+
 KDA_DEVERR_SLOT = 1
 KDA_DEVERR_SEQLEN = 2
 KDA_DEVERR_ACCEPTED = 4
@@ -53,7 +57,7 @@ class kda_replay_buf(ctypes.Structure):
 
 
 class kda_options(ctypes.Structure):
-    _fields_ = [("tile_w", ctypes.c_int32)]
+    _fields_ = [("tile_w", ctypes.c_int32), ("verify_form", ctypes.c_int32)]
 
 
 _lib = None
@@ -167,8 +171,8 @@ def _epilogue(gate, weight, eps):
     return kda_epilogue(gate.data_ptr(), _ptr(weight), float(eps))
 
 
-def _opts(tile_w: int):
-    return kda_options(int(tile_w)) if tile_w else None
+def _opts(tile_w: int, verify_form: int = 0):
+    return kda_options(int(tile_w), int(verify_form)) if (tile_w or verify_form) else None
 
 
 def _ref(x):
@@ -210,7 +214,8 @@ def kda_verify_chunk(cache: torch.Tensor, slot_ids: torch.Tensor, cu_seqlens: to
                      T_max: int, q, k, v, alpha, beta, out: torch.Tensor, *, mode: int = KDA_REPLAY,
                      t1_inplace: bool = False, replay: Optional[dict] = None,
                      draft: Optional[torch.Tensor] = None, gate=None, weight=None, eps: float = 1e-6,
-                     dev_err: Optional[torch.Tensor] = None, tile_w: int = 0, stream=None) -> None:
+                     dev_err: Optional[torch.Tensor] = None, tile_w: int = 0, verify_form: int = 0,
+                     stream=None) -> None:
     """Packed speculative chunk; token arrays are [n_tok, H, .], row b owns tokens
     [cu[b], cu[b+1]). replay = dict(k, v, alpha, beta) with shapes [B, T_max, H, .]
     (mode KDA_REPLAY); draft float32 [B, T_max, H, dv, dk] (mode KDA_PER_POSITION)."""
@@ -240,7 +245,7 @@ def kda_verify_chunk(cache: torch.Tensor, slot_ids: torch.Tensor, cu_seqlens: to
         cache.data_ptr(), ns, stride, slot_ids.data_ptr(), cu_seqlens.data_ptr(), B, int(T_max),
         n_tok, H, dk, dv, q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(), beta.data_ptr(),
         out.data_ptr(), _ref(epi), int(mode), int(bool(t1_inplace)), _ref(rb), _ptr(draft),
-        _ptr(dev_err), _ref(_opts(tile_w)), _stream(stream))
+        _ptr(dev_err), _ref(_opts(tile_w, verify_form)), _stream(stream))
     if rc != KDA_OK:
         raise KdaError(rc, "kda_verify_chunk")
 

@@ -109,11 +109,29 @@ typedef struct kda_replay_buf {
     float *beta;  /* [B][T_max][H] */
 } kda_replay_buf;
 
-/* Launch options (host struct, may be NULL). */
+/* How kda_verify_chunk computes its outputs.
+ *   KDA_VERIFY_RECURRENT: token by token on the state, the same arithmetic as
+ *     kda_decode_step (outputs bit-identical to successive decode steps).
+ *   KDA_VERIFY_CHUNKED: the chunk form of the same recurrence. Decays are
+ *     accumulated per key channel, the state products (decayed keys and queries
+ *     times the committed state) run on MFMA, and the coupling between the
+ *     chunk's tokens is a small triangular solve. It needs no state until the
+ *     commit, so it serves KDA_REPLAY rows that are not updated in place and
+ *     have no output gate. Outputs agree with the recurrent form to rounding;
+ *     replay buffers and committed states are identical.
+ *   KDA_VERIFY_AUTO: the faster form on MI355X, currently the recurrent one
+ *     (the chunk form's per-head coupling and triangular solve cost more than
+ *     the MFMA products save at up to 16 tokens). */
+enum kda_verify_form { KDA_VERIFY_AUTO = 0, KDA_VERIFY_RECURRENT = 1, KDA_VERIFY_CHUNKED = 2 };
+
+/* Launch options (host struct, may be NULL = all zero). */
 typedef struct kda_options {
-    int32_t tile_w; /* value columns per workgroup: 0 = chosen from (B, H); otherwise one of
-                       4, 8, 16, 32, 64, 128 with tile_w <= dv (and tile_w == dv with the gate).
-                       Results are bit-identical for every legal width. */
+    int32_t tile_w;      /* value columns per workgroup of the recurrent kernels: 0 = chosen from
+                            (B, H); otherwise one of 4, 8, 16, 32, 64, 128 with tile_w <= dv (and
+                            tile_w == dv with the gate). Results are bit-identical for every legal
+                            width. */
+    int32_t verify_form; /* a kda_verify_form; KDA_VERIFY_CHUNKED where it does not apply is
+                            KDA_ERR_UNSUPPORTED */
 } kda_options;
 
 /*

@@ -25,7 +25,7 @@ STATE_TOL = 1e-3
 
 
 def _verify(w, cache_d, mode, *, t1_inplace=False, gate=False, weight=None, tile_w=0, slots=None, cu=None,
-            dev_err=None):
+            dev_err=None, form=0):
     x = step_inputs(w, 0)
     slots = w.slot_ids if slots is None else slots
     cu = w.cu_seqlens if cu is None else cu
@@ -35,7 +35,7 @@ def _verify(w, cache_d, mode, *, t1_inplace=False, gate=False, weight=None, tile
     K.kda_verify_chunk(cache_d, i32(slots), i32(cu), w.T_max, x["q"], x["k"], x["v"], x["alpha"], x["beta"],
                        out, mode=mode, t1_inplace=t1_inplace, replay=rb, draft=draft,
                        gate=x["gate"] if gate else None, weight=weight, eps=1e-6, dev_err=dev_err,
-                       tile_w=tile_w)
+                       tile_w=tile_w, verify_form=form)
     return out, rb, draft
 
 
@@ -80,8 +80,9 @@ def test_spec_verify_both_modes_and_commit():
         _commit(w, cache_d, mode, acc, rb, draft)
         torch.cuda.synchronize()
         results[mode] = (bits(out), bits(cache_d))
-    # both modes: same outputs, same committed slot bits
-    assert np.array_equal(results[0][0], results[1][0])
+    # both modes: the same committed slot bits; outputs agree to rounding (replay mode
+    # computes them in chunk form, per-position mode token by token)
+    assert rel_l2(results[0][0].view(np.float32), results[1][0].view(np.float32)) <= 1e-5
     assert np.array_equal(results[0][1], results[1][1])
     cache_h = w.cache.copy()
     assert oracle.commit(cache_h, w.slot_ids, w.cu_seqlens, acc, w.T_max, w.k[0], w.v[0], w.alpha[0],
@@ -111,13 +112,17 @@ def test_commit_equals_single_token_steps_bitwise():
         K.kda_decode_step(steps_d, i32(masked), tok["q"], tok["k"], tok["v"], tok["alpha"], tok["beta"], o)
         K.kda_decode_step(all_d, i32(w.slot_ids), tok["q"], tok["k"], tok["v"], tok["alpha"], tok["beta"], o)
         dec_out[r] = o
-    cache_r = f32(w.cache)
-    log("verify + replay commit")
-    out, rb, _ = _verify(w, cache_r, K.KDA_REPLAY)
-    _commit(w, cache_r, K.KDA_REPLAY, acc, rb, None)
-    torch.cuda.synchronize()
-    assert np.array_equal(bits(cache_r), bits(steps_d))
-    assert np.array_equal(bits(out), bits(dec_out))
+    for form in (K.KDA_VERIFY_RECURRENT, K.KDA_VERIFY_CHUNKED):
+        cache_r = f32(w.cache)
+        log(f"verify (form {form}) + replay commit")
+        out, rb, _ = _verify(w, cache_r, K.KDA_REPLAY, form=form)
+        _commit(w, cache_r, K.KDA_REPLAY, acc, rb, None)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(cache_r), bits(steps_d))
+        if form == K.KDA_VERIFY_RECURRENT:
+            assert np.array_equal(bits(out), bits(dec_out))
+        else:
+            assert rel_l2(out.cpu().numpy(), dec_out.cpu().numpy()) <= 1e-5
 
 
 def test_mixed_batch_inplace_gate_and_commit():
@@ -182,7 +187,11 @@ def test_ragged_rows_both_modes(dk, dv):
         _commit(w, cache_d, mode, acc, rb, draft, slots=slots)
         torch.cuda.synchronize()
         res[mode] = (bits(out), bits(cache_d))
-    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
+    o0, o1 = res[0][0].view(np.float32), res[1][0].view(np.float32)
+    live_rows = ~np.isnan(o1).any(axis=(1, 2))
+    assert rel_l2(o0[live_rows], o1[live_rows]) <= 1e-5
+    assert np.array_equal(res[0][0][~live_rows], res[1][0][~live_rows])     # padding rows untouched
+    assert np.array_equal(res[0][1], res[1][1])
     cache_h = w.cache.copy()
     assert oracle.commit(cache_h, slots, w.cu_seqlens, acc, w.T_max, w.k[0], w.v[0], w.alpha[0], w.beta[0]) == 0
     got = res[0][1].view(np.float32)
@@ -265,3 +274,70 @@ def test_empty_chunk_is_a_no_op():
                        draft=torch.zeros(3, 4, 2, 64, 64, device=dev()))
     torch.cuda.synchronize()
     assert float(cache.abs().sum()) == 0.0
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
+def test_chunked_form_matches_oracle_and_recurrent_form(dk, dv):
+    """Replay-mode verify in chunk form (MFMA products with the committed state):
+    every length from 1 to 16, a padding row, decays spanning (0, 1)."""
+    seqlens = [1, 2, 3, 5, 7, 8, 9, 11, 13, 15, 16, 4]
+    w = synth.make(len(seqlens), 6, dk, dv, seqlens=seqlens, num_slots=16, state_std=0.05, seed=51)
+    slots = w.slot_ids.copy()
+    slots[3] = -1
+    ref_out, ref_rb, _, rc = _oracle_verify(w, K.KDA_REPLAY, slots=slots)
+    assert rc == 0
+    live = np.concatenate([np.arange(w.cu_seqlens[b], w.cu_seqlens[b + 1]) for b in range(w.B) if b != 3])
+    pad = np.arange(w.cu_seqlens[3], w.cu_seqlens[4])
+    outs = {}
+    for form in (K.KDA_VERIFY_CHUNKED, K.KDA_VERIFY_RECURRENT):
+        cache_d = f32(w.cache)
+        log(f"chunked vs recurrent dk={dk} dv={dv}: form {form}")
+        out, rb, _ = _verify(w, cache_d, K.KDA_REPLAY, slots=slots, form=form)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        err = rel_l2(o[live], ref_out[live])
+        log(f"  outputs rel-L2 vs oracle {err:.3e}")
+        assert err <= OUT_TOL
+        assert np.all(bits(out)[pad] == SENTINEL_BITS)
+        assert np.array_equal(bits(cache_d), w.cache.view(np.uint32))
+        for key, rk in (("k", "rk"), ("v", "rv")):
+            got = bits(rb[key])
+            for b in range(w.B):
+                if b != 3:
+                    n = w.seqlens[b]
+                    assert np.array_equal(got[b, :n], ref_rb[rk][b, :n])
+        outs[form] = o
+    assert rel_l2(outs[K.KDA_VERIFY_CHUNKED][live], outs[K.KDA_VERIFY_RECURRENT][live]) <= 1e-5
+
+
+def test_chunked_form_with_extreme_decays():
+    """Decays near 0 and exactly 1 in the same chunk: running products stay finite."""
+    w = synth.make(3, 4, 128, 128, seqlens=[16, 16, 9], num_slots=4, state_std=0.05, seed=52)
+    rng = np.random.Generator(np.random.PCG64(53))
+    alpha = w.alpha.copy()
+    alpha[0, :16] = np.where(rng.random(alpha[0, :16].shape) < 0.3, 1e-30, alpha[0, :16])
+    alpha[0, 16:32] = 1.0
+    alpha[0, 32:] = 1e-7
+    w.alpha = alpha.astype(np.float32)
+    ref_out, _, _, rc = _oracle_verify(w, K.KDA_REPLAY)
+    assert rc == 0
+    cache_d = f32(w.cache)
+    log("chunked form, extreme decays")
+    out, _, _ = _verify(w, cache_d, K.KDA_REPLAY, form=K.KDA_VERIFY_CHUNKED)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(np.isfinite(o))
+    assert rel_l2(o, ref_out) <= OUT_TOL
+
+
+def test_chunked_form_rejected_where_it_does_not_apply():
+    w = synth.make(2, 2, 128, 128, seqlens=[2, 3], num_slots=3, state_std=0.05, seed=54)
+    cache_d = f32(w.cache)
+    for kw in (dict(mode=K.KDA_PER_POSITION), dict(mode=K.KDA_REPLAY, t1_inplace=True),
+               dict(mode=K.KDA_REPLAY, gate=True), dict(mode=K.KDA_REPLAY, tile_w=32)):
+        mode = kw.pop("mode")
+        if kw.get("gate"):
+            w.gate = synth.make(2, 2, 128, 128, seqlens=[2, 3], gate=True, seed=55).gate
+        with pytest.raises(K.KdaError) as e:
+            _verify(w, cache_d, mode, form=K.KDA_VERIFY_CHUNKED, **kw)
+        assert e.value.status == K.KDA_ERR_UNSUPPORTED
