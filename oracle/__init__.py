@@ -34,6 +34,7 @@ PER_POSITION = 1
 ERR_SLOT = 1
 ERR_SEQLEN = 2
 ERR_ACCEPTED = 4
+ERR_CKPT = 8
 
 _lib = None
 
@@ -63,6 +64,9 @@ def _load(path: Optional[str] = None):
     lib.kda_oracle_commit.argtypes = [P, i64, i64, P, P, P, i32, i32, i32, i32, i32, i32,
                                       P, P, P, P, i32, i32]
     lib.kda_oracle_commit.restype = ctypes.c_int
+    lib.kda_oracle_prefill.argtypes = [P, i64, i64, P, P, i32, i32, i32, i32, i32,
+                                       P, P, P, P, P, P, P, P, i32, i32]
+    lib.kda_oracle_prefill.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -216,3 +220,30 @@ def commit(cache, slot_ids, cu_seqlens, accepted_len, T_max, k, v, alpha, beta, 
     if rc < 0:
         raise ValueError("oracle commit: invalid arguments")
     return rc
+
+
+def prefill(cache, slot_ids, cu_seqlens, q, k, v, alpha, beta, *, ckpt_pos=None, out=None,
+            state_fp32: bool = True, nthreads: Optional[int] = None, lib=None):
+    """Whole prompts in one pass (in place on ``cache``). Token arrays are [n_tok][H][.];
+    row b owns tokens [cu[b], cu[b+1]). Returns (out [n_tok][H][dv], ckpt [B][H][dv][dk]
+    or None, error bits); ckpt[b] is the state after the first ckpt_pos[b] tokens."""
+    lib = lib or _load()
+    assert cache.dtype == np.float32 and cache.flags.c_contiguous
+    num_slots, H, dv, dk = cache.shape
+    slot_ids = _c(slot_ids, np.int32)
+    cu = _c(cu_seqlens, np.int32)
+    B = slot_ids.shape[0]
+    n_tok = int(k.shape[0])
+    q, k, v = (_c(x, np.uint16) for x in (q, k, v))
+    alpha, beta = (_c(x, np.float32) for x in (alpha, beta))
+    pos = _c(ckpt_pos, np.int32)
+    ckpt = np.full((B, H, dv, dk), np.nan, np.float32) if pos is not None else None
+    if out is None:
+        out = np.full((n_tok, H, dv), np.nan, np.float32)
+    rc = lib.kda_oracle_prefill(_ptr(cache), num_slots, _slot_stride(cache), _ptr(slot_ids), _ptr(cu),
+                                B, n_tok, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                _ptr(out), _ptr(pos), _ptr(ckpt), int(state_fp32),
+                                nthreads or default_threads())
+    if rc < 0:
+        raise ValueError("oracle prefill: invalid arguments")
+    return out, ckpt, rc

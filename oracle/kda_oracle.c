@@ -44,7 +44,14 @@
  * Slot and row handling: slot < 0 is padding (nothing read or written);
  * slot >= num_slots sets error bit 1; a row whose token range is decreasing,
  * out of [0, n_tok] or longer than T_max sets bit 2; an accepted length
- * outside [0, T_b] sets bit 4. A row with an error is skipped entirely.
+ * outside [0, T_b] sets bit 4; a checkpoint position outside [0, T_b] (prefill)
+ * sets bit 8. A row with an error is skipped entirely.
+ *
+ * Prefill ("Kimi K3 performance optimization in vLLM", section "Internal KDA
+ * prefix checkpoint"): one pass over a row's whole prompt from the slot's
+ * state, outputs for every token, the final state written back to the slot,
+ * and, in the same pass, the state after the first ckpt_pos[b] tokens exported
+ * to a checkpoint buffer [B][H][dv][dk] (ckpt_pos[b] < 0: no export).
  */
 #include <math.h>
 #include <pthread.h>
@@ -58,6 +65,7 @@
 #define ERR_SLOT 1
 #define ERR_SEQLEN 2
 #define ERR_ACCEPTED 4
+#define ERR_CKPT 8
 
 static double bf16_to_double(uint16_t bits)
 {
@@ -145,7 +153,7 @@ void kda_oracle_epilogue(const double *o, int dv, const double *g, const double 
  * (row b, head h); items are independent, so threads only split the list.
  * ------------------------------------------------------------------------- */
 
-enum { KIND_DECODE = 0, KIND_VERIFY = 1, KIND_COMMIT = 2 };
+enum { KIND_DECODE = 0, KIND_VERIFY = 1, KIND_COMMIT = 2, KIND_PREFILL = 3 };
 
 typedef struct {
     int kind;
@@ -160,6 +168,8 @@ typedef struct {
     int32_t mode, t1_inplace;
     uint16_t *rk, *rv;
     float *ralpha, *rbeta, *draft;
+    const int32_t *ckpt_pos;
+    float *ckpt;
     int32_t state_fp32;
 } call_t;
 
@@ -190,8 +200,14 @@ static int run_item(const call_t *c, int b, int h)
     } else {
         row0 = c->cu[b];
         Tb = (int64_t)c->cu[b + 1] - row0;
-        if (row0 < 0 || Tb < 0 || row0 + Tb > c->n_tok || Tb > c->T_max)
+        if (row0 < 0 || Tb < 0 || row0 + Tb > c->n_tok || (c->kind != KIND_PREFILL && Tb > c->T_max))
             return ERR_SEQLEN;
+    }
+    int64_t ckpt_at = -1;
+    if (c->kind == KIND_PREFILL && c->ckpt_pos) {
+        ckpt_at = c->ckpt_pos[b];
+        if (ckpt_at > Tb)
+            return ERR_CKPT;
     }
     int64_t n = Tb;
     if (c->kind == KIND_COMMIT) {
@@ -200,7 +216,7 @@ static int run_item(const call_t *c, int b, int h)
             return ERR_ACCEPTED;
         n = a;
     }
-    if (n == 0)
+    if (n == 0 && ckpt_at != 0)
         return 0;
 
     double *S = (double *)malloc(sizeof(double) * (size_t)dk * dv);
@@ -230,8 +246,19 @@ static int run_item(const call_t *c, int b, int h)
         be[t] = (double)c->beta[r];
     }
 
-    kda_oracle_unit(S, dk, dv, (int)n, q, k, v, a, be, c->state_fp32,
-                    c->kind == KIND_COMMIT ? NULL : o, S_tok);
+    if (c->kind == KIND_PREFILL && ckpt_at >= 0) {
+        /* the prompt in two runs, split at the checkpoint: the state carries over unchanged */
+        kda_oracle_unit(S, dk, dv, (int)ckpt_at, q, k, v, a, be, c->state_fp32, o, NULL);
+        float *dst = c->ckpt + ((int64_t)b * H + h) * (int64_t)dv * dk;
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j)
+                dst[(int64_t)j * dk + i] = (float)S[i * dv + j];
+        kda_oracle_unit(S, dk, dv, (int)(n - ckpt_at), q + ckpt_at * dk, k + ckpt_at * dk, v + ckpt_at * dv,
+                        a + ckpt_at * dk, be + ckpt_at, c->state_fp32, o + ckpt_at * dv, NULL);
+    } else {
+        kda_oracle_unit(S, dk, dv, (int)n, q, k, v, a, be, c->state_fp32,
+                        c->kind == KIND_COMMIT ? NULL : o, S_tok);
+    }
 
     if (c->kind != KIND_COMMIT && c->out) {
         double *y = (double *)malloc(sizeof(double) * (size_t)dv);
@@ -257,7 +284,7 @@ static int run_item(const call_t *c, int b, int h)
         free(w);
     }
 
-    const int write_slot = c->kind == KIND_DECODE || c->kind == KIND_COMMIT ||
+    const int write_slot = c->kind == KIND_DECODE || c->kind == KIND_COMMIT || c->kind == KIND_PREFILL ||
                            (c->kind == KIND_VERIFY && Tb == 1 && c->t1_inplace);
     if (write_slot) {
         for (int i = 0; i < dk; ++i)
@@ -485,6 +512,54 @@ int kda_oracle_commit(float *cache, int64_t num_slots, int64_t slot_stride,
     c.v = v;
     c.alpha = alpha;
     c.beta = beta;
+    c.state_fp32 = state_fp32;
+    return run_call(&c, nthreads);
+}
+
+/*
+ * Prefill: row b runs its whole prompt [cu[b], cu[b+1]) from the slot's state;
+ * outputs for every token; the final state goes back to the slot; the state
+ * after the first ckpt_pos[b] tokens (0 = the state before the prompt) is
+ * exported to ckpt [B][H][dv][dk] in the same pass. ckpt_pos may be NULL.
+ */
+int kda_oracle_prefill(float *cache, int64_t num_slots, int64_t slot_stride,
+                       const int32_t *slot_ids, const int32_t *cu_seqlens,
+                       int32_t B, int32_t n_tok, int32_t H, int32_t dk, int32_t dv,
+                       const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                       const float *alpha, const float *beta, float *out,
+                       const int32_t *ckpt_pos, float *ckpt,
+                       int32_t state_fp32, int32_t nthreads)
+{
+    if (!dims_ok(B, H, dk, dv, num_slots, slot_stride) || n_tok < 0)
+        return -1;
+    if (B == 0)
+        return 0;
+    if (!cache || !slot_ids || !cu_seqlens || !q || !k || !v || !alpha || !beta || !out)
+        return -1;
+    if (ckpt_pos && !ckpt)
+        return -1;
+    call_t c;
+    memset(&c, 0, sizeof c);
+    c.kind = KIND_PREFILL;
+    c.cache = cache;
+    c.num_slots = num_slots;
+    c.slot_stride = slot_stride;
+    c.slot_ids = slot_ids;
+    c.cu = cu_seqlens;
+    c.B = B;
+    c.T_max = n_tok;
+    c.n_tok = n_tok;
+    c.H = H;
+    c.dk = dk;
+    c.dv = dv;
+    c.q = q;
+    c.k = k;
+    c.v = v;
+    c.alpha = alpha;
+    c.beta = beta;
+    c.out = out;
+    c.ckpt_pos = ckpt_pos;
+    c.ckpt = ckpt;
     c.state_fp32 = state_fp32;
     return run_call(&c, nthreads);
 }

@@ -180,6 +180,39 @@ def check_brute_batch(lib):
             assert _rel(out[b, h], to_float(outs[0])) <= 1e-6, (b, h)
 
 
+def check_prefill_brute(lib):
+    """Prefill through the batch driver: outputs, final slot states and the in-pass
+    checkpoints against exact brute force, for empty, short and checkpoint-0 rows."""
+    w = synth.make(4, 2, 3, 4, seqlens=[6, 0, 3, 5], num_slots=6, state_std=0.5, seed=19)
+    pos = np.array([2, 0, 3, 0], np.int32)
+    cache = w.cache.copy()
+    out, ckpt, rc = oracle.prefill(cache, w.slot_ids, w.cu_seqlens, w.q[0], w.k[0], w.v[0], w.alpha[0],
+                                   w.beta[0], ckpt_pos=pos, lib=lib)
+    assert rc == 0
+    cu = w.cu_seqlens
+    for b in range(w.B):
+        s = w.slot_ids[b]
+        for h in range(w.H):
+            S0 = w.cache[s, h].T.astype(np.float64)
+            states, outs = brute_run(S0, _unit_tokens(w, range(cu[b], cu[b + 1]), h))
+            for t in range(cu[b + 1] - cu[b]):
+                assert _rel(out[cu[b] + t, h], to_float(outs[t])) <= 1e-6, (b, h, t)
+            final = to_float(states[-1]) if states else S0
+            assert _rel(cache[s, h].T, final) <= 1e-6, (b, h)
+            at = pos[b]
+            expect = S0 if at == 0 else to_float(states[at - 1])
+            assert _rel(ckpt[b, h].T, expect) <= 1e-6, (b, h)
+    untouched = np.setdiff1d(np.arange(w.num_slots), w.slot_ids)
+    assert np.array_equal(cache[untouched], w.cache[untouched])
+    # a checkpoint past the row: error bit 8, row skipped, others done
+    cache = w.cache.copy()
+    _, _, rc = oracle.prefill(cache, w.slot_ids, w.cu_seqlens, w.q[0], w.k[0], w.v[0], w.alpha[0],
+                              w.beta[0], ckpt_pos=np.array([7, 0, 3, 0], np.int32), lib=lib)
+    assert rc == oracle.ERR_CKPT
+    assert np.array_equal(cache[w.slot_ids[0]], w.cache[w.slot_ids[0]])
+    assert not np.array_equal(cache[w.slot_ids[2]], w.cache[w.slot_ids[2]])
+
+
 # ---------------------------------------------------------------- closed forms
 
 def check_write_then_read(lib):
@@ -444,7 +477,7 @@ def check_bounded_state(lib):
 
 
 CHECKS = [
-    check_golden_steps, check_golden_gate, check_brute_unit, check_brute_batch,
+    check_golden_steps, check_golden_gate, check_brute_unit, check_brute_batch, check_prefill_brute,
     check_write_then_read, check_alpha_zero, check_beta_zero, check_associative_recall,
     check_linearity, check_gate_closed_form, check_commit_equals_steps,
     check_column_permutation, check_slot_handling, check_fp32_state_storage, check_bounded_state,

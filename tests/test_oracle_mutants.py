@@ -42,6 +42,10 @@ MUTANTS = [
     ("accepted_not_checked", "if (a < 0 || a > Tb)", "if (a < 0)", 1),
     ("padding_uses_slot0", "const int64_t slot = c->slot_ids[b];",
      "const int64_t slot = c->slot_ids[b] < 0 ? 0 : c->slot_ids[b];", 1),
+    ("prefill_checkpoint_off_by_one", "kda_oracle_unit(S, dk, dv, (int)ckpt_at, q, k, v, a, be, c->state_fp32, o, NULL);",
+     "kda_oracle_unit(S, dk, dv, (int)(ckpt_at > 0 ? ckpt_at - 1 : 0), q, k, v, a, be, c->state_fp32, o, NULL);", 1),
+    ("prefill_slot_not_written", "c->kind == KIND_COMMIT || c->kind == KIND_PREFILL ||",
+     "c->kind == KIND_COMMIT ||", 1),
     ("gate_sum_not_mean", "ms /= (double)dv;", "ms /= 1.0;", 1),
     ("gate_sigmoid_sign", "exp(-g[j])", "exp(g[j])", 1),
     ("gate_eps_dropped", "sqrt(ms + eps)", "sqrt(ms)", 1),
