@@ -343,6 +343,34 @@ def mixed(D, K, synth, reps):
                 verify_plus_commit_us=round(p_ms * 1e3, 3))
 
 
+def prefill_8k(D, K, synth, reps):
+    """One 8000-token prompt, H=32, d=128, from a zero state, exporting the state after token
+    7680 in the same pass (the in-loop checkpoint of the pages' long-prompt prefill)."""
+    torch = D.torch
+    w = synth.make_workload("prefill_8k")
+    H, d = 32, 128
+    cache = D.f(w.cache)
+    slots, cu = D.i(w.slot_ids), D.i(w.cu_seqlens)
+    x = dict(q=D.bf(w.q[0]), k=D.bf(w.k[0]), v=D.bf(w.v[0]), alpha=D.f(w.alpha[0]), beta=D.f(w.beta[0]))
+    out = torch.empty(w.n_tok, H, d, device=D.dev)
+    pos = D.i([7680])
+    ckpt = torch.empty(1, H, d, d, device=D.dev)
+
+    def run(i):
+        K.kda_prefill(cache, slots, cu, x["q"], x["k"], x["v"], x["alpha"], x["beta"], out, ckpt_pos=pos, ckpt=ckpt)
+
+    run(0)
+    ms = timed_region(D, run, reps) / reps
+    n = w.n_tok
+    nbytes = n * H * ((2 * d + d) * 2 + d * 4 + 4 + d * 4) + 3 * H * d * d * 4 + 16
+    flops = n * H * 7 * d * d
+    log(f"prefill 8000 tokens: {ms * 1e3:.1f} us ({n / ms * 1e3:.0f} tok/s, {flops / ms / 1e9:.2f} TFLOP/s)")
+    return dict(tokens=n, heads=H, us=round(ms * 1e3, 2), tokens_per_s=round(n / ms * 1e3, 1),
+                algorithmic_bytes=nbytes, gbs=round(nbytes / ms / 1e6, 1), flops=flops,
+                tflops=round(flops / ms / 1e9, 3), checkpoint_at=7680,
+                tile_w=K.kda_query_variant(1, H, d, d, T_max=n, op=K.KDA_OP_PREFILL)[0])
+
+
 def copy_calibration(D, nbytes=256 << 20, reps=5):
     """A plain device copy of known size (for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)."""
     src = D.torch.empty(nbytes // 4, dtype=D.torch.float32, device=D.dev).normal_()
@@ -436,6 +464,7 @@ def main():
             b1_latency_1024_steps=b1_latency(D, K, synth),
             spec_verify_b16_t8=spec_verify(D, K, synth, reps=200),
             mixed_b64_gated=mixed(D, K, synth, reps=200),
+            prefill_8k_checkpoint=prefill_8k(D, K, synth, reps=5),
             headline_same_table_kernel_us=round(h["hot_ms"] * 1e3, 3),
         )
     if args.copy_calibration:

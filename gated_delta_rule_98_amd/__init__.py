@@ -7,6 +7,7 @@ torch-facing binding of that library.
 
 from .kda import (  # noqa: F401
     KDA_DEVERR_ACCEPTED,
+    KDA_DEVERR_CKPT,
     KDA_DEVERR_SEQLEN,
     KDA_DEVERR_SLOT,
     KDA_ERR_ALIGN,
@@ -17,6 +18,7 @@ from .kda import (  # noqa: F401
     KDA_OP_COMMIT_COPY,
     KDA_OP_COMMIT_REPLAY,
     KDA_OP_DECODE,
+    KDA_OP_PREFILL,
     KDA_OP_VERIFY,
     KDA_PER_POSITION,
     KDA_REPLAY,
@@ -26,6 +28,7 @@ from .kda import (  # noqa: F401
     LIB_PATH,
     KdaError,
     kda_decode_step,
+    kda_prefill,
     kda_query_variant,
     kda_replay_commit,
     kda_status_str,

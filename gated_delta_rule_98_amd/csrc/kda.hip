@@ -54,6 +54,8 @@ struct Args {
   int32_t *dev_err;
   uint16_t *rk, *rv;
   float *ralpha, *rbeta, *draft;
+  const int32_t *ckpt_pos;  // prefill
+  float *ckpt;
   float eps;
   int32_t B, H, dv, T_max, n_tok, ntile, mode, t1_inplace;
 };
@@ -142,6 +144,47 @@ __device__ __forceinline__ void token_readout(const float4 (&s)[C][NV], const fl
   for (int c = 0; c < C; ++c) o[c] = lane_dot<NV>(s[c], q);
 #pragma unroll
   for (int c = 0; c < C; ++c) o[c] = row16_sum(o[c]);
+}
+
+// One token on C columns with the read-out taken in the same pass as u:
+// o = S_dec^T q + (k . q) delta, where S_dec is the decayed state. The state
+// arithmetic (decay, u, delta, rank-1 write) is exactly token_update's, so the
+// state matches the single-token step bit for bit; the read-out equals
+// S_new^T q up to rounding, and its dot product no longer waits for the write.
+template <int NV, int C>
+__device__ __forceinline__ void token_fused(float4 (&s)[C][NV], const float4 (&a)[NV], const float4 (&k)[NV],
+                                            const float4 (&q)[NV], const float (&vj)[C], float beta,
+                                            float kq, float (&o)[C]) {
+  float u[C], p[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      s[c][e].x = s[c][e].x * a[e].x;
+      s[c][e].y = s[c][e].y * a[e].y;
+      s[c][e].z = s[c][e].z * a[e].z;
+      s[c][e].w = s[c][e].w * a[e].w;
+    }
+    u[c] = lane_dot<NV>(s[c], k);
+    p[c] = lane_dot<NV>(s[c], q);
+  }
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    u[c] = row16_sum(u[c]);
+    p[c] = row16_sum(p[c]);
+  }
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const float d = beta * (vj[c] - u[c]);
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      s[c][e].x = __builtin_fmaf(k[e].x, d, s[c][e].x);
+      s[c][e].y = __builtin_fmaf(k[e].y, d, s[c][e].y);
+      s[c][e].z = __builtin_fmaf(k[e].z, d, s[c][e].z);
+      s[c][e].w = __builtin_fmaf(k[e].w, d, s[c][e].w);
+    }
+    o[c] = __builtin_fmaf(kq, d, p[c]);
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -477,6 +520,161 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
 }
 
 // ----------------------------------------------------------------------------
+// Prefill with an in-pass checkpoint
+// ----------------------------------------------------------------------------
+//
+// One pass over each row's whole prompt from its slot ("Internal KDA prefix
+// checkpoint"): outputs for every token, the final state written back, and the
+// state after the first ckpt_pos[b] tokens exported inside the same loop.
+// Tokens are staged through LDS in chunks of kPrefillChunk, double-buffered:
+// the next chunk's loads are in flight while the current chunk computes.
+// Workgroups are 256 threads (W = 16 or 32 value columns). The state update is
+// the single-token step's, so a checkpoint after n tokens equals n decode steps
+// bit for bit.
+
+constexpr int kPrefillChunk = 16;
+
+template <int DK>
+struct PrefillBuf {
+  float *k, *q, *a, *v, *beta;
+  __device__ PrefillBuf(float *base, int W) {
+    k = base;
+    q = k + kPrefillChunk * DK;
+    a = q + kPrefillChunk * DK;
+    v = a + kPrefillChunk * DK;
+    beta = v + kPrefillChunk * W;
+  }
+};
+
+inline size_t prefill_lds_bytes(int dk, int W) {
+  return (2 * (size_t)kPrefillChunk * (3 * dk + W + 1) * sizeof(float) + 15) / 16 * 16;
+}
+
+// A chunk's inputs held in registers between the global loads and the LDS writes.
+template <int DK, int W>
+struct PrefillRegs {
+  static constexpr int MK = kPrefillChunk * (DK / 4) / 256;  // k/q/alpha quads per thread
+  static constexpr int MV = (kPrefillChunk * W + 255) / 256;  // v entries per thread
+  uint2 k[MK], q[MK];
+  float4 a[MK];
+  uint16_t v[MV];
+  float beta;
+};
+
+template <int DK, int W>
+__device__ __forceinline__ void prefill_fetch(const Args &a, int64_t row0, int n, int h, int tile,
+                                              PrefillRegs<DK, W> &r) {
+#pragma unroll
+  for (int m = 0; m < PrefillRegs<DK, W>::MK; ++m) {
+    const int idx = threadIdx.x + 256 * m;
+    const int t = idx / (DK / 4), i = (idx % (DK / 4)) * 4;
+    if (t < n) {
+      const int64_t off = ((row0 + t) * a.H + h) * DK + i;
+      r.k[m] = *reinterpret_cast<const uint2 *>(a.k + off);
+      r.q[m] = *reinterpret_cast<const uint2 *>(a.q + off);
+      r.a[m] = *reinterpret_cast<const float4 *>(a.alpha + off);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < PrefillRegs<DK, W>::MV; ++m) {
+    const int idx = threadIdx.x + 256 * m;
+    const int t = idx / W, jj = idx % W;
+    if (t < n && idx < kPrefillChunk * W)
+      r.v[m] = a.v[((row0 + t) * a.H + h) * a.dv + (int64_t)tile * W + jj];
+  }
+  if ((int)threadIdx.x < n) r.beta = a.beta[(row0 + threadIdx.x) * a.H + h];
+}
+
+template <int DK, int W>
+__device__ __forceinline__ void prefill_stage(const PrefillRegs<DK, W> &r, int n, PrefillBuf<DK> &B) {
+#pragma unroll
+  for (int m = 0; m < PrefillRegs<DK, W>::MK; ++m) {
+    const int idx = threadIdx.x + 256 * m;
+    const int t = idx / (DK / 4), i = (idx % (DK / 4)) * 4;
+    if (t < n) {
+      *reinterpret_cast<float4 *>(B.k + t * DK + i) = unpack_bf16x4(r.k[m]);
+      *reinterpret_cast<float4 *>(B.q + t * DK + i) = unpack_bf16x4(r.q[m]);
+      *reinterpret_cast<float4 *>(B.a + t * DK + i) = r.a[m];
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < PrefillRegs<DK, W>::MV; ++m) {
+    const int idx = threadIdx.x + 256 * m;
+    const int t = idx / W;
+    if (t < n && idx < kPrefillChunk * W) B.v[idx] = bf16_to_f32(r.v[m]);
+  }
+  if ((int)threadIdx.x < n) B.beta[threadIdx.x] = r.beta;
+}
+
+template <int DK, int C>
+__global__ __launch_bounds__(256) void prefill_kernel(Args a) {
+  constexpr int NV = DK / 64;
+  constexpr int W = 16 * C;  // 4 waves x 4 columns x C slabs
+  extern __shared__ float4 lds_dyn[];
+  const Unit u = unit_of_block(a.ntile, a.H);
+  const int32_t slot = a.slot_ids[u.b];
+  if (slot < 0) return;
+  if (slot >= a.num_slots) {
+    report(a.dev_err, u, KDA_DEVERR_SLOT);
+    return;
+  }
+  const int32_t c0 = a.cu[u.b], c1 = a.cu[u.b + 1];
+  if (c0 < 0 || c1 < c0 || c1 > a.n_tok) {
+    report(a.dev_err, u, KDA_DEVERR_SEQLEN);
+    return;
+  }
+  const int Tb = c1 - c0;
+  const int ck = a.ckpt_pos ? a.ckpt_pos[u.b] : -1;
+  if (ck > Tb) {
+    report(a.dev_err, u, KDA_DEVERR_CKPT);
+    return;
+  }
+  if (Tb == 0 && ck != 0) return;
+  const Lane L = lane_geometry();
+  float *S = a.cache + (int64_t)slot * a.slot_stride + ((int64_t)u.h * a.dv + (int64_t)u.tile * W) * DK;
+  float *CK = ck >= 0 ? a.ckpt + (((int64_t)u.b * a.H + u.h) * a.dv + (int64_t)u.tile * W) * DK : nullptr;
+  float4 s[C][NV];
+  load_tile<DK, C, kVerifyLoadStream>(s, S, L);
+  if (ck == 0) store_tile<DK, C, kVerifyStoreStream>(CK, s, L);
+  if (Tb == 0) return;
+
+  PrefillBuf<DK> buf[2] = {PrefillBuf<DK>(reinterpret_cast<float *>(lds_dyn), W),
+                           PrefillBuf<DK>(reinterpret_cast<float *>(lds_dyn) + kPrefillChunk * (3 * DK + W + 1), W)};
+  const int nchunks = (Tb + kPrefillChunk - 1) / kPrefillChunk;
+  PrefillRegs<DK, W> regs;
+  prefill_fetch<DK, W>(a, c0, min(kPrefillChunk, Tb), u.h, u.tile, regs);
+  for (int ci = 0; ci < nchunks; ++ci) {
+    const int t0 = ci * kPrefillChunk;
+    const int n = min(kPrefillChunk, Tb - t0);
+    PrefillBuf<DK> &B = buf[ci & 1];
+    prefill_stage<DK, W>(regs, n, B);
+    __syncthreads();
+    if (ci + 1 < nchunks)
+      prefill_fetch<DK, W>(a, c0 + t0 + kPrefillChunk, min(kPrefillChunk, Tb - t0 - kPrefillChunk), u.h, u.tile,
+                           regs);
+    for (int t = 0; t < n; ++t) {
+      float4 kk[NV], qq[NV], aa[NV];
+#pragma unroll
+      for (int e = 0; e < NV; ++e) {
+        const int i = t * DK + 4 * L.r + 64 * e;
+        kk[e] = *reinterpret_cast<const float4 *>(B.k + i);
+        qq[e] = *reinterpret_cast<const float4 *>(B.q + i);
+        aa[e] = *reinterpret_cast<const float4 *>(B.a + i);
+      }
+      float vj[C];
+#pragma unroll
+      for (int c = 0; c < C; ++c) vj[c] = B.v[t * W + L.col0 + c * L.slab];
+      const float kq = row16_sum(lane_dot<NV>(kk, qq));
+      float o[C];
+      token_fused<NV, C>(s, aa, kk, qq, vj, B.beta[t], kq, o);
+      store_cols<C>(a.out + ((c0 + t0 + t) * (int64_t)a.H + u.h) * a.dv + (int64_t)u.tile * W, L, o);
+      if (t0 + t + 1 == ck) store_tile<DK, C, kVerifyStoreStream>(CK, s, L);
+    }
+  }
+  store_tile<DK, C, kVerifyStoreStream>(S, s, L);
+}
+
+// ----------------------------------------------------------------------------
 // Chunk form of verify (outputs only), MFMA for the state products
 // ----------------------------------------------------------------------------
 //
@@ -768,7 +966,7 @@ __global__ __launch_bounds__(256) void commit_copy_kernel(Args a) {
 // Host side: checks, launch shape, dispatch
 // ----------------------------------------------------------------------------
 
-enum Kind { KIND_DECODE, KIND_VERIFY, KIND_COMMIT_REPLAY, KIND_COMMIT_COPY };
+enum Kind { KIND_DECODE, KIND_VERIFY, KIND_COMMIT_REPLAY, KIND_COMMIT_COPY, KIND_PREFILL };
 
 // Gated launches use a fixed number of slabs per lane for each op (see
 // choose_width); only those are instantiated with the gate.
@@ -788,6 +986,8 @@ const void *kernel_for(Kind kind, bool gate) {
       return (const void *)commit_replay_kernel<DK, C>;
     case KIND_COMMIT_COPY:
       return (const void *)commit_copy_kernel<DK, C>;
+    case KIND_PREFILL:
+      return nullptr;  // launched directly by kda_prefill
   }
   return nullptr;
 }
@@ -841,6 +1041,12 @@ int choose_width(Kind kind, int64_t rows, int H, int dv, bool gate, int requeste
     *l = {dv, dv / (4 * C), C};
     return KDA_OK;
   }
+  if (kind == KIND_PREFILL) {
+    // 256-thread workgroups (the staging is spread over them): 16 or 32 columns
+    const int W = requested != 0 ? requested : ((int64_t)rows * H * (dv / 16) > 2048 ? 32 : 16);
+    if ((W != 16 && W != 32) || W > dv) return KDA_ERR_UNSUPPORTED;
+    return launch_of_width(W, l) ? KDA_OK : KDA_ERR_UNSUPPORTED;
+  }
   if (requested != 0) {
     if (requested > dv || dv % requested != 0 || !launch_of_width(requested, l)) return KDA_ERR_UNSUPPORTED;
     return KDA_OK;
@@ -868,6 +1074,7 @@ int choose_width(Kind kind, int64_t rows, int H, int dv, bool gate, int requeste
       }
       break;
     case KIND_COMMIT_COPY:
+    case KIND_PREFILL:
       W = 16;
       break;
   }
@@ -930,6 +1137,54 @@ int check_replay_buf(const kda_replay_buf *rb) {
 }  // namespace
 
 extern "C" {
+
+int kda_prefill(float *cache, int64_t num_slots, int64_t slot_stride, const int32_t *slot_ids,
+                const int32_t *cu_seqlens, int32_t B, int32_t n_tok, int32_t H, int32_t dk, int32_t dv,
+                const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *alpha,
+                const float *beta, float *out, const int32_t *ckpt_pos, float *ckpt, int32_t *dev_err,
+                const kda_options *opts, void *stream) {
+  if (B < 0 || H <= 0 || dk <= 0 || dv <= 0 || n_tok < 0) return KDA_ERR_INVALID;
+  if (!dims_supported(dk, dv)) return KDA_ERR_UNSUPPORTED;
+  if (B == 0 || (n_tok == 0 && !ckpt_pos)) return KDA_OK;
+  if (!slot_ids || !cu_seqlens) return KDA_ERR_INVALID;
+  KDA_TRY(check_cache(cache, num_slots, slot_stride, H, dk, dv));
+  if (n_tok > 0) KDA_TRY(check_inputs(q, k, v, alpha, beta, out, true));
+  if (ckpt_pos) {
+    if (!ckpt) return KDA_ERR_INVALID;
+    if (!aligned(ckpt, 16) || !aligned(ckpt_pos, 4)) return KDA_ERR_ALIGN;
+  }
+  if (!aligned(cu_seqlens, 4) || (dev_err && !aligned(dev_err, 4))) return KDA_ERR_ALIGN;
+  Launch l;
+  KDA_TRY(choose_width(KIND_PREFILL, B, H, dv, false, opts ? opts->tile_w : 0, &l));
+
+  Args a;
+  memset(&a, 0, sizeof a);
+  a.cache = cache;
+  a.num_slots = num_slots;
+  a.slot_stride = slot_stride;
+  a.slot_ids = slot_ids;
+  a.cu = cu_seqlens;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.out = out;
+  a.ckpt_pos = ckpt_pos;
+  a.ckpt = ckpt;
+  a.dev_err = dev_err;
+  a.B = B;
+  a.H = H;
+  a.dv = dv;
+  a.n_tok = n_tok;
+  a.ntile = dv / l.W;
+  const int64_t units = (int64_t)B * H * a.ntile;
+  if (units > 0x7fffffff) return KDA_ERR_UNSUPPORTED;
+  const void *fn = nullptr;
+  if (dk == 64) fn = l.C == 1 ? (const void *)prefill_kernel<64, 1> : (const void *)prefill_kernel<64, 2>;
+  else fn = l.C == 1 ? (const void *)prefill_kernel<128, 1> : (const void *)prefill_kernel<128, 2>;
+  return launch_fn(fn, units, 256, prefill_lds_bytes(dk, l.W), a, stream);
+}
 
 int kda_decode_step(float *cache, int64_t num_slots, int64_t slot_stride, const int32_t *slot_ids,
                     int32_t B, int32_t H, int32_t dk, int32_t dv, const uint16_t *q,
@@ -1115,9 +1370,10 @@ int kda_query_variant(int32_t op, int32_t B, int32_t H, int32_t dk, int32_t dv, 
     case KDA_OP_VERIFY: kind = KIND_VERIFY; break;
     case KDA_OP_COMMIT_REPLAY: kind = KIND_COMMIT_REPLAY; break;
     case KDA_OP_COMMIT_COPY: kind = KIND_COMMIT_COPY; break;
+    case KDA_OP_PREFILL: kind = KIND_PREFILL; break;
     default: return KDA_ERR_INVALID;
   }
-  if (!dims_supported(dk, dv) || T_max < 1 || T_max > kMaxT) return KDA_ERR_UNSUPPORTED;
+  if (!dims_supported(dk, dv) || T_max < 1 || (kind != KIND_PREFILL && T_max > kMaxT)) return KDA_ERR_UNSUPPORTED;
   if (epilogue && kind != KIND_DECODE && kind != KIND_VERIFY) return KDA_ERR_INVALID;
   Launch l;
   KDA_TRY(choose_width(kind, B, H, dv, epilogue != 0, requested_tile_w, &l));

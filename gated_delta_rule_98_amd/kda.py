@@ -31,6 +31,7 @@ KDA_OP_DECODE = 0
 KDA_OP_VERIFY = 1
 KDA_OP_COMMIT_REPLAY = 2
 KDA_OP_COMMIT_COPY = 3
+KDA_OP_PREFILL = 4
 
 KDA_VERIFY_AUTO = 0
 KDA_VERIFY_RECURRENT = 1
@@ -39,6 +40,7 @@ KDA_VERIFY_CHUNKED = 2
 KDA_DEVERR_SLOT = 1
 KDA_DEVERR_SEQLEN = 2
 KDA_DEVERR_ACCEPTED = 4
+KDA_DEVERR_CKPT = 8
 
 
 class KdaError(RuntimeError):
@@ -82,6 +84,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_replay_commit.argtypes = [P, i64, i64, P, P, P, i32, i32, i32, i32, i32, i32, i32,
                                       P, P, P, P, P]
     lib.kda_replay_commit.restype = ctypes.c_int
+    lib.kda_prefill.argtypes = [P, i64, i64, P, P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P]
+    lib.kda_prefill.restype = ctypes.c_int
     lib.kda_query_variant.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32,
                                       ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.kda_query_variant.restype = ctypes.c_int
@@ -274,3 +278,40 @@ def kda_replay_commit(cache: torch.Tensor, slot_ids: torch.Tensor, cu_seqlens: O
         _ref(_opts(tile_w)), _stream(stream))
     if rc != KDA_OK:
         raise KdaError(rc, "kda_replay_commit")
+
+
+def kda_prefill(cache: torch.Tensor, slot_ids: torch.Tensor, cu_seqlens: torch.Tensor, q, k, v, alpha, beta,
+                out: torch.Tensor, *, ckpt_pos: Optional[torch.Tensor] = None, ckpt: Optional[torch.Tensor] = None,
+                dev_err: Optional[torch.Tensor] = None, tile_w: int = 0, stream=None) -> None:
+    """Whole prompts in one pass with an in-pass checkpoint. Token arrays are [n_tok, H, .];
+    row b owns tokens [cu[b], cu[b+1]); ckpt_pos int32 [B], ckpt float32 [B, H, dv, dk]."""
+    ns, stride, H, dv, dk = _cache(cache)
+    _dev(slot_ids, "slot_ids", (torch.int32,), 1)
+    _dev(cu_seqlens, "cu_seqlens", (torch.int32,), 1)
+    B = slot_ids.shape[0]
+    _shape(cu_seqlens, "cu_seqlens", (B + 1,))
+    for name, t, d in (("q", q, _BF16_TYPES), ("k", k, _BF16_TYPES), ("v", v, _BF16_TYPES),
+                       ("alpha", alpha, (torch.float32,)), ("beta", beta, (torch.float32,)),
+                       ("out", out, (torch.float32,))):
+        _dev(t, name, d)
+    n_tok = k.shape[0]
+    for name, t, shape in (("q", q, (n_tok, H, dk)), ("k", k, (n_tok, H, dk)), ("v", v, (n_tok, H, dv)),
+                           ("alpha", alpha, (n_tok, H, dk)), ("beta", beta, (n_tok, H)),
+                           ("out", out, (n_tok, H, dv))):
+        _shape(t, name, shape)
+    if ckpt_pos is not None:
+        _dev(ckpt_pos, "ckpt_pos", (torch.int32,), 1)
+        _shape(ckpt_pos, "ckpt_pos", (B,))
+        if ckpt is None:
+            raise ValueError("ckpt_pos needs a ckpt buffer")
+    if ckpt is not None:
+        _dev(ckpt, "ckpt", (torch.float32,))
+        _shape(ckpt, "ckpt", (B, H, dv, dk))
+    if dev_err is not None:
+        _dev(dev_err, "dev_err", (torch.int32,))
+    rc = load_library().kda_prefill(
+        cache.data_ptr(), ns, stride, slot_ids.data_ptr(), cu_seqlens.data_ptr(), B, n_tok, H, dk, dv,
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(), beta.data_ptr(), out.data_ptr(),
+        _ptr(ckpt_pos), _ptr(ckpt), _ptr(dev_err), _ref(_opts(tile_w)), _stream(stream))
+    if rc != KDA_OK:
+        raise KdaError(rc, "kda_prefill")

@@ -54,6 +54,7 @@
  *   KDA_DEVERR_SEQLEN    row b's token range [cu[b], cu[b+1]) is decreasing, leaves
  *                        [0, n_tok] or is longer than T_max
  *   KDA_DEVERR_ACCEPTED  accepted_len[b] outside [0, T_b]
+ *   KDA_DEVERR_CKPT      kda_prefill: checkpoint position past the row
  * The library never falls back to another path: an unsupported shape is
  * reported (KDA_ERR_UNSUPPORTED) and left to the caller.
  */
@@ -79,14 +80,20 @@ enum kda_status {
 
 enum kda_mode { KDA_REPLAY = 0, KDA_PER_POSITION = 1 };
 
-enum kda_device_error { KDA_DEVERR_SLOT = 1, KDA_DEVERR_SEQLEN = 2, KDA_DEVERR_ACCEPTED = 4 };
+enum kda_device_error {
+    KDA_DEVERR_SLOT = 1,
+    KDA_DEVERR_SEQLEN = 2,
+    KDA_DEVERR_ACCEPTED = 4,
+    KDA_DEVERR_CKPT = 8 /* kda_prefill: ckpt_pos[b] > T_b */
+};
 
 /* Operations, for kda_query_variant. */
 enum kda_op {
     KDA_OP_DECODE = 0,        /* kda_decode_step */
     KDA_OP_VERIFY = 1,        /* kda_verify_chunk */
     KDA_OP_COMMIT_REPLAY = 2, /* kda_replay_commit, mode KDA_REPLAY */
-    KDA_OP_COMMIT_COPY = 3    /* kda_replay_commit, mode KDA_PER_POSITION */
+    KDA_OP_COMMIT_COPY = 3,   /* kda_replay_commit, mode KDA_PER_POSITION */
+    KDA_OP_PREFILL = 4        /* kda_prefill */
 };
 
 /* Output gate fused into the read-out, per (token, head) over the whole value
@@ -187,6 +194,30 @@ int kda_replay_commit(float *cache, int64_t num_slots, int64_t slot_stride,
                       int32_t H, int32_t dk, int32_t dv, int32_t mode,
                       const kda_replay_buf *rb, const float *draft, int32_t *dev_err,
                       const kda_options *opts, void *stream);
+
+/*
+ * Prefill with an in-pass checkpoint ("Kimi K3 performance optimization in
+ * vLLM", section "Internal KDA prefix checkpoint": one pass over the whole
+ * prompt that also exports the state at an earlier token). Row b runs its
+ * prompt, tokens [cu_seqlens[b], cu_seqlens[b+1]) of the packed [n_tok] arrays
+ * (any length), from the state in slot slot_ids[b] (zero it for a fresh
+ * prompt, or copy a checkpoint into it to resume); out[cu_seqlens[b] + t] gets
+ * token t's read-out and the final state is written back to the slot. With
+ * ckpt_pos (int32 [B], may be NULL), the state after the first ckpt_pos[b]
+ * tokens (0 = before the prompt, < 0 = none) is written to ckpt
+ * (float [B][H][dv][dk]) during the same pass; ckpt_pos[b] > T_b sets
+ * KDA_DEVERR_CKPT and skips the row. The states match that many
+ * kda_decode_step calls bit for bit; outputs agree to rounding (the read-out
+ * is taken on the decayed state plus (k . q) delta). kda_options.tile_w may be
+ * 16 or 32. With B == 0, or n_tok == 0 and no ckpt_pos, nothing is enqueued.
+ */
+int kda_prefill(float *cache, int64_t num_slots, int64_t slot_stride,
+                const int32_t *slot_ids, const int32_t *cu_seqlens,
+                int32_t B, int32_t n_tok, int32_t H, int32_t dk, int32_t dv,
+                const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                const float *alpha, const float *beta, float *out,
+                const int32_t *ckpt_pos, float *ckpt, int32_t *dev_err,
+                const kda_options *opts, void *stream);
 
 /*
  * Host only. Reports the launch shape operation op (a kda_op) would use for

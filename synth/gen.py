@@ -11,6 +11,8 @@ the shapes of that decode path:
   spec_verify    B=16, H=32, dk=dv=128, 8 draft tokens each, 256-slot cache
   mixed          B=64 packed: 40 single-token rows then 24 rows of 4 tokens,
                  512-slot cache, output gate
+  prefill_8k     B=1, H=32, dk=dv=128, one 8000-token prompt from a zero state
+                 (the state after token 7680 is the checkpoint)
 
 Draw order from ``numpy.random.Generator(PCG64(seed))`` (all float32 standard
 normal unless noted), shaped ``[steps][n_tok][H][.]``:
@@ -170,6 +172,7 @@ WORKLOADS = {
     "spec_verify": dict(B=16, H=32, dk=128, dv=128, seqlens=[8] * 16, num_slots=256, state_std=0.02),
     "mixed": dict(B=64, H=32, dk=128, dv=128, seqlens=[1] * 40 + [4] * 24, num_slots=512,
                   state_std=0.02, gate=True),
+    "prefill_8k": dict(B=1, H=32, dk=128, dv=128, seqlens=[8000], num_slots=1),
 }
 
 

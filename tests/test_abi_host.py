@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert set(declared_functions()) == {"kda_decode_step", "kda_verify_chunk", "kda_replay_commit",
-                                         "kda_query_variant", "kda_status_str"}
+                                         "kda_prefill", "kda_query_variant", "kda_status_str"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -61,6 +61,12 @@ def test_query_variant_launch_shapes():
     assert q(2, 32, 128, 128, T_max=8, op=V) == (16, 256)
     assert q(1, 4, 128, 128, T_max=8, op=V) == (8, 128)
     assert q(16, 32, 128, 128, T_max=8, op=CC) == (16, 256)
+    P = kda.KDA_OP_PREFILL
+    assert q(1, 32, 128, 128, T_max=8000, op=P) == (16, 256)     # prompts of any length
+    assert q(64, 32, 128, 128, T_max=100, op=P) == (32, 256)
+    assert q(1, 32, 128, 128, T_max=100, op=P, tile_w=32) == (32, 256)
+    with pytest.raises(kda.KdaError):
+        q(1, 32, 128, 128, T_max=100, op=P, tile_w=64)
     # the output gate needs the whole head in one workgroup
     assert q(64, 32, 128, 128, epilogue=True) == (128, 1024)   # decode: 16 waves x 2 slabs
     assert q(64, 32, 128, 128, T_max=4, epilogue=True, op=V) == (128, 512)
@@ -154,9 +160,9 @@ def test_decode_host_checks():
     assert _decode(epi=ctypes.byref(nan_eps)) == E.KDA_ERR_INVALID
     gate_mis = kda.kda_epilogue(A + 2, None, 1e-6)
     assert _decode(epi=ctypes.byref(gate_mis)) == E.KDA_ERR_ALIGN
-    assert _decode(opts=ctypes.byref(kda.kda_options(24))) == E.KDA_ERR_UNSUPPORTED
+    assert _decode(opts=ctypes.byref(kda.kda_options(24, 0))) == E.KDA_ERR_UNSUPPORTED
     ok_gate = kda.kda_epilogue(A, None, 1e-6)
-    assert _decode(epi=ctypes.byref(ok_gate), opts=ctypes.byref(kda.kda_options(64))) == E.KDA_ERR_UNSUPPORTED
+    assert _decode(epi=ctypes.byref(ok_gate), opts=ctypes.byref(kda.kda_options(64, 0))) == E.KDA_ERR_UNSUPPORTED
 
 
 @needs_no_gpu
@@ -191,3 +197,26 @@ def test_commit_host_checks():
     assert _commit(mode=1, draft=A, acc=A + 2) == E.KDA_ERR_ALIGN
     assert _commit(mode=1, draft=A, T_max=32) == E.KDA_ERR_UNSUPPORTED
     assert _commit(mode=1, draft=A, slot_stride=100) == E.KDA_ERR_INVALID
+
+
+def _prefill(**over):
+    d = dict(cache=A, num_slots=8, slot_stride=2 * 128 * 128, slot_ids=A, cu=A, B=4, n_tok=90, H=2, dk=128,
+             dv=128, q=A, k=A, v=A, alpha=A, beta=A, out=A, ckpt_pos=None, ckpt=None, dev_err=None, opts=None,
+             stream=None)
+    d.update(over)
+    return kda.load_library().kda_prefill(*d.values())
+
+
+@needs_no_gpu
+def test_prefill_host_checks():
+    E = kda
+    assert _prefill(B=0) == E.KDA_OK
+    assert _prefill(n_tok=0) == E.KDA_OK                     # no tokens, no checkpoint: nothing to do
+    assert _prefill(n_tok=-1) == E.KDA_ERR_INVALID
+    assert _prefill(cu=None) == E.KDA_ERR_INVALID
+    assert _prefill(q=None) == E.KDA_ERR_INVALID
+    assert _prefill(ckpt_pos=A, ckpt=None) == E.KDA_ERR_INVALID
+    assert _prefill(ckpt_pos=A, ckpt=A + 4) == E.KDA_ERR_ALIGN
+    assert _prefill(dk=96) == E.KDA_ERR_UNSUPPORTED
+    assert _prefill(opts=ctypes.byref(kda.kda_options(64, 0))) == E.KDA_ERR_UNSUPPORTED
+    assert _prefill(alpha=A + 4) == E.KDA_ERR_ALIGN

@@ -1,0 +1,166 @@
+"""GPU parity of kda_prefill (whole prompts, in-pass checkpoint) against the CPU oracle.
+
+Outputs within 1e-4 relative L2 of the oracle's per call, final and checkpoint
+states within 1e-3 relative Frobenius; slot handling bit-exact. The states are
+also checked bit for bit against the same number of kda_decode_step calls.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_98_amd as K
+import oracle
+import synth
+from gpu_util import SENTINEL_BITS, bits, dev, f32, i32, log, rel_l2, sentinel, step_inputs
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 1e-4
+STATE_TOL = 1e-3
+
+
+def _prefill(w, cache_d, *, slots=None, pos=None, tile_w=0, dev_err=None):
+    x = step_inputs(w, 0)
+    slots = w.slot_ids if slots is None else slots
+    out = sentinel((w.n_tok, w.H, w.dv))
+    ckpt = None
+    if pos is not None:
+        ckpt = sentinel((w.B, w.H, w.dv, w.dk))
+    K.kda_prefill(cache_d, i32(slots), i32(w.cu_seqlens), x["q"], x["k"], x["v"], x["alpha"], x["beta"], out,
+                  ckpt_pos=None if pos is None else i32(pos), ckpt=ckpt, dev_err=dev_err, tile_w=tile_w)
+    return out, ckpt
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (64, 128), (128, 64)])
+def test_prefill_matches_oracle(dk, dv):
+    seqlens = [40, 1, 77, 0, 16, 33, 5]
+    w = synth.make(len(seqlens), 4, dk, dv, seqlens=seqlens, num_slots=10, state_std=0.05, seed=61)
+    slots = w.slot_ids.copy()
+    slots[6] = -1                                   # padding row with tokens
+    pos = np.array([13, 1, 77, 0, -1, 32, 2], np.int32)
+    cache_d = f32(w.cache)
+    log(f"prefill dk={dk} dv={dv}")
+    out, ckpt = _prefill(w, cache_d, slots=slots, pos=pos)
+    torch.cuda.synchronize()
+    cache_h = w.cache.copy()
+    ref_out, ref_ckpt, rc = oracle.prefill(cache_h, slots, w.cu_seqlens, w.q[0], w.k[0], w.v[0], w.alpha[0],
+                                           w.beta[0], ckpt_pos=pos)
+    assert rc == 0
+    live = np.concatenate([np.arange(w.cu_seqlens[b], w.cu_seqlens[b + 1]) for b in range(w.B) if b != 6])
+    pad = np.arange(w.cu_seqlens[6], w.cu_seqlens[7])
+    err = rel_l2(out.cpu().numpy()[live], ref_out[live])
+    log(f"  outputs rel-L2 {err:.3e}")
+    assert err <= OUT_TOL
+    assert np.all(bits(out)[pad] == SENTINEL_BITS)
+    got = cache_d.cpu().numpy()
+    live_slots = slots[slots >= 0]
+    assert rel_l2(got[live_slots], cache_h[live_slots]) <= STATE_TOL
+    others = np.setdiff1d(np.arange(w.num_slots), live_slots)
+    assert np.array_equal(got[others].view(np.uint32), w.cache[others].view(np.uint32))
+    ck = ckpt.cpu().numpy()
+    for b in range(w.B):
+        if slots[b] >= 0 and pos[b] >= 0:
+            assert rel_l2(ck[b], ref_ckpt[b]) <= STATE_TOL, b
+        else:
+            assert np.all(bits(ckpt)[b] == SENTINEL_BITS), b     # no export: untouched
+
+
+def test_prefill_states_equal_decode_steps_bitwise():
+    T = 37
+    w = synth.make(3, 8, 128, 128, seqlens=[T] * 3, num_slots=5, state_std=0.05, seed=62)
+    pos = np.array([7, 0, 37], np.int32)
+    cache_p = f32(w.cache)
+    log("prefill vs single-token steps")
+    out, ckpt = _prefill(w, cache_p, pos=pos)
+    x = step_inputs(w, 0)
+    cache_d = f32(w.cache)
+    dec_out = torch.empty(w.n_tok, w.H, w.dv, device=dev())
+    snaps = {}
+    for t in range(T):
+        r = torch.from_numpy((w.cu_seqlens[:-1] + t).astype(np.int64)).to(dev())
+        o = torch.empty(w.B, w.H, w.dv, device=dev())
+        K.kda_decode_step(cache_d, i32(w.slot_ids), *(x[n][r].contiguous() for n in ("q", "k", "v", "alpha", "beta")),
+                          o)
+        dec_out[r] = o
+        snaps[t + 1] = bits(cache_d)
+    torch.cuda.synchronize()
+    snaps[0] = w.cache.view(np.uint32)
+    assert np.array_equal(bits(cache_p), snaps[T])
+    ck = bits(ckpt)
+    for b in range(w.B):
+        assert np.array_equal(ck[b], snaps[int(pos[b])][w.slot_ids[b]]), b
+    assert rel_l2(out.cpu().numpy(), dec_out.cpu().numpy()) <= 1e-5
+
+
+def test_prefill_resume_from_checkpoint_is_bitwise_identical():
+    """Prefill the whole prompt, or the first p tokens, copy the checkpoint into the slot and
+    prefill the rest: the same final state and the same outputs, bit for bit."""
+    T, p = 50, 21
+    w = synth.make(1, 4, 128, 128, seqlens=[T], num_slots=2, state_std=0.05, seed=63)
+    full_d = f32(w.cache)
+    log("prefill whole prompt")
+    out_full, ckpt = _prefill(w, full_d, pos=np.array([p], np.int32))
+    head = synth.make(1, 4, 128, 128, seqlens=[T], num_slots=2, state_std=0.05, seed=63)
+    tail = synth.make(1, 4, 128, 128, seqlens=[T], num_slots=2, state_std=0.05, seed=63)
+    for part, lo, hi in ((head, 0, p), (tail, p, T)):
+        part.q, part.k, part.v = part.q[:, lo:hi], part.k[:, lo:hi], part.v[:, lo:hi]
+        part.alpha, part.beta = part.alpha[:, lo:hi], part.beta[:, lo:hi]
+        part.cu_seqlens = np.array([0, hi - lo], np.int32)
+    res_d = f32(w.cache)
+    log("prefill head, resume from its checkpoint")
+    out_head, ck_head = _prefill(head, res_d, pos=np.array([p], np.int32))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(ck_head), bits(ckpt))
+    res_d[w.slot_ids[0]] = ck_head[0]
+    out_tail, _ = _prefill(tail, res_d)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(res_d)[w.slot_ids[0]], bits(full_d)[w.slot_ids[0]])
+    assert np.array_equal(bits(out_head), bits(out_full)[:p])
+    assert np.array_equal(bits(out_tail), bits(out_full)[p:])
+
+
+def test_prefill_8k_prompt_checkpoint_at_7680():
+    """One 8000-token prompt, H=32, d=128, from a zero state, exporting the state after
+    token 7680 in the same pass (the launch the benchmark times)."""
+    w = synth.make_workload("prefill_8k")
+    pos = np.array([7680], np.int32)
+    cache_d = f32(w.cache)
+    log("prefill 8000 tokens, checkpoint at 7680")
+    out, ckpt = _prefill(w, cache_d, pos=pos)
+    torch.cuda.synchronize()
+    cache_h = w.cache.copy()
+    ref_out, ref_ckpt, rc = oracle.prefill(cache_h, w.slot_ids, w.cu_seqlens, w.q[0], w.k[0], w.v[0],
+                                           w.alpha[0], w.beta[0], ckpt_pos=pos)
+    assert rc == 0
+    o = out.cpu().numpy()
+    err = rel_l2(o, ref_out)
+    worst = max(rel_l2(o[t], ref_out[t]) for t in range(0, w.n_tok, 97))
+    serr = rel_l2(cache_d.cpu().numpy(), cache_h)
+    cerr = rel_l2(ckpt.cpu().numpy(), ref_ckpt)
+    log(f"  outputs rel-L2 {err:.3e} (worst sampled token {worst:.3e}), final state {serr:.3e}, checkpoint {cerr:.3e}")
+    assert err <= OUT_TOL and worst <= OUT_TOL and serr <= STATE_TOL and cerr <= STATE_TOL
+
+
+def test_prefill_tile_widths_and_errors():
+    w = synth.make(3, 4, 128, 128, seqlens=[9, 20, 4], num_slots=6, state_std=0.05, seed=64)
+    runs = []
+    for tw in (16, 32):
+        cache_d = f32(w.cache)
+        log(f"prefill tile width {tw}")
+        out, ckpt = _prefill(w, cache_d, pos=np.array([3, 20, 0], np.int32), tile_w=tw)
+        torch.cuda.synchronize()
+        runs.append((bits(cache_d), bits(out), bits(ckpt)))
+    for a, b in zip(*runs):
+        assert np.array_equal(a, b)
+    err = torch.zeros(1, dtype=torch.int32, device=dev())
+    cache_d = f32(w.cache)
+    slots = w.slot_ids.copy()
+    slots[2] = w.num_slots
+    log("prefill device errors")
+    out, _ = _prefill(w, cache_d, slots=slots, pos=np.array([3, 21, 0], np.int32), dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == K.KDA_DEVERR_SLOT | K.KDA_DEVERR_CKPT
+    got = cache_d.cpu().numpy()
+    assert np.array_equal(got[w.slot_ids[1]].view(np.uint32), w.cache[w.slot_ids[1]].view(np.uint32))
+    assert not np.array_equal(got[w.slot_ids[0]], w.cache[w.slot_ids[0]])
