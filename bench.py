@@ -343,7 +343,7 @@ def mixed(D, K, synth, reps):
                 verify_plus_commit_us=round(p_ms * 1e3, 3))
 
 
-def prefill_8k(D, K, synth, reps):
+def prefill_8k(D, K, synth, reps, tile_w=0):
     """One 8000-token prompt, H=32, d=128, from a zero state, exporting the state after token
     7680 in the same pass (the in-loop checkpoint of the pages' long-prompt prefill)."""
     torch = D.torch
@@ -357,7 +357,8 @@ def prefill_8k(D, K, synth, reps):
     ckpt = torch.empty(1, H, d, d, device=D.dev)
 
     def run(i):
-        K.kda_prefill(cache, slots, cu, x["q"], x["k"], x["v"], x["alpha"], x["beta"], out, ckpt_pos=pos, ckpt=ckpt)
+        K.kda_prefill(cache, slots, cu, x["q"], x["k"], x["v"], x["alpha"], x["beta"], out, ckpt_pos=pos, ckpt=ckpt,
+                      tile_w=tile_w)
 
     run(0)
     ms = timed_region(D, run, reps) / reps
@@ -368,7 +369,7 @@ def prefill_8k(D, K, synth, reps):
     return dict(tokens=n, heads=H, us=round(ms * 1e3, 2), tokens_per_s=round(n / ms * 1e3, 1),
                 algorithmic_bytes=nbytes, gbs=round(nbytes / ms / 1e6, 1), flops=flops,
                 tflops=round(flops / ms / 1e9, 3), checkpoint_at=7680,
-                tile_w=K.kda_query_variant(1, H, d, d, T_max=n, op=K.KDA_OP_PREFILL)[0])
+                tile_w=K.kda_query_variant(1, H, d, d, T_max=n, op=K.KDA_OP_PREFILL, tile_w=tile_w)[0])
 
 
 def copy_calibration(D, nbytes=256 << 20, reps=5):

@@ -536,18 +536,26 @@ constexpr int kPrefillChunk = 16;
 
 template <int DK>
 struct PrefillBuf {
-  float *k, *q, *a, *v, *beta;
+  float *k, *q, *a, *v, *beta, *kq;
   __device__ PrefillBuf(float *base, int W) {
     k = base;
     q = k + kPrefillChunk * DK;
     a = q + kPrefillChunk * DK;
     v = a + kPrefillChunk * DK;
     beta = v + kPrefillChunk * W;
+    kq = beta + kPrefillChunk;
   }
 };
 
+// floats of one staging buffer: k, q, alpha, the tile's v, beta and k . q per token
+template <int DK>
+__host__ __device__ constexpr int prefill_buf_floats(int W) {
+  return kPrefillChunk * (3 * DK + W + 2);
+}
+
 inline size_t prefill_lds_bytes(int dk, int W) {
-  return (2 * (size_t)kPrefillChunk * (3 * dk + W + 1) * sizeof(float) + 15) / 16 * 16;
+  const int floats = dk == 64 ? prefill_buf_floats<64>(W) : prefill_buf_floats<128>(W);
+  return (2 * (size_t)floats * sizeof(float) + 15) / 16 * 16;
 }
 
 // A chunk's inputs held in registers between the global loads and the LDS writes.
@@ -606,6 +614,38 @@ __device__ __forceinline__ void prefill_stage(const PrefillRegs<DK, W> &r, int n
   if ((int)threadIdx.x < n) B.beta[threadIdx.x] = r.beta;
 }
 
+// One token's inputs for a lane, read from the staged chunk.
+template <int NV, int C>
+struct PrefillToken {
+  float4 k[NV], q[NV], a[NV];
+  float v[C], beta, kq;
+};
+
+template <int DK, int C>
+__device__ __forceinline__ void prefill_token_read(const PrefillBuf<DK> &B, int t, int W, const Lane &L,
+                                                   PrefillToken<DK / 64, C> &x) {
+#pragma unroll
+  for (int e = 0; e < DK / 64; ++e) {
+    const int i = t * DK + 4 * L.r + 64 * e;
+    x.k[e] = *reinterpret_cast<const float4 *>(B.k + i);
+    x.q[e] = *reinterpret_cast<const float4 *>(B.q + i);
+    x.a[e] = *reinterpret_cast<const float4 *>(B.a + i);
+  }
+#pragma unroll
+  for (int c = 0; c < C; ++c) x.v[c] = B.v[t * W + L.col0 + c * L.slab];
+  x.beta = B.beta[t];
+  x.kq = B.kq[t];
+}
+
+template <int DK, int C>
+__device__ __forceinline__ void prefill_token_step(const Args &a, float4 (&s)[C][DK / 64],
+                                                   const PrefillToken<DK / 64, C> &x, int64_t row, const Unit &u,
+                                                   int W, const Lane &L) {
+  float o[C];
+  token_fused<DK / 64, C>(s, x.a, x.k, x.q, x.v, x.beta, x.kq, o);
+  store_cols<C>(a.out + (row * a.H + u.h) * a.dv + (int64_t)u.tile * W, L, o);
+}
+
 template <int DK, int C>
 __global__ __launch_bounds__(256) void prefill_kernel(Args a) {
   constexpr int NV = DK / 64;
@@ -638,37 +678,48 @@ __global__ __launch_bounds__(256) void prefill_kernel(Args a) {
   if (ck == 0) store_tile<DK, C, kVerifyStoreStream>(CK, s, L);
   if (Tb == 0) return;
 
-  PrefillBuf<DK> buf[2] = {PrefillBuf<DK>(reinterpret_cast<float *>(lds_dyn), W),
-                           PrefillBuf<DK>(reinterpret_cast<float *>(lds_dyn) + kPrefillChunk * (3 * DK + W + 1), W)};
+  // the two LDS buffers are addressed from the shared base each chunk (an array of
+  // buffer views indexed at run time would live in scratch and lose the LDS address space)
+  float *const lds = reinterpret_cast<float *>(lds_dyn);
+  constexpr int kBufFloats = prefill_buf_floats<DK>(W);
   const int nchunks = (Tb + kPrefillChunk - 1) / kPrefillChunk;
   PrefillRegs<DK, W> regs;
   prefill_fetch<DK, W>(a, c0, min(kPrefillChunk, Tb), u.h, u.tile, regs);
   for (int ci = 0; ci < nchunks; ++ci) {
     const int t0 = ci * kPrefillChunk;
     const int n = min(kPrefillChunk, Tb - t0);
-    PrefillBuf<DK> &B = buf[ci & 1];
+    PrefillBuf<DK> B(lds + (ci & 1) * kBufFloats, W);
     prefill_stage<DK, W>(regs, n, B);
     __syncthreads();
     if (ci + 1 < nchunks)
       prefill_fetch<DK, W>(a, c0 + t0 + kPrefillChunk, min(kPrefillChunk, Tb - t0 - kPrefillChunk), u.h, u.tile,
                            regs);
-    for (int t = 0; t < n; ++t) {
-      float4 kk[NV], qq[NV], aa[NV];
+    // k . q per token, once per workgroup: thread (t, chunk of DK / 16 channels), a
+    // 16-lane row per token
+    {
+      constexpr int CPT = DK / 16;
+      const int t = threadIdx.x >> 4, c = threadIdx.x & 15;
+      float p = 0.0f;
+      if (t < n) {
 #pragma unroll
-      for (int e = 0; e < NV; ++e) {
-        const int i = t * DK + 4 * L.r + 64 * e;
-        kk[e] = *reinterpret_cast<const float4 *>(B.k + i);
-        qq[e] = *reinterpret_cast<const float4 *>(B.q + i);
-        aa[e] = *reinterpret_cast<const float4 *>(B.a + i);
+        for (int e = 0; e < CPT; ++e) p = __builtin_fmaf(B.k[t * DK + c * CPT + e], B.q[t * DK + c * CPT + e], p);
       }
-      float vj[C];
-#pragma unroll
-      for (int c = 0; c < C; ++c) vj[c] = B.v[t * W + L.col0 + c * L.slab];
-      const float kq = row16_sum(lane_dot<NV>(kk, qq));
-      float o[C];
-      token_fused<NV, C>(s, aa, kk, qq, vj, B.beta[t], kq, o);
-      store_cols<C>(a.out + ((c0 + t0 + t) * (int64_t)a.H + u.h) * a.dv + (int64_t)u.tile * W, L, o);
+      p = row16_sum(p);
+      if (c == 0 && t < n) B.kq[t] = p;
+    }
+    __syncthreads();
+    // tokens in pairs: the second token's LDS reads are issued before the first computes
+    PrefillToken<NV, C> ta, tb;
+    prefill_token_read<DK, C>(B, 0, W, L, ta);
+    for (int t = 0; t < n; t += 2) {
+      const bool pair = t + 1 < n;
+      if (pair) prefill_token_read<DK, C>(B, t + 1, W, L, tb);
+      prefill_token_step<DK, C>(a, s, ta, c0 + t0 + t, u, W, L);
       if (t0 + t + 1 == ck) store_tile<DK, C, kVerifyStoreStream>(CK, s, L);
+      if (!pair) break;
+      if (t + 2 < n) prefill_token_read<DK, C>(B, t + 2, W, L, ta);
+      prefill_token_step<DK, C>(a, s, tb, c0 + t0 + t + 1, u, W, L);
+      if (t0 + t + 2 == ck) store_tile<DK, C, kVerifyStoreStream>(CK, s, L);
     }
   }
   store_tile<DK, C, kVerifyStoreStream>(S, s, L);
