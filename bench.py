@@ -372,6 +372,30 @@ def prefill_8k(D, K, synth, reps, tile_w=0):
                 tile_w=K.kda_query_variant(1, H, d, d, T_max=n, op=K.KDA_OP_PREFILL, tile_w=tile_w)[0])
 
 
+def state_transfer(D, K, synth, reps):
+    """Pack / unpack the states of 64 slots x 32 heads (128 MiB) between the slot cache and a
+    contiguous buffer on the GPU, and in pinned host memory over PCIe."""
+    torch = D.torch
+    w = synth.make(64, 32, 128, 128, num_slots=256, state_std=0.02, seed=81)
+    cache = D.f(w.cache)
+    tables = [D.i(t) for t in w.slot_tables]
+    nbytes = 64 * 32 * 128 * 128 * 4
+    dbuf = torch.empty(64, 32, 128, 128, device=D.dev)
+    hbuf = torch.empty(64, 32, 128, 128, pin_memory=True)
+    res = {}
+    for name, buf, op in (("pack_device", dbuf, K.kda_state_pack), ("unpack_device", dbuf, K.kda_state_unpack),
+                          ("pack_pinned_host", hbuf, K.kda_state_pack),
+                          ("unpack_pinned_host", hbuf, K.kda_state_unpack)):
+        n = reps if "device" in name else max(2, reps // 20)
+        op(cache, tables[0], buf)
+        ms = timed_region(D, lambda i: op(cache, tables[i % len(tables)], buf), n) / n
+        # a copy reads and writes the bytes once; over PCIe the host side is what counts
+        moved = 2 * nbytes if "device" in name else nbytes
+        res[name] = dict(us=round(ms * 1e3, 2), bytes=moved, gbs=round(moved / ms / 1e6, 1))
+        log(f"state transfer {name}: {ms * 1e3:.1f} us ({moved / ms / 1e6:.0f} GB/s)")
+    return res
+
+
 def copy_calibration(D, nbytes=256 << 20, reps=5):
     """A plain device copy of known size (for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)."""
     src = D.torch.empty(nbytes // 4, dtype=D.torch.float32, device=D.dev).normal_()
@@ -466,6 +490,7 @@ def main():
             spec_verify_b16_t8=spec_verify(D, K, synth, reps=200),
             mixed_b64_gated=mixed(D, K, synth, reps=200),
             prefill_8k_checkpoint=prefill_8k(D, K, synth, reps=5),
+            state_transfer_64x32_heads=state_transfer(D, K, synth, reps=100),
             headline_same_table_kernel_us=round(h["hot_ms"] * 1e3, 3),
         )
     if args.copy_calibration:

@@ -31,6 +31,8 @@ from .kda import (  # noqa: F401
     kda_prefill,
     kda_query_variant,
     kda_replay_commit,
+    kda_state_pack,
+    kda_state_unpack,
     kda_status_str,
     kda_verify_chunk,
     load_library,

@@ -1014,6 +1014,49 @@ __global__ __launch_bounds__(256) void commit_copy_kernel(Args a) {
 }
 
 // ----------------------------------------------------------------------------
+// State transfer (pack / unpack)
+// ----------------------------------------------------------------------------
+//
+// For prefill/decode disaggregation and offload ("Prefill/Decode
+// disaggregation and hybrid state offload": the KDA state is split by head
+// and by dimension and boundary states are kept outside the GPU): the heads
+// [head0, head0 + nheads) and value columns [col0, col0 + ncols) of each row's
+// slot are copied to or from buf[b][nheads][ncols][dk]. Within one head the
+// selected columns are one contiguous span of ncols * dk floats, so each
+// workgroup streams one (row, head) span with 128-bit accesses. buf may be
+// pinned host memory: the kernel then reads or writes it over PCIe directly.
+
+struct PackArgs {
+  float *cache;
+  int64_t num_slots, slot_stride;
+  const int32_t *slot_ids;
+  float *buf;
+  int32_t *dev_err;
+  int32_t H, dk, dv, head0, nheads, col0, ncols;
+};
+
+template <bool PACK>
+__global__ __launch_bounds__(256) void state_copy_kernel(PackArgs p) {
+  const int b = blockIdx.x / p.nheads, hh = blockIdx.x % p.nheads;
+  const int32_t slot = p.slot_ids[b];
+  if (slot < 0) return;
+  if (slot >= p.num_slots) {
+    if (p.dev_err && hh == 0 && threadIdx.x == 0) atomicOr(p.dev_err, KDA_DEVERR_SLOT);
+    return;
+  }
+  float *src = p.cache + (int64_t)slot * p.slot_stride + ((int64_t)(p.head0 + hh) * p.dv + p.col0) * p.dk;
+  float *dst = p.buf + ((int64_t)b * p.nheads + hh) * (int64_t)p.ncols * p.dk;
+  if (!PACK) {
+    float *t = src;
+    src = dst;
+    dst = t;
+  }
+  const int n4 = p.ncols * p.dk / 4;
+  for (int i = threadIdx.x; i < n4; i += blockDim.x)
+    reinterpret_cast<float4 *>(dst)[i] = reinterpret_cast<const float4 *>(src)[i];
+}
+
+// ----------------------------------------------------------------------------
 // Host side: checks, launch shape, dispatch
 // ----------------------------------------------------------------------------
 
@@ -1431,6 +1474,53 @@ int kda_query_variant(int32_t op, int32_t B, int32_t H, int32_t dk, int32_t dv, 
   if (tile_w) *tile_w = l.W;
   if (threads) *threads = 64 * l.waves;
   return KDA_OK;
+}
+
+static int state_copy(bool pack, float *cache, int64_t num_slots, int64_t slot_stride, const int32_t *slot_ids,
+                      int32_t B, int32_t H, int32_t dk, int32_t dv, int32_t head0, int32_t nheads, int32_t col0,
+                      int32_t ncols, float *buf, int32_t *dev_err, void *stream) {
+  if (B < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID;
+  if (head0 < 0 || nheads < 0 || head0 + nheads > H || col0 < 0 || ncols < 0 || col0 + ncols > dv)
+    return KDA_ERR_INVALID;
+  if (!dims_supported(dk, dv)) return KDA_ERR_UNSUPPORTED;
+  if (B == 0 || nheads == 0 || ncols == 0) return KDA_OK;
+  if (!slot_ids || !buf) return KDA_ERR_INVALID;
+  KDA_TRY(check_cache(cache, num_slots, slot_stride, H, dk, dv));
+  if (!aligned(buf, 16) || (dev_err && !aligned(dev_err, 4))) return KDA_ERR_ALIGN;
+  const int64_t blocks = (int64_t)B * nheads;
+  if (blocks > 0x7fffffff) return KDA_ERR_UNSUPPORTED;
+  PackArgs p;
+  p.cache = cache;
+  p.num_slots = num_slots;
+  p.slot_stride = slot_stride;
+  p.slot_ids = slot_ids;
+  p.buf = buf;
+  p.dev_err = dev_err;
+  p.H = H;
+  p.dk = dk;
+  p.dv = dv;
+  p.head0 = head0;
+  p.nheads = nheads;
+  p.col0 = col0;
+  p.ncols = ncols;
+  void *args[] = {&p};
+  const void *fn = pack ? (const void *)state_copy_kernel<true> : (const void *)state_copy_kernel<false>;
+  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, 0, (hipStream_t)stream);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_state_pack(const float *cache, int64_t num_slots, int64_t slot_stride, const int32_t *slot_ids,
+                   int32_t B, int32_t H, int32_t dk, int32_t dv, int32_t head0, int32_t nheads, int32_t col0,
+                   int32_t ncols, float *buf, int32_t *dev_err, void *stream) {
+  return state_copy(true, const_cast<float *>(cache), num_slots, slot_stride, slot_ids, B, H, dk, dv, head0,
+                    nheads, col0, ncols, buf, dev_err, stream);
+}
+
+int kda_state_unpack(float *cache, int64_t num_slots, int64_t slot_stride, const int32_t *slot_ids, int32_t B,
+                     int32_t H, int32_t dk, int32_t dv, int32_t head0, int32_t nheads, int32_t col0,
+                     int32_t ncols, const float *buf, int32_t *dev_err, void *stream) {
+  return state_copy(false, cache, num_slots, slot_stride, slot_ids, B, H, dk, dv, head0, nheads, col0, ncols,
+                    const_cast<float *>(buf), dev_err, stream);
 }
 
 const char *kda_status_str(int32_t status) {

@@ -86,6 +86,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_replay_commit.restype = ctypes.c_int
     lib.kda_prefill.argtypes = [P, i64, i64, P, P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P]
     lib.kda_prefill.restype = ctypes.c_int
+    for name in ("kda_state_pack", "kda_state_unpack"):
+        fn = getattr(lib, name)
+        fn.argtypes = [P, i64, i64, P, i32, i32, i32, i32, i32, i32, i32, i32, P, P, P]
+        fn.restype = ctypes.c_int
     lib.kda_query_variant.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32,
                                       ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.kda_query_variant.restype = ctypes.c_int
@@ -315,3 +319,35 @@ def kda_prefill(cache: torch.Tensor, slot_ids: torch.Tensor, cu_seqlens: torch.T
         _ptr(ckpt_pos), _ptr(ckpt), _ptr(dev_err), _ref(_opts(tile_w)), _stream(stream))
     if rc != KDA_OK:
         raise KdaError(rc, "kda_prefill")
+
+
+def _state_copy(name, cache, slot_ids, buf, heads, cols, dev_err, stream):
+    ns, stride, H, dv, dk = _cache(cache)
+    _dev(slot_ids, "slot_ids", (torch.int32,), 1)
+    B = slot_ids.shape[0]
+    head0, nheads = (0, H) if heads is None else (int(heads[0]), int(heads[1]) - int(heads[0]))
+    col0, ncols = (0, dv) if cols is None else (int(cols[0]), int(cols[1]) - int(cols[0]))
+    if not isinstance(buf, torch.Tensor) or buf.dtype != torch.float32 or not buf.is_contiguous():
+        raise TypeError("buf must be a contiguous float32 tensor")
+    if buf.device.type != "cuda" and not buf.is_pinned():
+        raise ValueError("buf must be on the GPU or in pinned host memory")
+    _shape(buf, "buf", (B, nheads, ncols, dk))
+    if dev_err is not None:
+        _dev(dev_err, "dev_err", (torch.int32,))
+    rc = getattr(load_library(), name)(cache.data_ptr(), ns, stride, slot_ids.data_ptr(), B, H, dk, dv, head0,
+                                       nheads, col0, ncols, buf.data_ptr(), _ptr(dev_err), _stream(stream))
+    if rc != KDA_OK:
+        raise KdaError(rc, name)
+
+
+def kda_state_pack(cache: torch.Tensor, slot_ids: torch.Tensor, buf: torch.Tensor, *, heads=None, cols=None,
+                   dev_err: Optional[torch.Tensor] = None, stream=None) -> None:
+    """buf[b] <- heads [h0, h1) x value columns [c0, c1) of slot slot_ids[b]; buf float32
+    [B, h1 - h0, c1 - c0, dk] on the GPU or in pinned host memory."""
+    _state_copy("kda_state_pack", cache, slot_ids, buf, heads, cols, dev_err, stream)
+
+
+def kda_state_unpack(cache: torch.Tensor, slot_ids: torch.Tensor, buf: torch.Tensor, *, heads=None, cols=None,
+                     dev_err: Optional[torch.Tensor] = None, stream=None) -> None:
+    """The inverse of kda_state_pack: slots <- buf."""
+    _state_copy("kda_state_unpack", cache, slot_ids, buf, heads, cols, dev_err, stream)

@@ -220,6 +220,31 @@ int kda_prefill(float *cache, int64_t num_slots, int64_t slot_stride,
                 const kda_options *opts, void *stream);
 
 /*
+ * State transfer for prefill/decode disaggregation and offload ("Kimi K3
+ * performance optimization in vLLM", section "Prefill/Decode disaggregation
+ * and hybrid state offload": the KDA state is split by head and by dimension,
+ * and boundary states are stored outside the GPU). For every row b with
+ * slot_ids[b] >= 0, kda_state_pack copies heads [head0, head0 + nheads) and
+ * value columns [col0, col0 + ncols) of slot slot_ids[b] to
+ * buf[b][nheads][ncols][dk] (float, contiguous), and kda_state_unpack copies
+ * them back. Bit-exact copies. buf is device memory or pinned host memory
+ * mapped for the device (hipHostMalloc); the kernel reads or writes it
+ * directly. Padding rows (slot < 0) leave their part of buf (pack) or the
+ * cache (unpack) untouched; slot >= num_slots sets KDA_DEVERR_SLOT. Ranges
+ * outside [0, H) or [0, dv) are KDA_ERR_INVALID; an empty range enqueues
+ * nothing.
+ */
+int kda_state_pack(const float *cache, int64_t num_slots, int64_t slot_stride,
+                   const int32_t *slot_ids, int32_t B, int32_t H, int32_t dk, int32_t dv,
+                   int32_t head0, int32_t nheads, int32_t col0, int32_t ncols,
+                   float *buf, int32_t *dev_err, void *stream);
+
+int kda_state_unpack(float *cache, int64_t num_slots, int64_t slot_stride,
+                     const int32_t *slot_ids, int32_t B, int32_t H, int32_t dk, int32_t dv,
+                     int32_t head0, int32_t nheads, int32_t col0, int32_t ncols,
+                     const float *buf, int32_t *dev_err, void *stream);
+
+/*
  * Host only. Reports the launch shape operation op (a kda_op) would use for
  * these sizes (tile_w value columns per workgroup, threads per workgroup),
  * chosen from the batch size and head count when requested_tile_w == 0 (the

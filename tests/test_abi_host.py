@@ -26,7 +26,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert set(declared_functions()) == {"kda_decode_step", "kda_verify_chunk", "kda_replay_commit",
-                                         "kda_prefill", "kda_query_variant", "kda_status_str"}
+                                         "kda_prefill", "kda_state_pack", "kda_state_unpack",
+                                         "kda_query_variant", "kda_status_str"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -220,3 +221,26 @@ def test_prefill_host_checks():
     assert _prefill(dk=96) == E.KDA_ERR_UNSUPPORTED
     assert _prefill(opts=ctypes.byref(kda.kda_options(64, 0))) == E.KDA_ERR_UNSUPPORTED
     assert _prefill(alpha=A + 4) == E.KDA_ERR_ALIGN
+
+
+def _pack(**over):
+    d = dict(cache=A, num_slots=8, slot_stride=4 * 128 * 128, slot_ids=A, B=4, H=4, dk=128, dv=128, head0=0,
+             nheads=4, col0=0, ncols=128, buf=A, dev_err=None, stream=None)
+    d.update(over)
+    return kda.load_library().kda_state_pack(*d.values())
+
+
+@needs_no_gpu
+def test_state_transfer_host_checks():
+    E = kda
+    assert _pack(B=0) == E.KDA_OK
+    assert _pack(nheads=0) == E.KDA_OK
+    assert _pack(ncols=0) == E.KDA_OK
+    assert _pack(head0=2, nheads=3) == E.KDA_ERR_INVALID
+    assert _pack(col0=100, ncols=29) == E.KDA_ERR_INVALID
+    assert _pack(head0=-1) == E.KDA_ERR_INVALID
+    assert _pack(buf=None) == E.KDA_ERR_INVALID
+    assert _pack(buf=A + 8) == E.KDA_ERR_ALIGN
+    assert _pack(dk=32) == E.KDA_ERR_UNSUPPORTED
+    assert kda.load_library().kda_state_unpack(A, 8, 4 * 128 * 128, A, 4, 4, 128, 128, 0, 4, 0, 128, None,
+                                               None, None) == E.KDA_ERR_INVALID
