@@ -55,17 +55,17 @@ def _load(path: Optional[str] = None):
     lib.kda_oracle_epilogue.argtypes = [P, ctypes.c_int, P, P, f64, P]
     lib.kda_oracle_epilogue.restype = None
     lib.kda_oracle_decode.argtypes = [P, i64, i64, P, i32, i32, i32, i32,
-                                      P, P, P, P, P, P, P, P, f64, i32, i32]
+                                      P, P, P, P, P, P, P, P, f64, i32, i32, i32]
     lib.kda_oracle_decode.restype = ctypes.c_int
     lib.kda_oracle_verify.argtypes = [P, i64, i64, P, P, i32, i32, i32, i32, i32, i32,
                                       P, P, P, P, P, P, P, P, f64, i32, i32,
-                                      P, P, P, P, P, i32, i32]
+                                      P, P, P, P, P, i32, i32, i32]
     lib.kda_oracle_verify.restype = ctypes.c_int
     lib.kda_oracle_commit.argtypes = [P, i64, i64, P, P, P, i32, i32, i32, i32, i32, i32,
-                                      P, P, P, P, i32, i32]
+                                      P, P, P, P, i32, i32, i32]
     lib.kda_oracle_commit.restype = ctypes.c_int
     lib.kda_oracle_prefill.argtypes = [P, i64, i64, P, P, i32, i32, i32, i32, i32,
-                                       P, P, P, P, P, P, P, P, i32, i32]
+                                       P, P, P, P, P, P, P, P, i32, i32, i32]
     lib.kda_oracle_prefill.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -136,7 +136,8 @@ def _slot_stride(cache: np.ndarray) -> int:
 
 
 def decode(cache, slot_ids, q, k, v, alpha, beta, *, out=None, gate=None, weight=None,
-           eps: float = 1e-6, state_fp32: bool = True, nthreads: Optional[int] = None, lib=None):
+           eps: float = 1e-6, prologue: bool = False, state_fp32: bool = True,
+           nthreads: Optional[int] = None, lib=None):
     """Single-token step for B rows, in place on ``cache`` [num_slots][H][dv][dk] float32.
 
     q, k: uint16 bf16 bits [B][H][dk]; v (and gate): [B][H][dv]; alpha [B][H][dk];
@@ -153,8 +154,8 @@ def decode(cache, slot_ids, q, k, v, alpha, beta, *, out=None, gate=None, weight
         out = np.full((B, H, dv), np.nan, np.float32)
     rc = lib.kda_oracle_decode(_ptr(cache), num_slots, _slot_stride(cache), _ptr(slot_ids),
                                B, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                               _ptr(out), _ptr(gate), _ptr(weight), float(eps), int(state_fp32),
-                               nthreads or default_threads())
+                               _ptr(out), _ptr(gate), _ptr(weight), float(eps), int(bool(prologue)),
+                               int(state_fp32), nthreads or default_threads())
     if rc < 0:
         raise ValueError("oracle decode: invalid arguments")
     return out, rc
@@ -162,8 +163,8 @@ def decode(cache, slot_ids, q, k, v, alpha, beta, *, out=None, gate=None, weight
 
 def verify(cache, slot_ids, cu_seqlens, T_max, q, k, v, alpha, beta, *, mode=REPLAY,
            t1_inplace: bool = False, out=None, gate=None, weight=None, eps: float = 1e-6,
-           replay=None, draft=None, state_fp32: bool = True, nthreads: Optional[int] = None,
-           lib=None):
+           replay=None, draft=None, prologue: bool = False, state_fp32: bool = True,
+           nthreads: Optional[int] = None, lib=None):
     """Packed speculative chunk. Token arrays are [n_tok][H][.]; row b owns
     tokens [cu[b], cu[b+1]). Returns (out, replay dict or None, draft or None, error bits).
     replay buffers are rk [B][T_max][H][dk] (uint16), rv [B][T_max][H][dv] (uint16),
@@ -193,14 +194,14 @@ def verify(cache, slot_ids, cu_seqlens, T_max, q, k, v, alpha, beta, *, mode=REP
                                _ptr(gate), _ptr(weight), float(eps), int(mode), int(bool(t1_inplace)),
                                _ptr(rb.get("rk")), _ptr(rb.get("rv")), _ptr(rb.get("ralpha")),
                                _ptr(rb.get("rbeta")), _ptr(draft if mode == PER_POSITION else None),
-                               int(state_fp32), nthreads or default_threads())
+                               int(bool(prologue)), int(state_fp32), nthreads or default_threads())
     if rc < 0:
         raise ValueError("oracle verify: invalid arguments")
     return out, (replay if mode == REPLAY else None), (draft if mode == PER_POSITION else None), rc
 
 
 def commit(cache, slot_ids, cu_seqlens, accepted_len, T_max, k, v, alpha, beta, *,
-           state_fp32: bool = True, nthreads: Optional[int] = None, lib=None):
+           prologue: bool = False, state_fp32: bool = True, nthreads: Optional[int] = None, lib=None):
     """Slot of row b <- state after the first accepted_len[b] tokens of row b's chunk
     (in place on ``cache``). Returns the error bits."""
     lib = lib or _load()
@@ -215,15 +216,15 @@ def commit(cache, slot_ids, cu_seqlens, accepted_len, T_max, k, v, alpha, beta, 
     alpha, beta = (_c(x, np.float32) for x in (alpha, beta))
     rc = lib.kda_oracle_commit(_ptr(cache), num_slots, _slot_stride(cache), _ptr(slot_ids), _ptr(cu),
                                _ptr(acc), B, int(T_max), n_tok, H, dk, dv,
-                               _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), int(state_fp32),
-                               nthreads or default_threads())
+                               _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), int(bool(prologue)),
+                               int(state_fp32), nthreads or default_threads())
     if rc < 0:
         raise ValueError("oracle commit: invalid arguments")
     return rc
 
 
 def prefill(cache, slot_ids, cu_seqlens, q, k, v, alpha, beta, *, ckpt_pos=None, out=None,
-            state_fp32: bool = True, nthreads: Optional[int] = None, lib=None):
+            prologue: bool = False, state_fp32: bool = True, nthreads: Optional[int] = None, lib=None):
     """Whole prompts in one pass (in place on ``cache``). Token arrays are [n_tok][H][.];
     row b owns tokens [cu[b], cu[b+1]). Returns (out [n_tok][H][dv], ckpt [B][H][dv][dk]
     or None, error bits); ckpt[b] is the state after the first ckpt_pos[b] tokens."""
@@ -242,7 +243,7 @@ def prefill(cache, slot_ids, cu_seqlens, q, k, v, alpha, beta, *, ckpt_pos=None,
         out = np.full((n_tok, H, dv), np.nan, np.float32)
     rc = lib.kda_oracle_prefill(_ptr(cache), num_slots, _slot_stride(cache), _ptr(slot_ids), _ptr(cu),
                                 B, n_tok, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                                _ptr(out), _ptr(pos), _ptr(ckpt), int(state_fp32),
+                                _ptr(out), _ptr(pos), _ptr(ckpt), int(bool(prologue)), int(state_fp32),
                                 nthreads or default_threads())
     if rc < 0:
         raise ValueError("oracle prefill: invalid arguments")

@@ -47,6 +47,16 @@
  * outside [0, T_b] sets bit 4; a checkpoint position outside [0, T_b] (prefill)
  * sets bit 8. A row with an error is skipped entirely.
  *
+ * Raw inputs (prologue != 0): q, k, alpha and beta hold the raw projections and
+ * the oracle prepares them per (token, head) first, in double:
+ *     k <- k / sqrt(sum_i k_i^2 + 1e-12)
+ *     q <- q / sqrt(sum_i q_i^2 + 1e-12) / sqrt(dk)
+ *     alpha_i <- exp(-softplus(alpha_i)) = exp(-log(1 + exp(alpha_i)))
+ *     beta <- sigmoid(beta) = 1 / (1 + exp(-beta))
+ * (the normalization and gate activations that precede the recurrence; the
+ * fused form of "Hyper Optimizing Kimi K3 in vLLM", section "Finding time
+ * between operators"). Replay buffers then hold the raw values.
+ *
  * Prefill ("Kimi K3 performance optimization in vLLM", section "Internal KDA
  * prefix checkpoint"): one pass over a row's whole prompt from the slot's
  * state, outputs for every token, the final state written back to the slot,
@@ -148,6 +158,24 @@ void kda_oracle_epilogue(const double *o, int dv, const double *g, const double 
     }
 }
 
+/* Raw projections of one (token, head) to the recurrence's inputs (see the header). */
+static void prepare_inputs(double *q, double *k, double *alpha, double *beta, int dk)
+{
+    double kk = 0.0, qq = 0.0;
+    for (int i = 0; i < dk; ++i) {
+        kk += k[i] * k[i];
+        qq += q[i] * q[i];
+    }
+    const double kn = 1.0 / sqrt(kk + 1e-12);
+    const double qn = 1.0 / sqrt(qq + 1e-12) / sqrt((double)dk);
+    for (int i = 0; i < dk; ++i) {
+        k[i] *= kn;
+        q[i] *= qn;
+        alpha[i] = exp(-log1p(exp(alpha[i])));
+    }
+    *beta = 1.0 / (1.0 + exp(-*beta));
+}
+
 /* ---------------------------------------------------------------------------
  * Batch drivers: slot lookup, token ranges, layouts, modes. One work item per
  * (row b, head h); items are independent, so threads only split the list.
@@ -170,6 +198,7 @@ typedef struct {
     float *ralpha, *rbeta, *draft;
     const int32_t *ckpt_pos;
     float *ckpt;
+    int32_t prologue;
     int32_t state_fp32;
 } call_t;
 
@@ -244,6 +273,8 @@ static int run_item(const call_t *c, int b, int h)
         for (int j = 0; j < dv; ++j)
             v[t * dv + j] = bf16_to_double(c->v[r * dv + j]);
         be[t] = (double)c->beta[r];
+        if (c->prologue)
+            prepare_inputs(q + t * dk, k + t * dk, a + t * dk, &be[t], dk);
     }
 
     if (c->kind == KIND_PREFILL && ckpt_at >= 0) {
@@ -376,7 +407,7 @@ int kda_oracle_decode(float *cache, int64_t num_slots, int64_t slot_stride,
                       const uint16_t *q, const uint16_t *k, const uint16_t *v,
                       const float *alpha, const float *beta, float *out,
                       const uint16_t *gate, const float *weight, double eps,
-                      int32_t state_fp32, int32_t nthreads)
+                      int32_t prologue, int32_t state_fp32, int32_t nthreads)
 {
     if (!dims_ok(B, H, dk, dv, num_slots, slot_stride))
         return -1;
@@ -406,6 +437,7 @@ int kda_oracle_decode(float *cache, int64_t num_slots, int64_t slot_stride,
     c.gate = gate;
     c.weight = weight;
     c.eps = eps;
+    c.prologue = prologue;
     c.state_fp32 = state_fp32;
     return run_call(&c, nthreads);
 }
@@ -426,7 +458,7 @@ int kda_oracle_verify(float *cache, int64_t num_slots, int64_t slot_stride,
                       const uint16_t *gate, const float *weight, double eps,
                       int32_t mode, int32_t t1_inplace,
                       uint16_t *rk, uint16_t *rv, float *ralpha, float *rbeta, float *draft,
-                      int32_t state_fp32, int32_t nthreads)
+                      int32_t prologue, int32_t state_fp32, int32_t nthreads)
 {
     if (!dims_ok(B, H, dk, dv, num_slots, slot_stride) || T_max < 1 || n_tok < 0)
         return -1;
@@ -470,6 +502,7 @@ int kda_oracle_verify(float *cache, int64_t num_slots, int64_t slot_stride,
     c.ralpha = ralpha;
     c.rbeta = rbeta;
     c.draft = draft;
+    c.prologue = prologue;
     c.state_fp32 = state_fp32;
     return run_call(&c, nthreads);
 }
@@ -485,7 +518,7 @@ int kda_oracle_commit(float *cache, int64_t num_slots, int64_t slot_stride,
                       const int32_t *accepted_len,
                       int32_t B, int32_t T_max, int32_t n_tok, int32_t H, int32_t dk, int32_t dv,
                       const uint16_t *k, const uint16_t *v, const float *alpha, const float *beta,
-                      int32_t state_fp32, int32_t nthreads)
+                      int32_t prologue, int32_t state_fp32, int32_t nthreads)
 {
     if (!dims_ok(B, H, dk, dv, num_slots, slot_stride) || T_max < 1 || n_tok < 0)
         return -1;
@@ -512,6 +545,7 @@ int kda_oracle_commit(float *cache, int64_t num_slots, int64_t slot_stride,
     c.v = v;
     c.alpha = alpha;
     c.beta = beta;
+    c.prologue = prologue;
     c.state_fp32 = state_fp32;
     return run_call(&c, nthreads);
 }
@@ -528,7 +562,7 @@ int kda_oracle_prefill(float *cache, int64_t num_slots, int64_t slot_stride,
                        const uint16_t *q, const uint16_t *k, const uint16_t *v,
                        const float *alpha, const float *beta, float *out,
                        const int32_t *ckpt_pos, float *ckpt,
-                       int32_t state_fp32, int32_t nthreads)
+                       int32_t prologue, int32_t state_fp32, int32_t nthreads)
 {
     if (!dims_ok(B, H, dk, dv, num_slots, slot_stride) || n_tok < 0)
         return -1;
@@ -560,6 +594,7 @@ int kda_oracle_prefill(float *cache, int64_t num_slots, int64_t slot_stride,
     c.out = out;
     c.ckpt_pos = ckpt_pos;
     c.ckpt = ckpt;
+    c.prologue = prologue;
     c.state_fp32 = state_fp32;
     return run_call(&c, nthreads);
 }

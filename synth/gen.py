@@ -24,6 +24,8 @@ normal unless noted), shaped ``[steps][n_tok][H][.]``:
 Derived inputs:
   k = k_raw / |k_raw|_2 ; q = q_raw / |q_raw|_2 / sqrt(dk)  (float64, then bf16 RNE)
   alpha = exp(-softplus(a_raw)) ; beta = sigmoid(b_raw)      (float64, then float32)
+The raw projections themselves are kept too, for the raw-input mode: q_raw and
+k_raw as bf16 (RNE of the float32 draws), a_raw and b_raw as float32.
 """
 
 from __future__ import annotations
@@ -57,6 +59,7 @@ class Workload:
     q, k: uint16 bf16 bits [steps][n_tok][H][dk]; v: [steps][n_tok][H][dv]
     alpha: float32 [steps][n_tok][H][dk]; beta: float32 [steps][n_tok][H]
     gate: uint16 bf16 bits [steps][n_tok][H][dv] or None
+    q_raw, k_raw: uint16 bf16 bits like q, k; a_raw: float32 like alpha; b_raw: like beta
     cache: float32 [num_slots][H][dv][dk] (value column j holds its dk key channels)
     slot_ids: int32 [B]; slot_tables: int32 [num_slots // B][B], disjoint, first == slot_ids
     cu_seqlens: int32 [B + 1]; accepted: int32 [B] (0 for rows with one token) or None
@@ -81,6 +84,10 @@ class Workload:
     slot_tables: np.ndarray
     accepted: Optional[np.ndarray]
     seed: int
+    q_raw: Optional[np.ndarray] = None
+    k_raw: Optional[np.ndarray] = None
+    a_raw: Optional[np.ndarray] = None
+    b_raw: Optional[np.ndarray] = None
 
     @property
     def n_tok(self) -> int:
@@ -162,6 +169,7 @@ def make(B: int, H: int, dk: int, dv: int, *, seqlens=None, steps: int = 1,
         gate=f32_to_bf16_bits(g_raw) if gate else None,
         cache=cache, slot_ids=slot_ids, slot_tables=slot_tables,
         accepted=accepted, seed=seed,
+        q_raw=f32_to_bf16_bits(q_raw), k_raw=f32_to_bf16_bits(k_raw), a_raw=a_raw, b_raw=b_raw,
     )
 
 

@@ -8,7 +8,8 @@ with the fact it checks. The facts:
     heads, through the single-head routine and through the batch drivers;
   * closed forms: alpha = 0 erases the state, beta = 0 gives a pure decay,
     one-hot write-then-read returns v, associative recall, the output gate's
-    constants;
+    constants, the raw-input preparation on inputs where it is exact or has a
+    hand-derived value;
   * structure: linearity, column permutation equivariance, commit equals
     step-by-step, slot / row / error handling, fp32 state storage.
 """
@@ -342,6 +343,107 @@ def check_gate_closed_form(lib):
             assert _rel(gated[b, h], o / rms * weight * sig) <= 1e-6, (b, h)
 
 
+def _prologue_case():
+    """Raw projections whose normalization and activations have closed forms.
+
+    Head 0: k along channels 0 and 70 as (3, 4) -> (0.6, 0.8); q along channels 0
+    and 100 as (3, 4) -> (0.6, 0.8) / sqrt(128); a = 0 on even channels and ln 3 on
+    odd ones -> alpha = 1/(1 + e^a) = 1/2 and 1/4; b = ln 3 -> beta = 3/4; v = 0.
+    Head 1: zero key (normalizes to zero), q = 2 e_5 -> e_5 / sqrt(128), a = ln 3,
+    b = 0, v nonzero (must not reach the state). The state starts at all ones.
+    """
+    dk, dv, H = 128, 4, 2
+    ln3 = math.log(3.0)
+    q = np.zeros((1, H, dk), np.float32)
+    k = np.zeros((1, H, dk), np.float32)
+    v = np.zeros((1, H, dv), np.float32)
+    a = np.zeros((1, H, dk), np.float32)
+    b = np.zeros((1, H), np.float32)
+    k[0, 0, 0], k[0, 0, 70] = 3.0, 4.0
+    q[0, 0, 0], q[0, 0, 100] = 3.0, 4.0
+    a[0, 0, 1::2] = ln3
+    b[0, 0] = ln3
+    q[0, 1, 5] = 2.0
+    a[0, 1, :] = ln3
+    v[0, 1] = [1.0, 2.0, 3.0, 4.0]
+    # hand-derived result of one token
+    S = np.ones((H, dk, dv))
+    S[0, 0::2] = 0.5
+    S[0, 1::2] = 0.25
+    d = 0.75 * (0.0 - (0.6 * 0.5 + 0.8 * 0.5))      # beta (v - S^T k) = -0.525
+    S[0, 0] = 0.5 + 0.6 * d
+    S[0, 70] = 0.5 + 0.8 * d
+    S[1] = 0.25
+    o = np.zeros((H, dv))
+    o[0] = (0.6 * S[0, 0] + 0.8 * S[0, 100]) / math.sqrt(dk)
+    o[1] = S[1, 5] / math.sqrt(dk)
+    cache = np.ones((1, H, dv, dk), np.float32)
+    return dict(q=_bf(q), k=_bf(k), v=_bf(v), a=a, b=b, S=S, o=o, cache=cache)
+
+
+def check_prologue_closed_form(lib):
+    """Raw-input mode through every batch driver against the hand-derived state and
+    read-out of one token; the replay buffer keeps the raw inputs."""
+    c = _prologue_case()
+    cu = np.array([0, 1], np.int32)
+
+    def state(cache):
+        return cache[0].transpose(0, 2, 1)
+
+    cache = c["cache"].copy()
+    out, rc = oracle.decode(cache, [0], c["q"], c["k"], c["v"], c["a"], c["b"], prologue=True, lib=lib)
+    assert rc == 0
+    assert _rel(state(cache), c["S"]) <= 1e-7
+    assert _rel(out[0], c["o"]) <= 1e-7
+    assert np.all(state(cache)[1] == np.float32(0.25))          # zero key: a pure decay
+    cache = c["cache"].copy()
+    out, rb, _, rc = oracle.verify(cache, [0], cu, 1, c["q"], c["k"], c["v"], c["a"], c["b"],
+                                   mode=oracle.REPLAY, prologue=True, lib=lib)
+    assert rc == 0
+    assert _rel(out[0], c["o"]) <= 1e-7
+    assert np.array_equal(cache, c["cache"])
+    assert np.array_equal(rb["rk"][0], c["k"]) and np.array_equal(rb["ralpha"][0], c["a"])
+    assert np.array_equal(rb["rbeta"][0], c["b"])
+    rc = oracle.commit(cache, [0], cu, np.array([1], np.int32), 1, rb["rk"][0], rb["rv"][0],
+                       rb["ralpha"][0], rb["rbeta"][0], prologue=True, lib=lib)
+    assert rc == 0
+    assert _rel(state(cache), c["S"]) <= 1e-7
+    cache = c["cache"].copy()
+    out, ckpt, rc = oracle.prefill(cache, [0], cu, c["q"], c["k"], c["v"], c["a"], c["b"],
+                                   ckpt_pos=np.array([1], np.int32), prologue=True, lib=lib)
+    assert rc == 0
+    assert _rel(out[0], c["o"]) <= 1e-7
+    assert _rel(state(cache), c["S"]) <= 1e-7
+    assert np.array_equal(ckpt[0], cache[0])
+
+
+def check_prologue_prepared_equivalence(lib):
+    """Raw inputs whose preparation has an exact value give what the prepared inputs
+    passed directly give, to within the fp32 rounding of the state (the 1e-12 in the
+    norms moves the prepared values by about 1e-14): a one-hot key, a query of norm
+    8 with dk = 64 (the scale is 1/64), a = 0 (alpha = 1/2) and b = 0 (beta = 1/2),
+    over several tokens."""
+    w = synth.make(2, 3, 64, 8, steps=4, num_slots=3, state_std=0.1, seed=23)
+    rng = np.random.Generator(np.random.PCG64(24))
+    cache_raw, cache_prep = w.cache.copy(), w.cache.copy()
+    for t in range(4):
+        k = np.zeros((w.B, w.H, 64), np.float32)
+        q = np.zeros((w.B, w.H, 64), np.float32)
+        for bh in np.ndindex(w.B, w.H):
+            k[bh][rng.integers(64)] = rng.choice([-2.0, 0.5, 3.0])
+            q[bh][rng.permutation(64)[:4]] = 4.0 * rng.choice([-1.0, 1.0], 4)
+        kp = k / np.abs(k).max(axis=-1, keepdims=True)
+        zeros_a = np.zeros((w.B, w.H, 64), np.float32)
+        zeros_b = np.zeros((w.B, w.H), np.float32)
+        o1, rc1 = oracle.decode(cache_raw, w.slot_ids, _bf(q), _bf(k), w.v[t], zeros_a, zeros_b,
+                                prologue=True, lib=lib)
+        o2, rc2 = oracle.decode(cache_prep, w.slot_ids, _bf(q / 64.0), _bf(kp), w.v[t],
+                                np.full_like(zeros_a, 0.5), np.full_like(zeros_b, 0.5), lib=lib)
+        assert rc1 == 0 and rc2 == 0
+        assert _rel(cache_raw, cache_prep) <= 1e-6, t
+        assert _rel(o1, o2) <= 1e-6, t
+
+
 # ---------------------------------------------------------------- structure
 
 def check_commit_equals_steps(lib):
@@ -481,4 +583,5 @@ CHECKS = [
     check_write_then_read, check_alpha_zero, check_beta_zero, check_associative_recall,
     check_linearity, check_gate_closed_form, check_commit_equals_steps,
     check_column_permutation, check_slot_handling, check_fp32_state_storage, check_bounded_state,
+    check_prologue_closed_form, check_prologue_prepared_equivalence,
 ]

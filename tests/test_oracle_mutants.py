@@ -49,6 +49,14 @@ MUTANTS = [
     ("gate_sum_not_mean", "ms /= (double)dv;", "ms /= 1.0;", 1),
     ("gate_sigmoid_sign", "exp(-g[j])", "exp(g[j])", 1),
     ("gate_eps_dropped", "sqrt(ms + eps)", "sqrt(ms)", 1),
+    ("prologue_q_unscaled", "sqrt(qq + 1e-12) / sqrt((double)dk)", "sqrt(qq + 1e-12)", 1),
+    ("prologue_k_not_normalized", "k[i] *= kn;", "k[i] *= 1.0;", 1),
+    ("prologue_q_norm_from_k", "qq += q[i] * q[i];", "qq += k[i] * k[i];", 1),
+    ("prologue_half_norm", "kk += k[i] * k[i];", "kk += i < dk / 2 ? k[i] * k[i] : 0.0;", 1),
+    ("prologue_alpha_as_exp", "exp(-log1p(exp(alpha[i])))", "exp(-alpha[i])", 1),
+    ("prologue_alpha_as_sigmoid", "exp(-log1p(exp(alpha[i])))", "1.0 / (1.0 + exp(-alpha[i]))", 1),
+    ("prologue_beta_sign", "1.0 / (1.0 + exp(-*beta))", "1.0 / (1.0 + exp(*beta))", 1),
+    ("prologue_ignored", "if (c->prologue)", "if (0)", 1),
 ]
 
 RUNNER = r"""

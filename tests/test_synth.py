@@ -28,6 +28,10 @@ def test_workloads_are_deterministic_and_shaped():
     assert m.q.shape == (1, 7, 2, 8) and m.v.shape == (1, 7, 2, 16) and m.gate.shape == (1, 7, 2, 16)
     assert len(set(m.slot_ids.tolist())) == 5 and m.slot_ids.max() < 9
     assert m.accepted[0] == 0 and 1 <= m.accepted[1] <= 3 and m.accepted[2] == 0 and 1 <= m.accepted[3] <= 2
+    assert m.q_raw.shape == m.q.shape and m.q_raw.dtype == np.uint16 and m.k_raw.shape == m.k.shape
+    assert m.a_raw.shape == m.alpha.shape and m.a_raw.dtype == np.float32 and m.b_raw.shape == m.beta.shape
+    assert np.array_equal(synth.make(5, 2, 8, 16, seqlens=[1, 3, 0, 2, 1], num_slots=9, state_std=0.02,
+                                     gate=True).a_raw, m.a_raw)
     kf = synth.bf16_bits_to_f32(m.k).astype(np.float64)
     assert np.allclose(np.linalg.norm(kf, axis=-1), 1.0, atol=1e-2)
     assert np.all((m.alpha > 0) & (m.alpha < 1)) and np.all((m.beta > 0) & (m.beta < 1))
