@@ -242,6 +242,52 @@ def b1_latency(D, K, synth):
                 us_per_step_graph=round(g_ms * 1e3, 3), tile_w=K.kda_query_variant(1, 32, 128, 128)[0])
 
 
+def raw_inputs_decode(D, K, synth, reps):
+    """Single-token step from raw projections (q/k normalization and the alpha / beta
+    activations inside the kernel) against the prepared-input step, at B=1 and B=64,
+    with a bf16 output too; and, for scale, the same preparation done by separate
+    torch kernels ahead of the prepared-input step."""
+    torch = D.torch
+    rows = []
+    for B in (1, 64):
+        w = synth.make(B, 32, 128, 128, num_slots=256, state_std=0.02, seed=40 + B, name=f"raw_b{B}")
+        cache = D.f(w.cache)
+        tables = [D.i(t) for t in w.slot_tables]
+        prep = dict(q=D.bf(w.q[0]), k=D.bf(w.k[0]), v=D.bf(w.v[0]), alpha=D.f(w.alpha[0]), beta=D.f(w.beta[0]))
+        raw = dict(q=D.bf(w.q_raw[0]), k=D.bf(w.k_raw[0]), v=prep["v"], alpha=D.f(w.a_raw[0]),
+                   beta=D.f(w.b_raw[0]))
+        out = torch.empty(B, 32, 128, device=D.dev)
+        out16 = torch.empty(B, 32, 128, device=D.dev, dtype=torch.bfloat16)
+        tmp = {}
+
+        def run(x, o, flag):
+            return lambda i: K.kda_decode_step(cache, tables[i % len(tables)], x["q"], x["k"], x["v"],
+                                               x["alpha"], x["beta"], o, raw_inputs=flag)
+
+        def unfused(i):
+            tmp["k"] = torch.nn.functional.normalize(raw["k"].float(), dim=-1, eps=1e-6).to(torch.bfloat16)
+            tmp["q"] = (torch.nn.functional.normalize(raw["q"].float(), dim=-1, eps=1e-6)
+                        * (128 ** -0.5)).to(torch.bfloat16)
+            tmp["alpha"] = torch.exp(-torch.nn.functional.softplus(raw["alpha"]))
+            tmp["beta"] = torch.sigmoid(raw["beta"])
+            K.kda_decode_step(cache, tables[i % len(tables)], tmp["q"], tmp["k"], raw["v"], tmp["alpha"],
+                              tmp["beta"], out)
+
+        graph, eager = {}, {}
+        for name, fn in (("prepared_inputs", run(prep, out, False)), ("raw_inputs_fused", run(raw, out, True)),
+                         ("raw_inputs_fused_bf16_out", run(raw, out16, True)),
+                         ("torch_preparation_then_step", unfused)):
+            for i in range(10):
+                fn(i)
+            eager[name] = round(timed_region(D, fn, reps) / reps * 1e3, 3)
+            if name != "torch_preparation_then_step":   # torch's own kernels stay out of graphs
+                graph[name] = round(graph_ms(D, fn, reps) * 1e3, 3)
+        rows.append(dict(B=B, us_per_step_graph=graph, us_per_step_eager_python=eager))
+        log(f"raw inputs B={B}: graph " + ", ".join(f"{k} {v:.2f}" for k, v in graph.items())
+            + " us; eager " + ", ".join(f"{k} {v:.2f}" for k, v in eager.items()) + " us")
+    return rows
+
+
 def _replay_bufs(torch, dev, B, T, H, dk, dv):
     return dict(k=torch.zeros(B, T, H, dk, dtype=torch.bfloat16, device=dev),
                 v=torch.zeros(B, T, H, dv, dtype=torch.bfloat16, device=dev),
@@ -491,6 +537,7 @@ def main():
             mixed_b64_gated=mixed(D, K, synth, reps=200),
             prefill_8k_checkpoint=prefill_8k(D, K, synth, reps=5),
             state_transfer_64x32_heads=state_transfer(D, K, synth, reps=100),
+            raw_inputs_decode=raw_inputs_decode(D, K, synth, reps=200),
             headline_same_table_kernel_us=round(h["hot_ms"] * 1e3, 3),
         )
     if args.copy_calibration:

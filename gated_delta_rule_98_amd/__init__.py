@@ -20,7 +20,9 @@ from .kda import (  # noqa: F401
     KDA_OP_DECODE,
     KDA_OP_PREFILL,
     KDA_OP_VERIFY,
+    KDA_OUT_BF16,
     KDA_PER_POSITION,
+    KDA_RAW_INPUTS,
     KDA_REPLAY,
     KDA_VERIFY_AUTO,
     KDA_VERIFY_CHUNKED,

@@ -58,6 +58,8 @@ struct Args {
   float *ckpt;
   float eps;
   int32_t B, H, dv, T_max, n_tok, ntile, mode, t1_inplace;
+  int32_t raw;       // q, k, alpha, beta are raw projections (KDA_RAW_INPUTS)
+  int32_t out_bf16;  // out holds bf16 (KDA_OUT_BF16)
 };
 
 // ----------------------------------------------------------------------------
@@ -184,6 +186,85 @@ __device__ __forceinline__ void token_fused(float4 (&s)[C][NV], const float4 (&a
       s[c][e].w = __builtin_fmaf(k[e].w, d, s[c][e].w);
     }
     o[c] = __builtin_fmaf(kq, d, p[c]);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Raw-input preparation
+// ----------------------------------------------------------------------------
+//
+// With raw projections as inputs, each (token, head) is prepared before the
+// recurrence: k and q are divided by their L2 norm over all dk channels (q is
+// also scaled by 1/sqrt(dk)), alpha = exp(-softplus(a)) = 1 / (1 + e^a) and
+// beta = sigmoid(b) = 1 / (1 + e^-b). It is the normalization and gate
+// activation work that otherwise runs as separate small kernels ahead of the
+// recurrence, fused in ("Hyper Optimizing Kimi K3 in vLLM", section "Finding
+// time between operators"). Every op prepares through these functions on a
+// 16-lane row with the column engine's channel layout, so the prepared values,
+// and the states built from them, are the same bits in decode, verify, commit
+// and prefill. The hardware exp2, reciprocal and reciprocal square root are
+// each within about one ulp; exp's argument is a * log2(e) rounded to fp32.
+
+constexpr float kLog2e = 1.44269504088896341f;
+
+// x scaled by scale / sqrt(sum over the row's channels of x^2 + 1e-12)
+template <int NV>
+__device__ __forceinline__ void prep_normalize(float4 (&x)[NV], float scale) {
+  const float f = __builtin_amdgcn_rsqf(row16_sum(lane_dot<NV>(x, x)) + 1e-12f) * scale;
+#pragma unroll
+  for (int e = 0; e < NV; ++e) {
+    x[e].x = x[e].x * f;
+    x[e].y = x[e].y * f;
+    x[e].z = x[e].z * f;
+    x[e].w = x[e].w * f;
+  }
+}
+
+// 1 / (1 + e^x)
+__device__ __forceinline__ float prep_sigmoid_neg(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * kLog2e));
+}
+
+template <int NV>
+__device__ __forceinline__ void prep_decay(float4 (&a)[NV]) {
+#pragma unroll
+  for (int e = 0; e < NV; ++e) {
+    a[e].x = prep_sigmoid_neg(a[e].x);
+    a[e].y = prep_sigmoid_neg(a[e].y);
+    a[e].z = prep_sigmoid_neg(a[e].z);
+    a[e].w = prep_sigmoid_neg(a[e].w);
+  }
+}
+
+__device__ __forceinline__ float prep_beta(float b) { return prep_sigmoid_neg(-b); }
+
+// In-place preparation of tokens [0, n) staged in LDS as float [t][DK] for k,
+// alpha (and q when non-null) and beta [t]: one 16-lane row per token. Must be
+// reached by the whole workgroup between two barriers.
+template <int DK>
+__device__ __forceinline__ void prep_staged(float *k, float *q, float *al, float *beta, int n) {
+  constexpr int NV = DK / 64;
+  const int rows = blockDim.x >> 4, r = threadIdx.x & 15;
+  for (int t = threadIdx.x >> 4; t < n; t += rows) {
+    float4 kk[NV], qq[NV], aa[NV];
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      const int i = t * DK + 4 * r + 64 * e;
+      kk[e] = *reinterpret_cast<const float4 *>(k + i);
+      aa[e] = *reinterpret_cast<const float4 *>(al + i);
+      if (q) qq[e] = *reinterpret_cast<const float4 *>(q + i);
+    }
+    prep_normalize<NV>(kk, 1.0f);
+    prep_decay<NV>(aa);
+    if (q) prep_normalize<NV>(qq, 1.0f / __builtin_sqrtf((float)DK));
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      const int i = t * DK + 4 * r + 64 * e;
+      *reinterpret_cast<float4 *>(k + i) = kk[e];
+      *reinterpret_cast<float4 *>(al + i) = aa[e];
+      if (q) *reinterpret_cast<float4 *>(q + i) = qq[e];
+    }
+    if (r == 0) beta[t] = prep_beta(beta[t]);
   }
 }
 
@@ -329,15 +410,45 @@ __device__ __forceinline__ void store_cols(float *dst, const Lane &L, const floa
     if (L.r == c) dst[L.col0 + c * L.slab] = o[c];
 }
 
+// fp32 to bf16, round to nearest even (NaN stays a quiet NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Output element idx of out: bf16 or fp32. Kernels on the hot paths pass a
+// compile-time bf16 (a run-time choice costs them registers and occupancy).
+__device__ __forceinline__ void put_out(const Args &a, bool bf16, int64_t idx, float y) {
+  if (bf16)
+    reinterpret_cast<uint16_t *>(a.out)[idx] = f32_to_bf16(y);
+  else
+    a.out[idx] = y;
+}
+
+// store_cols into out at element base
+template <int C>
+__device__ __forceinline__ void store_out(const Args &a, bool bf16, int64_t base, const Lane &L,
+                                          const float (&o)[C]) {
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+    if (L.r == c) put_out(a, bf16, base + L.col0 + c * L.slab, o[c]);
+}
+
+// Input/output variant of the decode and verify kernels: bit 0 = raw inputs,
+// bit 1 = bf16 output.
+constexpr int kIoRaw = 1, kIoBf16 = 2;
+
 // ----------------------------------------------------------------------------
 // Kernels
 // ----------------------------------------------------------------------------
 
 // Single-token step, in place. Inputs go straight to registers: a lane's key
 // channels are fixed, so it loads exactly the k, q, alpha it uses.
-template <int DK, int C, bool GATE>
+template <int DK, int C, bool GATE, int IO>
 __global__ __launch_bounds__(GATE ? 1024 : 256) void decode_kernel(Args a) {
   constexpr int NV = DK / 64;
+  constexpr bool RAW = IO & kIoRaw, BF16 = IO & kIoBf16;
   const Unit u = unit_of_block(a.ntile, a.H);
   const int32_t slot = a.slot_ids[u.b];
   if (slot < 0) return;
@@ -364,7 +475,13 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void decode_kernel(Args a) {
   float vj[C];
 #pragma unroll
   for (int c = 0; c < C; ++c) vj[c] = bf16_to_f32(a.v[vbase + L.col0 + c * L.slab]);
-  const float beta = a.beta[th];
+  float beta = a.beta[th];
+  if constexpr (RAW) {
+    prep_normalize<NV>(kk, 1.0f);
+    prep_normalize<NV>(qq, 1.0f / __builtin_sqrtf((float)DK));
+    prep_decay<NV>(aa);
+    beta = prep_beta(beta);
+  }
   float gj = 0.0f, wj = 1.0f;
   if constexpr (GATE) {
     const int j = L.col0 + (L.r < C ? L.r : 0) * L.slab;
@@ -384,10 +501,10 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void decode_kernel(Args a) {
     __syncthreads();
     if (L.r < C) {
       const int j = L.col0 + L.r * L.slab;
-      a.out[vbase + j] = gate_apply(a, part, raw[j], gj, wj);
+      put_out(a, BF16, vbase + j, gate_apply(a, part, raw[j], gj, wj));
     }
   } else {
-    store_cols<C>(a.out + vbase, L, o);
+    store_out<C>(a, BF16, vbase, L, o);
   }
 }
 
@@ -415,9 +532,10 @@ inline size_t staged_bytes(int dk, int T_max, int W, bool gate) {
 // Speculative verify over a packed chunk: T_b tokens with the state in
 // registers; outputs per token; the committed slot stays untouched unless the
 // row is a single in-place token.
-template <int DK, int C, bool GATE>
+template <int DK, int C, bool GATE, int IO>
 __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
   constexpr int NV = DK / 64;
+  constexpr bool RAW = IO & kIoRaw, BF16 = IO & kIoBf16;
   extern __shared__ float4 lds_dyn[];
   const Unit u = unit_of_block(a.ntile, a.H);
   const int32_t slot = a.slot_ids[u.b];
@@ -469,6 +587,10 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
     if (replay && u.tile == 0) a.rbeta[((int64_t)u.b * a.T_max + threadIdx.x) * a.H + u.h] = bt;
   }
   __syncthreads();
+  if constexpr (RAW) {
+    prep_staged<DK>(st.k, st.q, st.a, st.beta, Tb);
+    __syncthreads();
+  }
 
   float *S = a.cache + (int64_t)slot * a.slot_stride + ((int64_t)u.h * a.dv + (int64_t)u.tile * W) * DK;
   float4 s[C][NV];
@@ -497,7 +619,7 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
       store_cols<C>(raw + t * kMaxDv, L, o);
       gate_partial<C>(o, part + t * kMaxWaves);
     } else {
-      store_cols<C>(a.out + obase, L, o);
+      store_out<C>(a, BF16, obase, L, o);
     }
     if (perpos) {
       float *D = a.draft + ((((int64_t)u.b * a.T_max + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W) * DK;
@@ -513,7 +635,7 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
       const float wj = a.weight ? a.weight[j] : 1.0f;
       for (int t = 0; t < Tb; ++t) {
         const int64_t obase = ((row0 + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W;
-        a.out[obase + j] = gate_apply(a, part + t * kMaxWaves, raw[t * kMaxDv + j], st.g[t * W + j], wj);
+        put_out(a, BF16, obase + j, gate_apply(a, part + t * kMaxWaves, raw[t * kMaxDv + j], st.g[t * W + j], wj));
       }
     }
   }
@@ -643,7 +765,7 @@ __device__ __forceinline__ void prefill_token_step(const Args &a, float4 (&s)[C]
                                                    int W, const Lane &L) {
   float o[C];
   token_fused<DK / 64, C>(s, x.a, x.k, x.q, x.v, x.beta, x.kq, o);
-  store_cols<C>(a.out + (row * a.H + u.h) * a.dv + (int64_t)u.tile * W, L, o);
+  store_out<C>(a, a.out_bf16 != 0, (row * a.H + u.h) * a.dv + (int64_t)u.tile * W, L, o);
 }
 
 template <int DK, int C>
@@ -695,8 +817,36 @@ __global__ __launch_bounds__(256) void prefill_kernel(Args a) {
       prefill_fetch<DK, W>(a, c0 + t0 + kPrefillChunk, min(kPrefillChunk, Tb - t0 - kPrefillChunk), u.h, u.tile,
                            regs);
     // k . q per token, once per workgroup: thread (t, chunk of DK / 16 channels), a
-    // 16-lane row per token
-    {
+    // 16-lane row per token. Raw inputs are prepared in the same pass (one row per
+    // token, the column engine's channel layout) and k . q taken on the prepared values.
+    if (a.raw) {
+      const int t = threadIdx.x >> 4, r = threadIdx.x & 15;
+      if (t < n) {
+        float4 kk[NV], qq[NV], aa[NV];
+#pragma unroll
+        for (int e = 0; e < NV; ++e) {
+          const int i = t * DK + 4 * r + 64 * e;
+          kk[e] = *reinterpret_cast<const float4 *>(B.k + i);
+          qq[e] = *reinterpret_cast<const float4 *>(B.q + i);
+          aa[e] = *reinterpret_cast<const float4 *>(B.a + i);
+        }
+        prep_normalize<NV>(kk, 1.0f);
+        prep_normalize<NV>(qq, 1.0f / __builtin_sqrtf((float)DK));
+        prep_decay<NV>(aa);
+        const float kq = row16_sum(lane_dot<NV>(kk, qq));
+#pragma unroll
+        for (int e = 0; e < NV; ++e) {
+          const int i = t * DK + 4 * r + 64 * e;
+          *reinterpret_cast<float4 *>(B.k + i) = kk[e];
+          *reinterpret_cast<float4 *>(B.q + i) = qq[e];
+          *reinterpret_cast<float4 *>(B.a + i) = aa[e];
+        }
+        if (r == 0) {
+          B.kq[t] = kq;
+          B.beta[t] = prep_beta(B.beta[t]);
+        }
+      }
+    } else {
       constexpr int CPT = DK / 16;
       const int t = threadIdx.x >> 4, c = threadIdx.x & 15;
       float p = 0.0f;
@@ -976,6 +1126,10 @@ __global__ __launch_bounds__(256) void commit_replay_kernel(Args a) {
   }
   if ((int)threadIdx.x < n) st.beta[threadIdx.x] = a.rbeta[((int64_t)u.b * a.T_max + threadIdx.x) * a.H + u.h];
   __syncthreads();
+  if (a.raw) {
+    prep_staged<DK>(st.k, nullptr, st.a, st.beta, n);
+    __syncthreads();
+  }
 
   float *S = a.cache + (int64_t)slot * a.slot_stride + ((int64_t)u.h * a.dv + (int64_t)u.tile * W) * DK;
   float4 s[C][NV];
@@ -1064,18 +1218,40 @@ enum Kind { KIND_DECODE, KIND_VERIFY, KIND_COMMIT_REPLAY, KIND_COMMIT_COPY, KIND
 
 // Gated launches use a fixed number of slabs per lane for each op (see
 // choose_width); only those are instantiated with the gate.
+// The four input/output variants of one decode or verify kernel.
+template <int DK, int C, bool GATE>
+struct decode_table {
+  template <int IO>
+  static const void *get() { return (const void *)decode_kernel<DK, C, GATE, IO>; }
+};
+template <int DK, int C, bool GATE>
+struct verify_table {
+  template <int IO>
+  static const void *get() { return (const void *)verify_kernel<DK, C, GATE, IO>; }
+};
+template <class T>
+const void *io_variant(int io) {
+  switch (io) {
+    case 0: return T::template get<0>();
+    case kIoRaw: return T::template get<kIoRaw>();
+    case kIoBf16: return T::template get<kIoBf16>();
+    case kIoRaw | kIoBf16: return T::template get<kIoRaw | kIoBf16>();
+  }
+  return nullptr;
+}
+
 template <int DK, int C>
-const void *kernel_for(Kind kind, bool gate) {
+const void *kernel_for(Kind kind, bool gate, int io) {
   if constexpr (C == kGateSlabsDecode)
-    if (gate && kind == KIND_DECODE) return (const void *)decode_kernel<DK, C, true>;
+    if (gate && kind == KIND_DECODE) return io_variant<decode_table<DK, C, true>>(io);
   if constexpr (C == kGateSlabsVerify)
-    if (gate && kind == KIND_VERIFY) return (const void *)verify_kernel<DK, C, true>;
+    if (gate && kind == KIND_VERIFY) return io_variant<verify_table<DK, C, true>>(io);
   if (gate) return nullptr;
   switch (kind) {
     case KIND_DECODE:
-      return (const void *)decode_kernel<DK, C, false>;
+      return io_variant<decode_table<DK, C, false>>(io);
     case KIND_VERIFY:
-      return (const void *)verify_kernel<DK, C, false>;
+      return io_variant<verify_table<DK, C, false>>(io);
     case KIND_COMMIT_REPLAY:
       return (const void *)commit_replay_kernel<DK, C>;
     case KIND_COMMIT_COPY:
@@ -1087,12 +1263,12 @@ const void *kernel_for(Kind kind, bool gate) {
 }
 
 template <int DK>
-const void *kernel_for_c(Kind kind, bool gate, int C) {
+const void *kernel_for_c(Kind kind, bool gate, int io, int C) {
   switch (C) {
-    case 1: return kernel_for<DK, 1>(kind, gate);
-    case 2: return kernel_for<DK, 2>(kind, gate);
-    case 4: return kernel_for<DK, 4>(kind, gate);
-    case 8: return kernel_for<DK, 8>(kind, gate);
+    case 1: return kernel_for<DK, 1>(kind, gate, io);
+    case 2: return kernel_for<DK, 2>(kind, gate, io);
+    case 4: return kernel_for<DK, 4>(kind, gate, io);
+    case 8: return kernel_for<DK, 8>(kind, gate, io);
   }
   return nullptr;
 }
@@ -1188,7 +1364,8 @@ int launch_fn(const void *fn, int64_t blocks, int threads, size_t shmem, Args &a
 int launch(Kind kind, bool gate, int dk, const Launch &l, int64_t units, size_t shmem, Args &a,
            void *stream) {
   if (units > 0x7fffffff) return KDA_ERR_UNSUPPORTED;
-  const void *fn = dk == 64 ? kernel_for_c<64>(kind, gate, l.C) : kernel_for_c<128>(kind, gate, l.C);
+  const int io = (a.raw ? kIoRaw : 0) | (a.out_bf16 ? kIoBf16 : 0);
+  const void *fn = dk == 64 ? kernel_for_c<64>(kind, gate, io, l.C) : kernel_for_c<128>(kind, gate, io, l.C);
   return launch_fn(fn, units, 64 * l.waves, shmem, a, stream);
 }
 
@@ -1200,11 +1377,21 @@ int check_cache(const float *cache, int64_t num_slots, int64_t slot_stride, int 
 }
 
 int check_inputs(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *alpha,
-                 const float *beta, float *out, bool need_q) {
+                 const float *beta, const void *out, bool need_q, bool out_bf16) {
   if ((need_q && !q) || !k || !v || !alpha || !beta || (need_q && !out)) return KDA_ERR_INVALID;
   if ((q && !aligned(q, 8)) || !aligned(k, 8) || !aligned(v, 8) || !aligned(alpha, 16) ||
-      !aligned(beta, 4) || (out && !aligned(out, 4)))
+      !aligned(beta, 4) || (out && !aligned(out, out_bf16 ? 2 : 4)))
     return KDA_ERR_ALIGN;
+  return KDA_OK;
+}
+
+// The option flags of a call: unknown bits are an error; `used` are the ones the
+// op acts on (the others it accepts and ignores).
+int read_flags(const kda_options *opts, int32_t used, Args &a) {
+  const int32_t f = opts ? opts->flags : 0;
+  if (f & ~(int32_t)(KDA_RAW_INPUTS | KDA_OUT_BF16)) return KDA_ERR_INVALID;
+  a.raw = (f & used & KDA_RAW_INPUTS) ? 1 : 0;
+  a.out_bf16 = (f & used & KDA_OUT_BF16) ? 1 : 0;
   return KDA_OK;
 }
 
@@ -1235,14 +1422,17 @@ extern "C" {
 int kda_prefill(float *cache, int64_t num_slots, int64_t slot_stride, const int32_t *slot_ids,
                 const int32_t *cu_seqlens, int32_t B, int32_t n_tok, int32_t H, int32_t dk, int32_t dv,
                 const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *alpha,
-                const float *beta, float *out, const int32_t *ckpt_pos, float *ckpt, int32_t *dev_err,
+                const float *beta, void *out, const int32_t *ckpt_pos, float *ckpt, int32_t *dev_err,
                 const kda_options *opts, void *stream) {
+  Args a;
+  memset(&a, 0, sizeof a);
   if (B < 0 || H <= 0 || dk <= 0 || dv <= 0 || n_tok < 0) return KDA_ERR_INVALID;
+  KDA_TRY(read_flags(opts, KDA_RAW_INPUTS | KDA_OUT_BF16, a));
   if (!dims_supported(dk, dv)) return KDA_ERR_UNSUPPORTED;
   if (B == 0 || (n_tok == 0 && !ckpt_pos)) return KDA_OK;
   if (!slot_ids || !cu_seqlens) return KDA_ERR_INVALID;
   KDA_TRY(check_cache(cache, num_slots, slot_stride, H, dk, dv));
-  if (n_tok > 0) KDA_TRY(check_inputs(q, k, v, alpha, beta, out, true));
+  if (n_tok > 0) KDA_TRY(check_inputs(q, k, v, alpha, beta, out, true, a.out_bf16));
   if (ckpt_pos) {
     if (!ckpt) return KDA_ERR_INVALID;
     if (!aligned(ckpt, 16) || !aligned(ckpt_pos, 4)) return KDA_ERR_ALIGN;
@@ -1251,8 +1441,6 @@ int kda_prefill(float *cache, int64_t num_slots, int64_t slot_stride, const int3
   Launch l;
   KDA_TRY(choose_width(KIND_PREFILL, B, H, dv, false, opts ? opts->tile_w : 0, &l));
 
-  Args a;
-  memset(&a, 0, sizeof a);
   a.cache = cache;
   a.num_slots = num_slots;
   a.slot_stride = slot_stride;
@@ -1263,7 +1451,7 @@ int kda_prefill(float *cache, int64_t num_slots, int64_t slot_stride, const int3
   a.v = v;
   a.alpha = alpha;
   a.beta = beta;
-  a.out = out;
+  a.out = static_cast<float *>(out);
   a.ckpt_pos = ckpt_pos;
   a.ckpt = ckpt;
   a.dev_err = dev_err;
@@ -1283,21 +1471,22 @@ int kda_prefill(float *cache, int64_t num_slots, int64_t slot_stride, const int3
 int kda_decode_step(float *cache, int64_t num_slots, int64_t slot_stride, const int32_t *slot_ids,
                     int32_t B, int32_t H, int32_t dk, int32_t dv, const uint16_t *q,
                     const uint16_t *k, const uint16_t *v, const float *alpha, const float *beta,
-                    float *out, const kda_epilogue *epi, int32_t *dev_err,
+                    void *out, const kda_epilogue *epi, int32_t *dev_err,
                     const kda_options *opts, void *stream) {
+  Args a;
+  memset(&a, 0, sizeof a);
   if (B < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID;
+  KDA_TRY(read_flags(opts, KDA_RAW_INPUTS | KDA_OUT_BF16, a));
   if (!dims_supported(dk, dv)) return KDA_ERR_UNSUPPORTED;
   if (B == 0) return KDA_OK;
   if (!slot_ids) return KDA_ERR_INVALID;
   KDA_TRY(check_cache(cache, num_slots, slot_stride, H, dk, dv));
-  KDA_TRY(check_inputs(q, k, v, alpha, beta, out, true));
+  KDA_TRY(check_inputs(q, k, v, alpha, beta, out, true, a.out_bf16));
   KDA_TRY(check_gate(epi));
   if (dev_err && !aligned(dev_err, 4)) return KDA_ERR_ALIGN;
   Launch l;
   KDA_TRY(choose_width(KIND_DECODE, B, H, dv, epi != nullptr, opts ? opts->tile_w : 0, &l));
 
-  Args a;
-  memset(&a, 0, sizeof a);
   a.cache = cache;
   a.num_slots = num_slots;
   a.slot_stride = slot_stride;
@@ -1307,7 +1496,7 @@ int kda_decode_step(float *cache, int64_t num_slots, int64_t slot_stride, const 
   a.v = v;
   a.alpha = alpha;
   a.beta = beta;
-  a.out = out;
+  a.out = static_cast<float *>(out);
   a.gate = epi ? epi->gate : nullptr;
   a.weight = epi ? epi->weight : nullptr;
   a.eps = epi ? epi->eps : 0.0f;
@@ -1326,16 +1515,19 @@ int kda_decode_step(float *cache, int64_t num_slots, int64_t slot_stride, const 
 int kda_verify_chunk(float *cache, int64_t num_slots, int64_t slot_stride, const int32_t *slot_ids,
                      const int32_t *cu_seqlens, int32_t B, int32_t T_max, int32_t n_tok, int32_t H,
                      int32_t dk, int32_t dv, const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                     const float *alpha, const float *beta, float *out, const kda_epilogue *epi,
+                     const float *alpha, const float *beta, void *out, const kda_epilogue *epi,
                      int32_t mode, int32_t t1_inplace, const kda_replay_buf *rb, float *draft,
                      int32_t *dev_err, const kda_options *opts, void *stream) {
+  Args a;
+  memset(&a, 0, sizeof a);
   if (B < 0 || H <= 0 || dk <= 0 || dv <= 0 || n_tok < 0) return KDA_ERR_INVALID;
   if (mode != KDA_REPLAY && mode != KDA_PER_POSITION) return KDA_ERR_INVALID;
+  KDA_TRY(read_flags(opts, KDA_RAW_INPUTS | KDA_OUT_BF16, a));
   if (!dims_supported(dk, dv) || T_max < 1 || T_max > kMaxT) return KDA_ERR_UNSUPPORTED;
   if (B == 0 || n_tok == 0) return KDA_OK;  // no tokens: nothing to read or write
   if (!slot_ids || !cu_seqlens) return KDA_ERR_INVALID;
   KDA_TRY(check_cache(cache, num_slots, slot_stride, H, dk, dv));
-  KDA_TRY(check_inputs(q, k, v, alpha, beta, out, true));
+  KDA_TRY(check_inputs(q, k, v, alpha, beta, out, true, a.out_bf16));
   KDA_TRY(check_gate(epi));
   if (mode == KDA_REPLAY) KDA_TRY(check_replay_buf(rb));
   if (mode == KDA_PER_POSITION) {
@@ -1346,7 +1538,8 @@ int kda_verify_chunk(float *cache, int64_t num_slots, int64_t slot_stride, const
   const int form = opts ? opts->verify_form : KDA_VERIFY_AUTO;
   if (form != KDA_VERIFY_AUTO && form != KDA_VERIFY_RECURRENT && form != KDA_VERIFY_CHUNKED)
     return KDA_ERR_INVALID;
-  const bool chunk_fits = mode == KDA_REPLAY && !t1_inplace && epi == nullptr && dv % kChunkW == 0;
+  const bool chunk_fits = mode == KDA_REPLAY && !t1_inplace && epi == nullptr && dv % kChunkW == 0 &&
+                          !a.raw && !a.out_bf16;
   if (form == KDA_VERIFY_CHUNKED && (!chunk_fits || (opts && opts->tile_w != 0))) return KDA_ERR_UNSUPPORTED;
   // Measured on MI355X (B=16, H=32, d=128, 8 drafts): the chunk form takes ~31 us against
   // ~19 us token by token, so the automatic choice is the recurrent kernel.
@@ -1358,8 +1551,6 @@ int kda_verify_chunk(float *cache, int64_t num_slots, int64_t slot_stride, const
     KDA_TRY(choose_width(KIND_VERIFY, B, H, dv, epi != nullptr, opts ? opts->tile_w : 0, &l));
   }
 
-  Args a;
-  memset(&a, 0, sizeof a);
   a.cache = cache;
   a.num_slots = num_slots;
   a.slot_stride = slot_stride;
@@ -1370,7 +1561,7 @@ int kda_verify_chunk(float *cache, int64_t num_slots, int64_t slot_stride, const
   a.v = v;
   a.alpha = alpha;
   a.beta = beta;
-  a.out = out;
+  a.out = static_cast<float *>(out);
   a.gate = epi ? epi->gate : nullptr;
   a.weight = epi ? epi->weight : nullptr;
   a.eps = epi ? epi->eps : 0.0f;
@@ -1406,8 +1597,11 @@ int kda_replay_commit(float *cache, int64_t num_slots, int64_t slot_stride, cons
                       int32_t T_max, int32_t n_tok, int32_t H, int32_t dk, int32_t dv, int32_t mode,
                       const kda_replay_buf *rb, const float *draft, int32_t *dev_err,
                       const kda_options *opts, void *stream) {
+  Args a;
+  memset(&a, 0, sizeof a);
   if (B < 0 || H <= 0 || dk <= 0 || dv <= 0 || n_tok < 0) return KDA_ERR_INVALID;
   if (mode != KDA_REPLAY && mode != KDA_PER_POSITION) return KDA_ERR_INVALID;
+  KDA_TRY(read_flags(opts, mode == KDA_REPLAY ? KDA_RAW_INPUTS : 0, a));
   if (!dims_supported(dk, dv) || T_max < 1 || T_max > kMaxT) return KDA_ERR_UNSUPPORTED;
   if (B == 0) return KDA_OK;
   if (!slot_ids || !accepted_len) return KDA_ERR_INVALID;
@@ -1424,8 +1618,6 @@ int kda_replay_commit(float *cache, int64_t num_slots, int64_t slot_stride, cons
   KDA_TRY(choose_width(mode == KDA_REPLAY ? KIND_COMMIT_REPLAY : KIND_COMMIT_COPY, B, H, dv, false,
                        opts ? opts->tile_w : 0, &l));
 
-  Args a;
-  memset(&a, 0, sizeof a);
   a.cache = cache;
   a.num_slots = num_slots;
   a.slot_stride = slot_stride;

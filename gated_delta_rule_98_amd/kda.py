@@ -42,6 +42,9 @@ KDA_DEVERR_SEQLEN = 2
 KDA_DEVERR_ACCEPTED = 4
 KDA_DEVERR_CKPT = 8
 
+KDA_RAW_INPUTS = 1
+KDA_OUT_BF16 = 2
+
 
 class KdaError(RuntimeError):
     def __init__(self, status: int, where: str):
@@ -59,7 +62,7 @@ class kda_replay_buf(ctypes.Structure):
 
 
 class kda_options(ctypes.Structure):
-    _fields_ = [("tile_w", ctypes.c_int32), ("verify_form", ctypes.c_int32)]
+    _fields_ = [("tile_w", ctypes.c_int32), ("verify_form", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 _lib = None
@@ -179,8 +182,18 @@ def _epilogue(gate, weight, eps):
     return kda_epilogue(gate.data_ptr(), _ptr(weight), float(eps))
 
 
-def _opts(tile_w: int, verify_form: int = 0):
-    return kda_options(int(tile_w), int(verify_form)) if (tile_w or verify_form) else None
+def _opts(tile_w: int, verify_form: int = 0, flags: int = 0):
+    if not (tile_w or verify_form or flags):
+        return None
+    return kda_options(int(tile_w), int(verify_form), int(flags))
+
+
+def _flags(raw_inputs: bool, out: Optional[torch.Tensor] = None) -> int:
+    """Option flags: raw inputs on request, bf16 output when out holds bf16."""
+    f = KDA_RAW_INPUTS if raw_inputs else 0
+    if out is not None and out.dtype in _BF16_TYPES:
+        f |= KDA_OUT_BF16
+    return f
 
 
 def _ref(x):
@@ -189,19 +202,21 @@ def _ref(x):
 
 def kda_decode_step(cache: torch.Tensor, slot_ids: torch.Tensor, q, k, v, alpha, beta,
                     out: torch.Tensor, *, gate=None, weight=None, eps: float = 1e-6,
-                    dev_err: Optional[torch.Tensor] = None, tile_w: int = 0, stream=None) -> None:
+                    dev_err: Optional[torch.Tensor] = None, tile_w: int = 0, raw_inputs: bool = False,
+                    stream=None) -> None:
     """One token per row, state updated in place.
 
     cache float32 [num_slots, H, dv, dk]; slot_ids int32 [B]; q, k bf16 [B, H, dk];
-    v bf16 [B, H, dv]; alpha float32 [B, H, dk]; beta float32 [B, H]; out float32
-    [B, H, dv]; gate bf16 [B, H, dv] (optional output gate), weight float32 [dv].
+    v bf16 [B, H, dv]; alpha float32 [B, H, dk]; beta float32 [B, H]; out float32 or
+    bf16 [B, H, dv]; gate bf16 [B, H, dv] (optional output gate), weight float32 [dv].
+    raw_inputs: q, k, alpha, beta are raw projections, prepared in the kernel.
     """
     ns, stride, H, dv, dk = _cache(cache)
     _dev(slot_ids, "slot_ids", (torch.int32,), 1)
     B = slot_ids.shape[0]
     for name, t, d in (("q", q, _BF16_TYPES), ("k", k, _BF16_TYPES), ("v", v, _BF16_TYPES),
                        ("alpha", alpha, (torch.float32,)), ("beta", beta, (torch.float32,)),
-                       ("out", out, (torch.float32,))):
+                       ("out", out, (torch.float32,) + _BF16_TYPES)):
         _dev(t, name, d)
     for name, t, shape in (("q", q, (B, H, dk)), ("k", k, (B, H, dk)), ("v", v, (B, H, dv)),
                            ("alpha", alpha, (B, H, dk)), ("beta", beta, (B, H)), ("out", out, (B, H, dv)),
@@ -213,7 +228,7 @@ def kda_decode_step(cache: torch.Tensor, slot_ids: torch.Tensor, q, k, v, alpha,
     rc = load_library().kda_decode_step(
         cache.data_ptr(), ns, stride, slot_ids.data_ptr(), B, H, dk, dv,
         q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(), beta.data_ptr(), out.data_ptr(),
-        _ref(epi), _ptr(dev_err), _ref(_opts(tile_w)), _stream(stream))
+        _ref(epi), _ptr(dev_err), _ref(_opts(tile_w, 0, _flags(raw_inputs, out))), _stream(stream))
     if rc != KDA_OK:
         raise KdaError(rc, "kda_decode_step")
 
@@ -223,10 +238,12 @@ def kda_verify_chunk(cache: torch.Tensor, slot_ids: torch.Tensor, cu_seqlens: to
                      t1_inplace: bool = False, replay: Optional[dict] = None,
                      draft: Optional[torch.Tensor] = None, gate=None, weight=None, eps: float = 1e-6,
                      dev_err: Optional[torch.Tensor] = None, tile_w: int = 0, verify_form: int = 0,
-                     stream=None) -> None:
+                     raw_inputs: bool = False, stream=None) -> None:
     """Packed speculative chunk; token arrays are [n_tok, H, .], row b owns tokens
     [cu[b], cu[b+1]). replay = dict(k, v, alpha, beta) with shapes [B, T_max, H, .]
-    (mode KDA_REPLAY); draft float32 [B, T_max, H, dv, dk] (mode KDA_PER_POSITION)."""
+    (mode KDA_REPLAY); draft float32 [B, T_max, H, dv, dk] (mode KDA_PER_POSITION).
+    out is float32 or bf16; raw_inputs as for kda_decode_step (the replay buffer then
+    holds the raw inputs and the commit needs raw_inputs too)."""
     ns, stride, H, dv, dk = _cache(cache)
     _dev(slot_ids, "slot_ids", (torch.int32,), 1)
     _dev(cu_seqlens, "cu_seqlens", (torch.int32,), 1)
@@ -235,7 +252,7 @@ def kda_verify_chunk(cache: torch.Tensor, slot_ids: torch.Tensor, cu_seqlens: to
         raise ValueError("cu_seqlens must have B + 1 entries")
     for name, t, d in (("q", q, _BF16_TYPES), ("k", k, _BF16_TYPES), ("v", v, _BF16_TYPES),
                        ("alpha", alpha, (torch.float32,)), ("beta", beta, (torch.float32,)),
-                       ("out", out, (torch.float32,))):
+                       ("out", out, (torch.float32,) + _BF16_TYPES)):
         _dev(t, name, d)
     n_tok = k.shape[0]
     for name, t, shape in (("q", q, (n_tok, H, dk)), ("k", k, (n_tok, H, dk)), ("v", v, (n_tok, H, dv)),
@@ -253,7 +270,7 @@ def kda_verify_chunk(cache: torch.Tensor, slot_ids: torch.Tensor, cu_seqlens: to
         cache.data_ptr(), ns, stride, slot_ids.data_ptr(), cu_seqlens.data_ptr(), B, int(T_max),
         n_tok, H, dk, dv, q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(), beta.data_ptr(),
         out.data_ptr(), _ref(epi), int(mode), int(bool(t1_inplace)), _ref(rb), _ptr(draft),
-        _ptr(dev_err), _ref(_opts(tile_w, verify_form)), _stream(stream))
+        _ptr(dev_err), _ref(_opts(tile_w, verify_form, _flags(raw_inputs, out))), _stream(stream))
     if rc != KDA_OK:
         raise KdaError(rc, "kda_verify_chunk")
 
@@ -261,8 +278,10 @@ def kda_verify_chunk(cache: torch.Tensor, slot_ids: torch.Tensor, cu_seqlens: to
 def kda_replay_commit(cache: torch.Tensor, slot_ids: torch.Tensor, cu_seqlens: Optional[torch.Tensor],
                       accepted_len: torch.Tensor, T_max: int, n_tok: int, *, mode: int = KDA_REPLAY,
                       replay: Optional[dict] = None, draft: Optional[torch.Tensor] = None,
-                      dev_err: Optional[torch.Tensor] = None, tile_w: int = 0, stream=None) -> None:
-    """Slot of row b <- state after the first accepted_len[b] tokens of its verified chunk."""
+                      dev_err: Optional[torch.Tensor] = None, tile_w: int = 0, raw_inputs: bool = False,
+                      stream=None) -> None:
+    """Slot of row b <- state after the first accepted_len[b] tokens of its verified chunk.
+    raw_inputs must match the verify call that filled the replay buffer (mode KDA_REPLAY)."""
     ns, stride, H, dv, dk = _cache(cache)
     _dev(slot_ids, "slot_ids", (torch.int32,), 1)
     _dev(accepted_len, "accepted_len", (torch.int32,), 1)
@@ -279,16 +298,18 @@ def kda_replay_commit(cache: torch.Tensor, slot_ids: torch.Tensor, cu_seqlens: O
     rc = load_library().kda_replay_commit(
         cache.data_ptr(), ns, stride, slot_ids.data_ptr(), _ptr(cu_seqlens), accepted_len.data_ptr(),
         B, int(T_max), int(n_tok), H, dk, dv, int(mode), _ref(rb), _ptr(draft), _ptr(dev_err),
-        _ref(_opts(tile_w)), _stream(stream))
+        _ref(_opts(tile_w, 0, _flags(raw_inputs))), _stream(stream))
     if rc != KDA_OK:
         raise KdaError(rc, "kda_replay_commit")
 
 
 def kda_prefill(cache: torch.Tensor, slot_ids: torch.Tensor, cu_seqlens: torch.Tensor, q, k, v, alpha, beta,
                 out: torch.Tensor, *, ckpt_pos: Optional[torch.Tensor] = None, ckpt: Optional[torch.Tensor] = None,
-                dev_err: Optional[torch.Tensor] = None, tile_w: int = 0, stream=None) -> None:
+                dev_err: Optional[torch.Tensor] = None, tile_w: int = 0, raw_inputs: bool = False,
+                stream=None) -> None:
     """Whole prompts in one pass with an in-pass checkpoint. Token arrays are [n_tok, H, .];
-    row b owns tokens [cu[b], cu[b+1]); ckpt_pos int32 [B], ckpt float32 [B, H, dv, dk]."""
+    row b owns tokens [cu[b], cu[b+1]); ckpt_pos int32 [B], ckpt float32 [B, H, dv, dk].
+    out is float32 or bf16; raw_inputs as for kda_decode_step."""
     ns, stride, H, dv, dk = _cache(cache)
     _dev(slot_ids, "slot_ids", (torch.int32,), 1)
     _dev(cu_seqlens, "cu_seqlens", (torch.int32,), 1)
@@ -296,7 +317,7 @@ def kda_prefill(cache: torch.Tensor, slot_ids: torch.Tensor, cu_seqlens: torch.T
     _shape(cu_seqlens, "cu_seqlens", (B + 1,))
     for name, t, d in (("q", q, _BF16_TYPES), ("k", k, _BF16_TYPES), ("v", v, _BF16_TYPES),
                        ("alpha", alpha, (torch.float32,)), ("beta", beta, (torch.float32,)),
-                       ("out", out, (torch.float32,))):
+                       ("out", out, (torch.float32,) + _BF16_TYPES)):
         _dev(t, name, d)
     n_tok = k.shape[0]
     for name, t, shape in (("q", q, (n_tok, H, dk)), ("k", k, (n_tok, H, dk)), ("v", v, (n_tok, H, dv)),
@@ -316,7 +337,8 @@ def kda_prefill(cache: torch.Tensor, slot_ids: torch.Tensor, cu_seqlens: torch.T
     rc = load_library().kda_prefill(
         cache.data_ptr(), ns, stride, slot_ids.data_ptr(), cu_seqlens.data_ptr(), B, n_tok, H, dk, dv,
         q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(), beta.data_ptr(), out.data_ptr(),
-        _ptr(ckpt_pos), _ptr(ckpt), _ptr(dev_err), _ref(_opts(tile_w)), _stream(stream))
+        _ptr(ckpt_pos), _ptr(ckpt), _ptr(dev_err), _ref(_opts(tile_w, 0, _flags(raw_inputs, out))),
+        _stream(stream))
     if rc != KDA_OK:
         raise KdaError(rc, "kda_prefill")
 

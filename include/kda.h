@@ -28,7 +28,7 @@
  *   v       bf16   [rows][H][dv]
  *   alpha   float  [rows][H][dk]   decay per key channel
  *   beta    float  [rows][H]       write strength per head
- *   out     float  [rows][H][dv]
+ *   out     float  [rows][H][dv]  (bf16 with KDA_OUT_BF16)
  * where rows is B for kda_decode_step and n_tok for kda_verify_chunk.
  *
  * Supported shapes: dk, dv in {64, 128}; 1 <= T_max <= 16.
@@ -69,12 +69,13 @@ extern "C" {
 
 enum kda_status {
     KDA_OK = 0,
-    KDA_ERR_INVALID = -1,     /* null required pointer, negative size, bad mode, slot_stride too small */
+    KDA_ERR_INVALID = -1,     /* null required pointer, negative size, bad mode, unknown option flag,
+                                 slot_stride too small */
     KDA_ERR_UNSUPPORTED = -2, /* dk or dv not in {64, 128}, T_max outside [1, 16], illegal tile width,
                                  grid too large */
     KDA_ERR_ALIGN = -3,       /* cache / alpha / draft / replay alpha not 16-byte aligned, slot_stride
-                                 not a multiple of 4, bf16 arrays not 8-byte aligned, out / beta not
-                                 4-byte aligned */
+                                 not a multiple of 4, bf16 input arrays not 8-byte aligned, out / beta
+                                 not 4-byte aligned (bf16 out: 2-byte) */
     KDA_ERR_HIP = -4          /* the HIP runtime rejected a launch */
 };
 
@@ -131,6 +132,27 @@ typedef struct kda_replay_buf {
  *     the MFMA products save at up to 16 tokens). */
 enum kda_verify_form { KDA_VERIFY_AUTO = 0, KDA_VERIFY_RECURRENT = 1, KDA_VERIFY_CHUNKED = 2 };
 
+/* Option flags (kda_options.flags, OR-ed).
+ *   KDA_RAW_INPUTS: q, k, alpha and beta hold the raw projections (same types and
+ *     layouts) and every token is prepared in the kernel before the recurrence, the
+ *     normalization and gate activations that otherwise run as separate small
+ *     kernels ("Hyper Optimizing Kimi K3 in vLLM", section "Finding time between
+ *     operators"):
+ *         k <- k / sqrt(sum_i k_i^2 + 1e-12)
+ *         q <- q / sqrt(sum_i q_i^2 + 1e-12) / sqrt(dk)
+ *         alpha_i <- exp(-softplus(alpha_i)) = 1 / (1 + exp(alpha_i))
+ *         beta <- sigmoid(beta) = 1 / (1 + exp(-beta))
+ *     in fp32 with the hardware exp2, reciprocal and reciprocal square root. Every
+ *     op prepares the same way, so states stay bit-identical across decode,
+ *     verify, commit and prefill. Replay buffers hold the raw inputs, and
+ *     kda_replay_commit in KDA_REPLAY mode must get the flag when the verify did.
+ *   KDA_OUT_BF16: out is bf16 [rows][H][dv] (2-byte aligned), each output rounded
+ *     to nearest even from the fp32 value the call computes otherwise.
+ * kda_replay_commit ignores KDA_OUT_BF16 (it has no output) and, in
+ * KDA_PER_POSITION mode, KDA_RAW_INPUTS. The chunk form of verify takes neither
+ * (KDA_ERR_UNSUPPORTED). Other bits are KDA_ERR_INVALID. */
+enum kda_flag { KDA_RAW_INPUTS = 1, KDA_OUT_BF16 = 2 };
+
 /* Launch options (host struct, may be NULL = all zero). */
 typedef struct kda_options {
     int32_t tile_w;      /* value columns per workgroup of the recurrent kernels: 0 = chosen from
@@ -139,6 +161,7 @@ typedef struct kda_options {
                             width. */
     int32_t verify_form; /* a kda_verify_form; KDA_VERIFY_CHUNKED where it does not apply is
                             KDA_ERR_UNSUPPORTED */
+    int32_t flags;       /* kda_flag bits */
 } kda_options;
 
 /*
@@ -149,7 +172,7 @@ typedef struct kda_options {
 int kda_decode_step(float *cache, int64_t num_slots, int64_t slot_stride,
                     const int32_t *slot_ids, int32_t B, int32_t H, int32_t dk, int32_t dv,
                     const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                    const float *alpha, const float *beta, float *out,
+                    const float *alpha, const float *beta, void *out,
                     const kda_epilogue *epi, int32_t *dev_err,
                     const kda_options *opts, void *stream);
 
@@ -172,7 +195,7 @@ int kda_verify_chunk(float *cache, int64_t num_slots, int64_t slot_stride,
                      const int32_t *slot_ids, const int32_t *cu_seqlens,
                      int32_t B, int32_t T_max, int32_t n_tok, int32_t H, int32_t dk, int32_t dv,
                      const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                     const float *alpha, const float *beta, float *out,
+                     const float *alpha, const float *beta, void *out,
                      const kda_epilogue *epi, int32_t mode, int32_t t1_inplace,
                      const kda_replay_buf *rb, float *draft, int32_t *dev_err,
                      const kda_options *opts, void *stream);
@@ -215,7 +238,7 @@ int kda_prefill(float *cache, int64_t num_slots, int64_t slot_stride,
                 const int32_t *slot_ids, const int32_t *cu_seqlens,
                 int32_t B, int32_t n_tok, int32_t H, int32_t dk, int32_t dv,
                 const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                const float *alpha, const float *beta, float *out,
+                const float *alpha, const float *beta, void *out,
                 const int32_t *ckpt_pos, float *ckpt, int32_t *dev_err,
                 const kda_options *opts, void *stream);
 

@@ -71,3 +71,12 @@ def replay_buffers(B, T_max, H, dk, dv):
                 v=torch.zeros(B, T_max, H, dv, dtype=torch.bfloat16, **z),
                 alpha=torch.zeros(B, T_max, H, dk, dtype=torch.float32, **z),
                 beta=torch.zeros(B, T_max, H, dtype=torch.float32, **z))
+
+
+def raw_step_inputs(w, step: int):
+    """Device tensors of one step's raw projections (q, k, alpha, beta before preparation)."""
+    d = dict(q=bf16(w.q_raw[step]), k=bf16(w.k_raw[step]), v=bf16(w.v[step]),
+             alpha=f32(w.a_raw[step]), beta=f32(w.b_raw[step]))
+    if w.gate is not None:
+        d["gate"] = bf16(w.gate[step])
+    return d

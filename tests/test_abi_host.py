@@ -164,6 +164,13 @@ def test_decode_host_checks():
     assert _decode(opts=ctypes.byref(kda.kda_options(24, 0))) == E.KDA_ERR_UNSUPPORTED
     ok_gate = kda.kda_epilogue(A, None, 1e-6)
     assert _decode(epi=ctypes.byref(ok_gate), opts=ctypes.byref(kda.kda_options(64, 0))) == E.KDA_ERR_UNSUPPORTED
+    # option flags: unknown bits are rejected; a bf16 output needs 2-byte alignment only
+    assert _decode(opts=ctypes.byref(kda.kda_options(0, 0, 4))) == E.KDA_ERR_INVALID
+    assert _decode(out=A + 2) == E.KDA_ERR_ALIGN
+    assert _decode(out=A + 1, opts=ctypes.byref(kda.kda_options(0, 0, E.KDA_OUT_BF16))) == E.KDA_ERR_ALIGN
+    # passes every host check: only the launch itself fails without a device
+    assert _decode(out=A + 2, opts=ctypes.byref(kda.kda_options(0, 0, E.KDA_OUT_BF16))) == E.KDA_ERR_HIP
+    assert _decode(opts=ctypes.byref(kda.kda_options(0, 0, E.KDA_RAW_INPUTS | E.KDA_OUT_BF16))) == E.KDA_ERR_HIP
 
 
 @needs_no_gpu
@@ -184,6 +191,12 @@ def test_verify_host_checks():
     assert _verify(mode=1, draft=A + 4) == E.KDA_ERR_ALIGN
     assert _verify(mode=1, draft=A, cache=A + 8) == E.KDA_ERR_ALIGN
     assert _verify(mode=1, draft=A, dk=64, dv=96) == E.KDA_ERR_UNSUPPORTED
+    # the chunk form takes neither raw inputs nor a bf16 output
+    rb_ok = ctypes.byref(rb)
+    for flags in (E.KDA_RAW_INPUTS, E.KDA_OUT_BF16):
+        opts = ctypes.byref(kda.kda_options(0, E.KDA_VERIFY_CHUNKED, flags))
+        assert _verify(mode=0, rb=rb_ok, opts=opts) == E.KDA_ERR_UNSUPPORTED
+    assert _verify(mode=0, rb=rb_ok, opts=ctypes.byref(kda.kda_options(0, 0, 8))) == E.KDA_ERR_INVALID
 
 
 @needs_no_gpu
@@ -198,6 +211,9 @@ def test_commit_host_checks():
     assert _commit(mode=1, draft=A, acc=A + 2) == E.KDA_ERR_ALIGN
     assert _commit(mode=1, draft=A, T_max=32) == E.KDA_ERR_UNSUPPORTED
     assert _commit(mode=1, draft=A, slot_stride=100) == E.KDA_ERR_INVALID
+    assert _commit(mode=1, draft=A, opts=ctypes.byref(kda.kda_options(0, 0, 16))) == E.KDA_ERR_INVALID
+    # a bf16-output flag carried over from the verify call is accepted and ignored
+    assert _commit(mode=1, draft=A, opts=ctypes.byref(kda.kda_options(0, 0, E.KDA_OUT_BF16))) == E.KDA_ERR_HIP
 
 
 def _prefill(**over):
@@ -221,6 +237,9 @@ def test_prefill_host_checks():
     assert _prefill(dk=96) == E.KDA_ERR_UNSUPPORTED
     assert _prefill(opts=ctypes.byref(kda.kda_options(64, 0))) == E.KDA_ERR_UNSUPPORTED
     assert _prefill(alpha=A + 4) == E.KDA_ERR_ALIGN
+    assert _prefill(opts=ctypes.byref(kda.kda_options(0, 0, 4))) == E.KDA_ERR_INVALID
+    assert _prefill(out=A + 2) == E.KDA_ERR_ALIGN
+    assert _prefill(out=A + 2, opts=ctypes.byref(kda.kda_options(0, 0, E.KDA_OUT_BF16))) == E.KDA_ERR_HIP
 
 
 def _pack(**over):
