@@ -36,7 +36,16 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 METRIC = "KDA decode steps/s + achieved HBM GB/s (fp32 state), B=1..64, H=32, dk=dv=128"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "kda_decode_b64_counters.txt")
-KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_98_amd", "csrc", "kda.hip")
+# the sources the decode kernel is compiled from: the counters hold only while these are unchanged
+KERNEL_SOURCES = [os.path.join(ROOT, "gated_delta_rule_98_amd", "csrc", f) for f in ("kda_engine.h", "kda_decode.hip")]
+
+
+def kernel_source_sha256():
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        h.update(os.path.basename(path).encode() + b"\0")
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
 
 
 def log(msg):
@@ -477,9 +486,9 @@ def cpu_baseline(w, budget_s=12.0, max_steps=2000):
 
 # ----------------------------------------------------------------------------- counters
 
-def stored_traffic(launch_bytes):
+def stored_traffic(tile):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
-    the current kernel source."""
+    the current decode kernel source and the same launch shape."""
     if not os.path.exists(COUNTERS_FILE):
         return None
     fields = {}
@@ -487,8 +496,9 @@ def stored_traffic(launch_bytes):
         if ":" in line and not line.startswith("#"):
             key, val = line.split(":", 1)
             fields[key.strip()] = val.strip()
-    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    if fields.get("kernel_source_sha256") != src_hash:
+    if fields.get("kernel_source_sha256") != kernel_source_sha256():
+        return None
+    if fields.get("launch") != f"tile_w {tile[0]}, threads {tile[1]}":
         return None
     try:
         return int(float(fields["hbm_bytes_per_launch"]))
@@ -563,7 +573,7 @@ def main():
                    "global_batch": 64, "heads": 32, "dk": 128, "dv": 128, "tile_w": h["tile"][0],
                    "threads": h["tile"][1], "tokens_per_s": round(64 * 1e3 / h["ms_step"], 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": stored_traffic(h["bytes"]),
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": stored_traffic(h["tile"]),
                      "algorithmic_bytes_per_launch": h["bytes"],
                      "kernel_us": round(h["kernel_ms"] * 1e3, 3),
                      "kernel_us_event_pair_per_launch": round(h["pairs_ms"] * 1e3, 3)},

@@ -1,6 +1,8 @@
 """Build the HIP library for gfx950: gated_delta_rule_98_amd/libkda.so.
 
-One translation unit (csrc/kda.hip) holds the kernels and the C ABI of
+Sources (csrc/): kda_engine.h holds the device building blocks every kernel
+shares; kda_decode.hip, kda_verify.hip, kda_verify_chunk.hip, kda_prefill.hip
+and kda_state.hip hold the kernels; kda_api.hip holds the C ABI of
 include/kda.h. Flags:
   -ffp-contract=off   no implicit FMA contraction: every FMA is written out, so
                       all kernels round identically
@@ -16,7 +18,10 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "kda.hip")
+CSRC = os.path.join(PKG, "csrc")
+SOURCES = [os.path.join(CSRC, f) for f in ("kda_api.hip", "kda_decode.hip", "kda_verify.hip",
+                                           "kda_verify_chunk.hip", "kda_prefill.hip", "kda_state.hip")]
+HEADERS = [os.path.join(CSRC, "kda_engine.h"), os.path.join(ROOT, "include", "kda.h")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkda.so")
 ARCH = "gfx950"
@@ -34,7 +39,7 @@ FLAGS = [
 def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
     """Compile the library (always recompiles); return its path."""
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, f"-I{INCLUDE}", SRC, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, *extra, f"-I{INCLUDE}", *SOURCES, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
