@@ -398,9 +398,10 @@ def mixed(D, K, synth, reps):
                 verify_plus_commit_us=round(p_ms * 1e3, 3))
 
 
-def prefill_8k(D, K, synth, reps, tile_w=0):
+def prefill_8k(D, K, synth, reps, tile_w=0, chunked=False):
     """One 8000-token prompt, H=32, d=128, from a zero state, exporting the state after token
-    7680 in the same pass (the in-loop checkpoint of the pages' long-prompt prefill)."""
+    7680 in the same pass (the in-loop checkpoint of the pages' long-prompt prefill); the
+    recurrent kernel, or the chunk form (its two kernels, with a preallocated workspace)."""
     torch = D.torch
     w = synth.make_workload("prefill_8k")
     H, d = 32, 128
@@ -411,20 +412,33 @@ def prefill_8k(D, K, synth, reps, tile_w=0):
     pos = D.i([7680])
     ckpt = torch.empty(1, H, d, d, device=D.dev)
 
+    ws_bytes = K.kda_prefill_chunked_workspace(1, w.n_tok, H, d, d) if chunked else 0
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=D.dev) if chunked else None
+
     def run(i):
-        K.kda_prefill(cache, slots, cu, x["q"], x["k"], x["v"], x["alpha"], x["beta"], out, ckpt_pos=pos, ckpt=ckpt,
-                      tile_w=tile_w)
+        if chunked:
+            K.kda_prefill_chunked(cache, slots, cu, x["q"], x["k"], x["v"], x["alpha"], x["beta"], out,
+                                  ckpt_pos=pos, ckpt=ckpt, workspace=ws)
+        else:
+            K.kda_prefill(cache, slots, cu, x["q"], x["k"], x["v"], x["alpha"], x["beta"], out, ckpt_pos=pos,
+                          ckpt=ckpt, tile_w=tile_w)
 
     run(0)
     ms = timed_region(D, run, reps) / reps
     n = w.n_tok
     nbytes = n * H * ((2 * d + d) * 2 + d * 4 + 4 + d * 4) + 3 * H * d * d * 4 + 16
     flops = n * H * 7 * d * d
-    log(f"prefill 8000 tokens: {ms * 1e3:.1f} us ({n / ms * 1e3:.0f} tok/s, {flops / ms / 1e9:.2f} TFLOP/s)")
-    return dict(tokens=n, heads=H, us=round(ms * 1e3, 2), tokens_per_s=round(n / ms * 1e3, 1),
-                algorithmic_bytes=nbytes, gbs=round(nbytes / ms / 1e6, 1), flops=flops,
-                tflops=round(flops / ms / 1e9, 3), checkpoint_at=7680,
-                tile_w=K.kda_query_variant(1, H, d, d, T_max=n, op=K.KDA_OP_PREFILL, tile_w=tile_w)[0])
+    form = "chunked" if chunked else "recurrent"
+    log(f"prefill 8000 tokens ({form}): {ms * 1e3:.1f} us ({n / ms * 1e3:.0f} tok/s, "
+        f"{flops / ms / 1e9:.2f} TFLOP/s of recurrence work)")
+    res = dict(form=form, tokens=n, heads=H, us=round(ms * 1e3, 2), tokens_per_s=round(n / ms * 1e3, 1),
+               algorithmic_bytes=nbytes, gbs=round(nbytes / ms / 1e6, 1), flops=flops,
+               tflops=round(flops / ms / 1e9, 3), checkpoint_at=7680)
+    if chunked:
+        res["workspace_bytes"] = ws_bytes
+    else:
+        res["tile_w"] = K.kda_query_variant(1, H, d, d, T_max=n, op=K.KDA_OP_PREFILL, tile_w=tile_w)[0]
+    return res
 
 
 def state_transfer(D, K, synth, reps):
@@ -546,6 +560,7 @@ def main():
             spec_verify_b16_t8=spec_verify(D, K, synth, reps=200),
             mixed_b64_gated=mixed(D, K, synth, reps=200),
             prefill_8k_checkpoint=prefill_8k(D, K, synth, reps=5),
+            prefill_8k_checkpoint_chunked=prefill_8k(D, K, synth, reps=5, chunked=True),
             state_transfer_64x32_heads=state_transfer(D, K, synth, reps=100),
             raw_inputs_decode=raw_inputs_decode(D, K, synth, reps=200),
             headline_same_table_kernel_us=round(h["hot_ms"] * 1e3, 3),

@@ -31,6 +31,8 @@ from .kda import (  # noqa: F401
     KdaError,
     kda_decode_step,
     kda_prefill,
+    kda_prefill_chunked,
+    kda_prefill_chunked_workspace,
     kda_query_variant,
     kda_replay_commit,
     kda_state_pack,

@@ -1,9 +1,9 @@
 """Build the HIP library for gfx950: gated_delta_rule_98_amd/libkda.so.
 
 Sources (csrc/): kda_engine.h holds the device building blocks every kernel
-shares; kda_decode.hip, kda_verify.hip, kda_verify_chunk.hip, kda_prefill.hip
-and kda_state.hip hold the kernels; kda_api.hip holds the C ABI of
-include/kda.h. Flags:
+shares; kda_decode.hip, kda_verify.hip, kda_verify_chunk.hip, kda_prefill.hip,
+kda_prefill_chunk.hip and kda_state.hip hold the kernels; kda_api.hip holds
+the C ABI of include/kda.h. Flags:
   -ffp-contract=off   no implicit FMA contraction: every FMA is written out, so
                       all kernels round identically
   -Xclang -target-feature -Xclang -packed-fp32-ops
@@ -20,7 +20,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = [os.path.join(CSRC, f) for f in ("kda_api.hip", "kda_decode.hip", "kda_verify.hip",
-                                           "kda_verify_chunk.hip", "kda_prefill.hip", "kda_state.hip")]
+                                           "kda_verify_chunk.hip", "kda_prefill.hip", "kda_prefill_chunk.hip",
+                                           "kda_state.hip")]
 HEADERS = [os.path.join(CSRC, "kda_engine.h"), os.path.join(ROOT, "include", "kda.h")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkda.so")

@@ -5,6 +5,7 @@
 
 #include <string.h>
 
+#include "kda_chunk.h"
 #include "kda_engine.h"
 
 using namespace kda;
@@ -164,7 +165,82 @@ int check_replay_buf(const kda_replay_buf *rb) {
 
 }  // namespace
 
+// Chunks the chunk form of prefill can meet: each row is cut at most once (at
+// its checkpoint) and then into chunks, so at most ceil(n_tok / L) + 2 B.
+int64_t prefill_chunk_bound(int64_t B, int64_t n_tok) {
+  return (n_tok + kChunkTokens - 1) / kChunkTokens + 2 * B;
+}
+
 extern "C" {
+
+int kda_prefill_chunked_workspace(int32_t B, int32_t n_tok, int32_t H, int32_t dk, int32_t dv, size_t *bytes) {
+  if (!bytes || B < 0 || n_tok < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID;
+  if (!dims_supported(dk, dv)) return KDA_ERR_UNSUPPORTED;
+  *bytes = (size_t)prefill_chunk_bound(B, n_tok) * (size_t)H * prefill_chunk_ws_floats(dk, dv) * sizeof(float);
+  return KDA_OK;
+}
+
+int kda_prefill_chunked(float *cache, int64_t num_slots, int64_t slot_stride, const int32_t *slot_ids,
+                        const int32_t *cu_seqlens, int32_t B, int32_t n_tok, int32_t H, int32_t dk, int32_t dv,
+                        const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *alpha,
+                        const float *beta, void *out, const int32_t *ckpt_pos, float *ckpt, void *workspace,
+                        size_t workspace_bytes, int32_t *dev_err, const kda_options *opts, void *stream) {
+  Args f;
+  memset(&f, 0, sizeof f);
+  if (B < 0 || H <= 0 || dk <= 0 || dv <= 0 || n_tok < 0) return KDA_ERR_INVALID;
+  KDA_TRY(read_flags(opts, KDA_RAW_INPUTS | KDA_OUT_BF16, f));
+  if (!dims_supported(dk, dv)) return KDA_ERR_UNSUPPORTED;
+  if (opts && opts->tile_w != 0 && opts->tile_w != 16) return KDA_ERR_UNSUPPORTED;
+  if (B == 0 || (n_tok == 0 && !ckpt_pos)) return KDA_OK;
+  if (!slot_ids || !cu_seqlens) return KDA_ERR_INVALID;
+  KDA_TRY(check_cache(cache, num_slots, slot_stride, H, dk, dv));
+  if (n_tok > 0) KDA_TRY(check_inputs(q, k, v, alpha, beta, out, true, f.out_bf16));
+  if (ckpt_pos) {
+    if (!ckpt) return KDA_ERR_INVALID;
+    if (!aligned(ckpt, 16) || !aligned(ckpt_pos, 4)) return KDA_ERR_ALIGN;
+  }
+  if (!aligned(cu_seqlens, 4) || (dev_err && !aligned(dev_err, 4))) return KDA_ERR_ALIGN;
+  const int64_t chunks = prefill_chunk_bound(B, n_tok);
+  const size_t need = (size_t)chunks * (size_t)H * prefill_chunk_ws_floats(dk, dv) * sizeof(float);
+  if (!workspace || workspace_bytes < need) return KDA_ERR_INVALID;
+  if (!aligned(workspace, 16)) return KDA_ERR_ALIGN;
+  const int64_t prep_blocks = chunks * H, state_blocks = (int64_t)B * H * (dv / 16);
+  if (prep_blocks > 0x7fffffff || state_blocks > 0x7fffffff) return KDA_ERR_UNSUPPORTED;
+
+  ChunkArgs a;
+  memset(&a, 0, sizeof a);
+  a.cache = cache;
+  a.num_slots = num_slots;
+  a.slot_stride = slot_stride;
+  a.slot_ids = slot_ids;
+  a.cu = cu_seqlens;
+  a.ckpt_pos = ckpt_pos;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.out = static_cast<float *>(out);
+  a.ckpt = ckpt;
+  a.ws = static_cast<float *>(workspace);
+  a.dev_err = dev_err;
+  a.B = B;
+  a.H = H;
+  a.n_tok = n_tok;
+  a.ws_chunks = (int32_t)chunks;
+  a.ntile = dv / 16;
+  a.raw = f.raw;
+  a.out_bf16 = f.out_bf16;
+  void *args[] = {&a};
+  if (n_tok > 0) {
+    const hipError_t e = hipLaunchKernel(prefill_chunk_prep_kernel_for(dk, dv), dim3((unsigned)prep_blocks),
+                                         dim3(256), args, 0, (hipStream_t)stream);
+    if (e != hipSuccess) return KDA_ERR_HIP;
+  }
+  const hipError_t e = hipLaunchKernel(prefill_chunk_state_kernel_for(dk, dv), dim3((unsigned)state_blocks),
+                                       dim3(256), args, 0, (hipStream_t)stream);
+  return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
 
 int kda_prefill(float *cache, int64_t num_slots, int64_t slot_stride, const int32_t *slot_ids,
                 const int32_t *cu_seqlens, int32_t B, int32_t n_tok, int32_t H, int32_t dk, int32_t dv,

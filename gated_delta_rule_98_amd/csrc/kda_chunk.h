@@ -1,0 +1,33 @@
+// kda_chunk.h - interface of the chunk form of prefill (kda_prefill_chunk.hip)
+// to the C ABI in kda_api.hip.
+
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kChunkTokens = 32;  // tokens per chunk of the chunk form of prefill
+
+// Arguments of both chunk-prefill kernels.
+struct ChunkArgs {
+  float *cache;
+  int64_t num_slots, slot_stride;
+  const int32_t *slot_ids, *cu, *ckpt_pos;
+  const uint16_t *q, *k, *v;
+  const float *alpha, *beta;
+  float *out;  // fp32, or bf16 when out_bf16
+  float *ckpt;
+  float *ws;
+  int32_t *dev_err;
+  int32_t B, H, n_tok, ws_chunks, ntile, raw, out_bf16;
+};
+
+// Floats of workspace per (chunk, head).
+size_t prefill_chunk_ws_floats(int dk, int dv);
+// Kernel handles: the per-chunk precompute and the sequential pass over chunks.
+const void *prefill_chunk_prep_kernel_for(int dk, int dv);
+const void *prefill_chunk_state_kernel_for(int dk, int dv);
+
+}  // namespace kda

@@ -1,0 +1,471 @@
+// kda_prefill_chunk.hip - the chunk form of prefill (kda_prefill_chunked).
+//
+// The prompt of each row is cut into chunks of L = 32 tokens (a row with a
+// checkpoint strictly inside it is cut at the checkpoint first, so the state
+// there falls on a chunk boundary). Within a chunk, with S0 the state entering
+// it, Gamma_t the product of the decays of tokens 1..t of the chunk and
+// D(t, s) = prod_{s < r <= t} alpha_r (elementwise over key channels), the
+// token-by-token recurrence unrolls to
+//   u_t     = S0^T (Gamma_t k_t) + sum_{s<t} A_ts delta_s,  A_ts = sum_i k_t,i D(t,s)_i k_s,i
+//   delta_t = beta_t (v_t - u_t)
+//   o_t     = S0^T (Gamma_t q_t) + sum_{s<=t} B_ts delta_s, B_ts = sum_i q_t,i D(t,s)_i k_s,i
+//   S_L     = Diag(Gamma_L) S0 + sum_s (k_s D(L,s)) delta_s^T
+// Solving the lower-triangular system once per chunk, T = (I + Diag(beta) A)^-1
+// Diag(beta), gives delta = U - W S0 with W = T [Gamma k] and U = T V: every
+// product with the state becomes a dense matrix product.
+//
+// Two kernels. The precompute runs once per (chunk, head), all chunks in
+// parallel, and leaves W, U, [Gamma q], the keys decayed to the chunk end, B
+// and Gamma_L in a caller-provided workspace. The state pass runs per (row,
+// head, 16 value columns) through the row's chunks in order, with the state in
+// MFMA accumulator registers:
+//   delta = U - W S0 ;  o = [Gamma q] S0 + B delta ;  S0 <- Diag(Gamma_L) S0 + Kt^T delta
+// all on v_mfma_f32_16x16x4f32.
+//
+// Decay products never divide. A chunk is two sub-blocks of 16 tokens. With
+// P_t the product over its own sub-block up to and including t, and R_s the
+// product over its sub-block after s:
+//   * across sub-blocks (t in block 1, s in block 0) D(t, s) = P_t R_s, so A
+//     and B there are MFMA products of [P k] and [P q] with [R k];
+//   * inside a sub-block D(t, s) is carried as a running product;
+//   * Gamma_t = (product of the earlier sub-blocks) P_t and the decay to the
+//     chunk end is R_s (product of the later sub-blocks).
+// Any decay in (0, 1] is safe: a product only underflows where the true value
+// does. The results equal the token-by-token recurrence up to rounding (not bit
+// for bit: the kernel of kda_prefill gives bit-identical states).
+
+#include "kda_chunk.h"
+#include "kda_engine.h"
+
+namespace kda {
+namespace {
+
+constexpr int kCL = kChunkTokens;  // tokens per chunk
+constexpr int kSB = 16;            // sub-block: the MFMA row block
+static_assert(kCL == 2 * kSB, "the chunk is two sub-blocks");
+
+// Workspace of one (chunk, head), in floats.
+template <int DK, int DV>
+struct ChunkWs {
+  static constexpr int W = 0;               // [kCL][DK]  T [Gamma k]
+  static constexpr int QD = W + kCL * DK;   // [kCL][DK]  Gamma q
+  static constexpr int KT = QD + kCL * DK;  // [DK][4][kCL / 4]  k_s R_s (decayed to the chunk end), by channel
+  static constexpr int U = KT + kCL * DK;   // [kCL][DV]  T v
+  static constexpr int BM = U + kCL * DV;   // [kCL][4][kCL / 4]  B
+  static constexpr int GL = BM + kCL * kCL; // [DK]  Gamma_L
+  static constexpr int FLOATS = GL + DK;
+  static_assert(FLOATS % 4 == 0, "float4 alignment of every (chunk, head)");
+};
+
+// [.][4][kCL / 4] layout of the KT and BM entries: element s of a row is at
+// (s % 4) * (kCL / 4) + s / 4, so the lane that feeds MFMA steps 0..7 with
+// entries g, 4 + g, ... reads two float4s.
+__device__ __forceinline__ int perm_col(int s) { return (s & 3) * (kCL / 4) + (s >> 2); }
+
+// Chunks of one row. nch = 0 for a row that does not run (padding, or any
+// device error; the state pass reports those).
+struct ChunkRow {
+  int nch, n1, s1, Tb;  // chunks, chunks before the checkpoint cut, the cut, tokens
+};
+
+__device__ __forceinline__ ChunkRow chunk_row(const ChunkArgs &a, int b) {
+  ChunkRow r = {0, 0, 0, 0};
+  const int32_t slot = a.slot_ids[b];
+  if (slot < 0 || slot >= a.num_slots) return r;
+  const int32_t c0 = a.cu[b], c1 = a.cu[b + 1];
+  if (c0 < 0 || c1 < c0 || c1 > a.n_tok) return r;
+  const int Tb = c1 - c0;
+  const int ck = a.ckpt_pos ? a.ckpt_pos[b] : -1;
+  if (ck > Tb) return r;
+  r.Tb = Tb;
+  r.s1 = (ck > 0 && ck < Tb) ? ck : Tb;
+  r.n1 = (r.s1 + kCL - 1) / kCL;
+  r.nch = r.n1 + (Tb - r.s1 + kCL - 1) / kCL;
+  return r;
+}
+
+// Token range [t0, t0 + n) of chunk j of a row.
+__device__ __forceinline__ void chunk_tokens(const ChunkRow &r, int j, int &t0, int &n) {
+  if (j < r.n1) {
+    t0 = j * kCL;
+    n = min(kCL, r.s1 - t0);
+  } else {
+    t0 = r.s1 + (j - r.n1) * kCL;
+    n = min(kCL, r.Tb - t0);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Precompute, one workgroup per (chunk, head)
+// ----------------------------------------------------------------------------
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void prefill_chunk_prep_kernel(ChunkArgs a) {
+  using WS = ChunkWs<DK, DV>;
+  constexpr int CPT = DK / 16;  // channels per lane when a 16-lane row spans DK
+  __shared__ float kb[kCL * DK];  // k, then [P k]
+  __shared__ float qb[kCL * DK];  // q, then [P q]
+  __shared__ float ab[kCL * DK];  // alpha, then [R k]
+  __shared__ float vb[kCL * DV];
+  __shared__ float bet[kCL];
+  __shared__ float Am[kCL * kCL];    // A (strictly lower)
+  __shared__ float Tm[kCL * kCL];    // T
+  __shared__ float bef[2 * DK];      // product of the sub-blocks before each sub-block
+
+  const int c = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  // the row and chunk this workgroup prepares
+  int b = 0, jc = c;
+  ChunkRow r = {0, 0, 0, 0};
+  for (; b < a.B; ++b) {
+    r = chunk_row(a, b);
+    if (jc < r.nch) break;
+    jc -= r.nch;
+  }
+  if (b >= a.B) return;
+  int t0, n;
+  chunk_tokens(r, jc, t0, n);
+  const int64_t row0 = (int64_t)a.cu[b] + t0;
+  float *ws = a.ws + ((int64_t)c * a.H + h) * WS::FLOATS;
+
+  // stage the chunk; tokens past its end are k = q = v = 0, alpha = 1, beta = 0
+  for (int idx = threadIdx.x; idx < kCL * (DK / 4); idx += blockDim.x) {
+    const int t = idx / (DK / 4), i = (idx % (DK / 4)) * 4;
+    float4 kk = make_float4(0.0f, 0.0f, 0.0f, 0.0f), qq = kk, al = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+    if (t < n) {
+      const int64_t off = ((row0 + t) * a.H + h) * DK + i;
+      kk = unpack_bf16x4(*reinterpret_cast<const uint2 *>(a.k + off));
+      qq = unpack_bf16x4(*reinterpret_cast<const uint2 *>(a.q + off));
+      al = *reinterpret_cast<const float4 *>(a.alpha + off);
+    }
+    *reinterpret_cast<float4 *>(kb + t * DK + i) = kk;
+    *reinterpret_cast<float4 *>(qb + t * DK + i) = qq;
+    *reinterpret_cast<float4 *>(ab + t * DK + i) = al;
+  }
+  for (int idx = threadIdx.x; idx < kCL * DV; idx += blockDim.x) {
+    const int t = idx / DV, j = idx % DV;
+    vb[idx] = t < n ? bf16_to_f32(a.v[((row0 + t) * a.H + h) * DV + j]) : 0.0f;
+  }
+  if ((int)threadIdx.x < kCL) bet[threadIdx.x] = (int)threadIdx.x < n ? a.beta[(row0 + threadIdx.x) * a.H + h] : 0.0f;
+  // B above the diagonal is zero
+  for (int idx = threadIdx.x; idx < kCL * kCL; idx += blockDim.x) {
+    const int t = idx / kCL, s = idx % kCL;
+    if (s > t) ws[WS::BM + t * kCL + perm_col(s)] = 0.0f;
+  }
+  __syncthreads();
+  if (a.raw) {
+    prep_staged<DK>(kb, qb, ab, bet, n);
+    __syncthreads();
+  }
+
+  // inside each sub-block: A and B by running products. Row (s, 16 lanes) carries
+  // D(t, s) over its lane's CPT channels as t advances and sums over the row.
+  {
+    const int s = threadIdx.x >> 4, cl = threadIdx.x & 15;
+#pragma unroll
+    for (int J = 0; J < 2; ++J) {
+      const int sg = J * kSB + s;
+      float d[CPT];
+      float pd = 0.0f;
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) {
+        d[e] = kb[sg * DK + cl * CPT + e];
+        pd = __builtin_fmaf(qb[sg * DK + cl * CPT + e], d[e], pd);
+      }
+      pd = row16_sum(pd);
+      if (cl == 0) ws[WS::BM + sg * kCL + perm_col(sg)] = pd;
+      for (int t = s + 1; t < kSB; ++t) {
+        const int tg = J * kSB + t;
+        float pa = 0.0f, pb = 0.0f;
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) {
+          const int ch = tg * DK + cl * CPT + e;
+          d[e] = d[e] * ab[ch];
+          pa = __builtin_fmaf(kb[ch], d[e], pa);
+          pb = __builtin_fmaf(qb[ch], d[e], pb);
+        }
+        pa = row16_sum(pa);
+        pb = row16_sum(pb);
+        if (cl == 0) {
+          Am[tg * kCL + sg] = pa;
+          ws[WS::BM + tg * kCL + perm_col(sg)] = pb;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // per key channel: [P k] and [P q] in place of k and q, [R k] in place of alpha,
+  // Gamma q and the keys decayed to the chunk end to the workspace
+  if ((int)threadIdx.x < DK) {
+    const int i = threadIdx.x;
+    float kf[kCL];
+    float P = 1.0f, G0 = 1.0f, G1 = 1.0f;
+#pragma unroll
+    for (int t = 0; t < kCL; ++t) {
+      if (t == kSB) P = 1.0f;
+      P = P * ab[t * DK + i];
+      kf[t] = kb[t * DK + i] * P;
+      qb[t * DK + i] = qb[t * DK + i] * P;
+      if (t == kSB - 1) G0 = P;
+      if (t == kCL - 1) G1 = P;
+    }
+    bef[i] = 1.0f;
+    bef[DK + i] = G0;
+    ws[WS::GL + i] = G0 * G1;
+#pragma unroll
+    for (int t = 0; t < kCL; ++t) ws[WS::QD + t * DK + i] = t < kSB ? qb[t * DK + i] : qb[t * DK + i] * G0;
+    float R = 1.0f;
+#pragma unroll
+    for (int s = kCL - 1; s >= 0; --s) {
+      if (s == kSB - 1) R = 1.0f;
+      const float kr = kb[s * DK + i] * R;
+      R = R * ab[s * DK + i];
+      ab[s * DK + i] = kr;
+      kb[s * DK + i] = kf[s];
+      ws[WS::KT + i * kCL + perm_col(s)] = s < kSB ? kr * G1 : kr;
+    }
+  }
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+  // across the sub-blocks: A (wave 0) and B (wave 1) for t in block 1, s in block 0,
+  // [P k]_t . [R k]_s and [P q]_t . [R k]_s over DK on MFMA
+  if (wave < 2) {
+    const float *arow = (wave == 0 ? kb : qb) + (kSB + m) * DK;  // A operand: row t = kSB + m
+    const float *brow = ab + m * DK;                             // B operand: column s = m
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int cb = 0; cb < DK / 16; ++cb) {
+      const float4 av = *reinterpret_cast<const float4 *>(arow + 16 * cb + 4 * g);
+      const float4 bv = *reinterpret_cast<const float4 *>(brow + 16 * cb + 4 * g);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, acc, 0, 0, 0);
+    }
+    // accumulator: lane (m, g) holds rows 4g .. 4g + 3 (t = kSB + 4g + e) of column s = m
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = kSB + 4 * g + e;
+      if (wave == 0)
+        Am[t * kCL + m] = acc[e];
+      else
+        ws[WS::BM + t * kCL + perm_col(m)] = acc[e];
+    }
+  }
+  __syncthreads();
+
+  // T = (I + Diag(beta) A)^-1 Diag(beta), one column per thread by forward substitution
+  if ((int)threadIdx.x < kCL) {
+    const int col = threadIdx.x;
+    float x[kCL];
+#pragma unroll
+    for (int t = 0; t < kCL; ++t) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int s = 0; s < t; ++s) acc = __builtin_fmaf(Am[t * kCL + s], x[s], acc);
+      x[t] = t == col ? 1.0f : (t < col ? 0.0f : -bet[t] * acc);
+    }
+    const float bc = bet[col];
+#pragma unroll
+    for (int t = 0; t < kCL; ++t) Tm[t * kCL + col] = x[t] * bc;
+  }
+  __syncthreads();
+
+  // W = T [Gamma k] and U = T V: 16 x 16 output tiles spread over the waves
+  constexpr int TW = DK / 16, TU = DV / 16, NT = 2 * (TW + TU);
+  for (int tile = wave; tile < NT; tile += 4) {
+    const int rt = tile & 1;
+    int ct = tile >> 1;
+    const bool isU = ct >= TW;
+    if (isU) ct -= TW;
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < kCL / 4; ++ks) {
+      const int tok = 4 * ks + g;
+      const float av = Tm[(16 * rt + m) * kCL + tok];
+      const float bv = isU ? vb[tok * DV + 16 * ct + m]
+                           : kb[tok * DK + 16 * ct + m] * bef[(tok >= kSB ? DK : 0) + 16 * ct + m];
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * rt + 4 * g + e;
+      if (isU)
+        ws[WS::U + row * DV + 16 * ct + m] = acc[e];
+      else
+        ws[WS::W + row * DK + 16 * ct + m] = acc[e];
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// State pass, one workgroup per (row, head, 16 value columns)
+// ----------------------------------------------------------------------------
+//
+// Wave w holds key channels [w DK/4, (w+1) DK/4) of the 16 columns in the
+// accumulator layout: lane (j, g) holds channels 16 ct + 4g .. + 3 (of its
+// quarter) of column j. The products with the state are split over the waves
+// along DK and summed in LDS.
+
+__device__ __forceinline__ void put_chunk_out(const ChunkArgs &a, int64_t idx, float y) {
+  if (a.out_bf16)
+    reinterpret_cast<uint16_t *>(a.out)[idx] = f32_to_bf16(y);
+  else
+    a.out[idx] = y;
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void prefill_chunk_state_kernel(ChunkArgs a) {
+  using WS = ChunkWs<DK, DV>;
+  constexpr int CPW = DK / 4;    // key channels per wave
+  constexpr int NCT = CPW / 16;  // 16-channel tiles per wave
+  __shared__ float part[4][2][kCL][16];  // per wave: W S and [Gamma q] S over its channels
+  __shared__ float dl[kCL][16];          // delta
+  __shared__ float o0[kCL][16];          // [Gamma q] S0
+
+  const Unit u = unit_of_block(a.ntile, a.H);
+  const int32_t slot = a.slot_ids[u.b];
+  if (slot < 0) return;
+  if (slot >= a.num_slots) {
+    report(a.dev_err, u, KDA_DEVERR_SLOT);
+    return;
+  }
+  const int32_t c0 = a.cu[u.b], c1 = a.cu[u.b + 1];
+  if (c0 < 0 || c1 < c0 || c1 > a.n_tok) {
+    report(a.dev_err, u, KDA_DEVERR_SEQLEN);
+    return;
+  }
+  const int ck = a.ckpt_pos ? a.ckpt_pos[u.b] : -1;
+  if (ck > c1 - c0) {
+    report(a.dev_err, u, KDA_DEVERR_CKPT);
+    return;
+  }
+  const ChunkRow r = chunk_row(a, u.b);
+  int cbase = 0;
+  for (int b = 0; b < u.b; ++b) cbase += chunk_row(a, b).nch;
+  if (cbase + r.nch > a.ws_chunks) {  // only with rows that overlap in cu_seqlens
+    report(a.dev_err, u, KDA_DEVERR_SEQLEN);
+    return;
+  }
+  if (r.nch == 0 && ck != 0) return;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
+  const int n0 = 16 * u.tile;
+  const int coff = CPW * wave + 4 * g;  // first channel of this lane in tile 0
+  float *S = a.cache + (int64_t)slot * a.slot_stride + ((int64_t)u.h * DV + n0 + j) * DK + coff;
+  float *CK = ck >= 0 ? a.ckpt + (((int64_t)u.b * a.H + u.h) * DV + n0 + j) * DK + coff : nullptr;
+  float4 s[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) s[ct] = ld4<kVerifyLoadStream>(S + 16 * ct);
+  if (ck == 0) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) st4<kVerifyStoreStream>(CK + 16 * ct, s[ct]);
+  }
+
+  for (int jc = 0; jc < r.nch; ++jc) {
+    int t0, n;
+    chunk_tokens(r, jc, t0, n);
+    const float *w = a.ws + ((int64_t)(cbase + jc) * a.H + u.h) * WS::FLOATS;
+
+    // W S0 and [Gamma q] S0 over this wave's channels
+    v4f pd[2], po[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      pd[rt] = {0.0f, 0.0f, 0.0f, 0.0f};
+      po[rt] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const int off = (16 * rt + j) * DK + coff + 16 * ct;
+        const float4 wv = *reinterpret_cast<const float4 *>(w + WS::W + off);
+        const float4 qv = *reinterpret_cast<const float4 *>(w + WS::QD + off);
+        pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv.x, s[ct].x, pd[rt], 0, 0, 0);
+        po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv.x, s[ct].x, po[rt], 0, 0, 0);
+        pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv.y, s[ct].y, pd[rt], 0, 0, 0);
+        po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv.y, s[ct].y, po[rt], 0, 0, 0);
+        pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv.z, s[ct].z, pd[rt], 0, 0, 0);
+        po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv.z, s[ct].z, po[rt], 0, 0, 0);
+        pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv.w, s[ct].w, pd[rt], 0, 0, 0);
+        po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv.w, s[ct].w, po[rt], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        part[wave][0][16 * rt + 4 * g + e][j] = pd[rt][e];
+        part[wave][1][16 * rt + 4 * g + e][j] = po[rt][e];
+      }
+    __syncthreads();
+
+    // delta = U - W S0, and [Gamma q] S0, summed over the waves in a fixed order
+    for (int idx = threadIdx.x; idx < kCL * 16; idx += blockDim.x) {
+      const int t = idx >> 4, col = idx & 15;
+      const float sd = ((part[0][0][t][col] + part[1][0][t][col]) + part[2][0][t][col]) + part[3][0][t][col];
+      const float so = ((part[0][1][t][col] + part[1][1][t][col]) + part[2][1][t][col]) + part[3][1][t][col];
+      dl[t][col] = w[WS::U + t * DV + n0 + col] - sd;
+      o0[t][col] = so;
+    }
+    __syncthreads();
+
+    // o = [Gamma q] S0 + B delta: waves 0 and 1, 16 tokens each
+    if (wave < 2) {
+      const int rt = wave;
+      v4f acc = {o0[16 * rt + 4 * g][j], o0[16 * rt + 4 * g + 1][j], o0[16 * rt + 4 * g + 2][j],
+                 o0[16 * rt + 4 * g + 3][j]};
+      const float *brow = w + WS::BM + (16 * rt + j) * kCL + g * (kCL / 4);
+      const float4 b0 = *reinterpret_cast<const float4 *>(brow);
+      const float4 b1 = *reinterpret_cast<const float4 *>(brow + 4);
+      const float bm[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bm[ks], dl[4 * ks + g][j], acc, 0, 0, 0);
+      const int64_t obase = ((int64_t)c0 + t0) * a.H + u.h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tok = 16 * rt + 4 * g + e;
+        if (tok < n) put_chunk_out(a, (obase + (int64_t)tok * a.H) * DV + n0 + j, acc[e]);
+      }
+    }
+
+    // S0 <- Diag(Gamma_L) S0 + Kt^T delta over this wave's channels
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const float4 gl = *reinterpret_cast<const float4 *>(w + WS::GL + coff + 16 * ct);
+      v4f acc = {s[ct].x * gl.x, s[ct].y * gl.y, s[ct].z * gl.z, s[ct].w * gl.w};
+      const float *krow = w + WS::KT + (CPW * wave + 16 * ct + j) * kCL + g * (kCL / 4);
+      const float4 k0 = *reinterpret_cast<const float4 *>(krow);
+      const float4 k1 = *reinterpret_cast<const float4 *>(krow + 4);
+      const float kt[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[ks], dl[4 * ks + g][j], acc, 0, 0, 0);
+      s[ct] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+    if (ck > 0 && t0 + n == ck) {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) st4<kVerifyStoreStream>(CK + 16 * ct, s[ct]);
+    }
+  }
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) st4<kVerifyStoreStream>(S + 16 * ct, s[ct]);
+}
+
+}  // namespace
+
+size_t prefill_chunk_ws_floats(int dk, int dv) {
+  if (dk == 64) return dv == 64 ? ChunkWs<64, 64>::FLOATS : ChunkWs<64, 128>::FLOATS;
+  return dv == 64 ? ChunkWs<128, 64>::FLOATS : ChunkWs<128, 128>::FLOATS;
+}
+
+const void *prefill_chunk_prep_kernel_for(int dk, int dv) {
+  if (dk == 64) return dv == 64 ? (const void *)prefill_chunk_prep_kernel<64, 64> : (const void *)prefill_chunk_prep_kernel<64, 128>;
+  if (dk == 128) return dv == 64 ? (const void *)prefill_chunk_prep_kernel<128, 64> : (const void *)prefill_chunk_prep_kernel<128, 128>;
+  return nullptr;
+}
+
+const void *prefill_chunk_state_kernel_for(int dk, int dv) {
+  if (dk == 64) return dv == 64 ? (const void *)prefill_chunk_state_kernel<64, 64> : (const void *)prefill_chunk_state_kernel<64, 128>;
+  if (dk == 128) return dv == 64 ? (const void *)prefill_chunk_state_kernel<128, 64> : (const void *)prefill_chunk_state_kernel<128, 128>;
+  return nullptr;
+}
+
+}  // namespace kda

@@ -89,6 +89,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_replay_commit.restype = ctypes.c_int
     lib.kda_prefill.argtypes = [P, i64, i64, P, P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P]
     lib.kda_prefill.restype = ctypes.c_int
+    lib.kda_prefill_chunked.argtypes = [P, i64, i64, P, P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P,
+                                        P, ctypes.c_size_t, P, P, P]
+    lib.kda_prefill_chunked.restype = ctypes.c_int
+    lib.kda_prefill_chunked_workspace.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.kda_prefill_chunked_workspace.restype = ctypes.c_int
     for name in ("kda_state_pack", "kda_state_unpack"):
         fn = getattr(lib, name)
         fn.argtypes = [P, i64, i64, P, i32, i32, i32, i32, i32, i32, i32, i32, P, P, P]
@@ -341,6 +346,60 @@ def kda_prefill(cache: torch.Tensor, slot_ids: torch.Tensor, cu_seqlens: torch.T
         _stream(stream))
     if rc != KDA_OK:
         raise KdaError(rc, "kda_prefill")
+
+
+def kda_prefill_chunked_workspace(B: int, n_tok: int, H: int, dk: int, dv: int) -> int:
+    """Workspace bytes kda_prefill_chunked needs for these sizes."""
+    n = ctypes.c_size_t(0)
+    rc = load_library().kda_prefill_chunked_workspace(B, n_tok, H, dk, dv, ctypes.byref(n))
+    if rc != KDA_OK:
+        raise KdaError(rc, "kda_prefill_chunked_workspace")
+    return n.value
+
+
+def kda_prefill_chunked(cache: torch.Tensor, slot_ids: torch.Tensor, cu_seqlens: torch.Tensor, q, k, v, alpha,
+                        beta, out: torch.Tensor, *, ckpt_pos: Optional[torch.Tensor] = None,
+                        ckpt: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                        dev_err: Optional[torch.Tensor] = None, tile_w: int = 0, raw_inputs: bool = False,
+                        stream=None) -> None:
+    """Chunk form of kda_prefill: same arguments plus a device workspace (any dtype, at least
+    kda_prefill_chunked_workspace() bytes); None allocates one for the call."""
+    ns, stride, H, dv, dk = _cache(cache)
+    _dev(slot_ids, "slot_ids", (torch.int32,), 1)
+    _dev(cu_seqlens, "cu_seqlens", (torch.int32,), 1)
+    B = slot_ids.shape[0]
+    _shape(cu_seqlens, "cu_seqlens", (B + 1,))
+    for name, t, d in (("q", q, _BF16_TYPES), ("k", k, _BF16_TYPES), ("v", v, _BF16_TYPES),
+                       ("alpha", alpha, (torch.float32,)), ("beta", beta, (torch.float32,)),
+                       ("out", out, (torch.float32,) + _BF16_TYPES)):
+        _dev(t, name, d)
+    n_tok = k.shape[0]
+    for name, t, shape in (("q", q, (n_tok, H, dk)), ("k", k, (n_tok, H, dk)), ("v", v, (n_tok, H, dv)),
+                           ("alpha", alpha, (n_tok, H, dk)), ("beta", beta, (n_tok, H)),
+                           ("out", out, (n_tok, H, dv))):
+        _shape(t, name, shape)
+    if ckpt_pos is not None:
+        _dev(ckpt_pos, "ckpt_pos", (torch.int32,), 1)
+        _shape(ckpt_pos, "ckpt_pos", (B,))
+        if ckpt is None:
+            raise ValueError("ckpt_pos needs a ckpt buffer")
+    if ckpt is not None:
+        _dev(ckpt, "ckpt", (torch.float32,))
+        _shape(ckpt, "ckpt", (B, H, dv, dk))
+    if dev_err is not None:
+        _dev(dev_err, "dev_err", (torch.int32,))
+    if workspace is None:
+        workspace = torch.empty(kda_prefill_chunked_workspace(B, n_tok, H, dk, dv), dtype=torch.uint8,
+                                device=cache.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    rc = load_library().kda_prefill_chunked(
+        cache.data_ptr(), ns, stride, slot_ids.data_ptr(), cu_seqlens.data_ptr(), B, n_tok, H, dk, dv,
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(), beta.data_ptr(), out.data_ptr(),
+        _ptr(ckpt_pos), _ptr(ckpt), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _ptr(dev_err), _ref(_opts(tile_w, 0, _flags(raw_inputs, out))), _stream(stream))
+    if rc != KDA_OK:
+        raise KdaError(rc, "kda_prefill_chunked")
 
 
 def _state_copy(name, cache, slot_ids, buf, heads, cols, dev_err, stream):

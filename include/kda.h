@@ -61,6 +61,7 @@
 #ifndef KDA_H
 #define KDA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -241,6 +242,36 @@ int kda_prefill(float *cache, int64_t num_slots, int64_t slot_stride,
                 const float *alpha, const float *beta, void *out,
                 const int32_t *ckpt_pos, float *ckpt, int32_t *dev_err,
                 const kda_options *opts, void *stream);
+
+/*
+ * Chunk form of kda_prefill (the same call plus a workspace): each row's prompt
+ * is cut into chunks of 32 tokens (first at ckpt_pos[b] when it falls strictly
+ * inside the row, so the checkpoint lies on a chunk boundary). A first kernel
+ * prepares every (chunk, head) in parallel: the decay products inside the
+ * chunk, the lower-triangular system of the delta rule solved once per chunk,
+ * and the matrices that turn the chunk's effect on the state into dense
+ * products. A second kernel runs each (row, head, 16 value columns) through its
+ * chunks in order with those products on MFMA. Outputs and states agree with
+ * kda_prefill to rounding (not bit for bit). Arguments, layouts, flags and
+ * device errors are kda_prefill's; kda_options.tile_w may be 0 or 16.
+ * workspace: device memory of at least kda_prefill_chunked_workspace() bytes,
+ * 16-byte aligned, owned by the caller; its contents need no initialization
+ * and are dead when the stream has passed the call. A smaller workspace is
+ * KDA_ERR_INVALID.
+ */
+int kda_prefill_chunked(float *cache, int64_t num_slots, int64_t slot_stride,
+                        const int32_t *slot_ids, const int32_t *cu_seqlens,
+                        int32_t B, int32_t n_tok, int32_t H, int32_t dk, int32_t dv,
+                        const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                        const float *alpha, const float *beta, void *out,
+                        const int32_t *ckpt_pos, float *ckpt,
+                        void *workspace, size_t workspace_bytes, int32_t *dev_err,
+                        const kda_options *opts, void *stream);
+
+/* Host only. Workspace bytes kda_prefill_chunked needs for these sizes
+ * (written to *bytes): about 2.1 KB per (token, head) at dk = dv = 128. */
+int kda_prefill_chunked_workspace(int32_t B, int32_t n_tok, int32_t H, int32_t dk, int32_t dv,
+                                  size_t *bytes);
 
 /*
  * State transfer for prefill/decode disaggregation and offload ("Kimi K3

@@ -26,7 +26,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert set(declared_functions()) == {"kda_decode_step", "kda_verify_chunk", "kda_replay_commit",
-                                         "kda_prefill", "kda_state_pack", "kda_state_unpack",
+                                         "kda_prefill", "kda_prefill_chunked", "kda_prefill_chunked_workspace",
+                                         "kda_state_pack", "kda_state_unpack",
                                          "kda_query_variant", "kda_status_str"}
 
 
@@ -240,6 +241,40 @@ def test_prefill_host_checks():
     assert _prefill(opts=ctypes.byref(kda.kda_options(0, 0, 4))) == E.KDA_ERR_INVALID
     assert _prefill(out=A + 2) == E.KDA_ERR_ALIGN
     assert _prefill(out=A + 2, opts=ctypes.byref(kda.kda_options(0, 0, E.KDA_OUT_BF16))) == E.KDA_ERR_HIP
+
+
+def _prefill_chunked(**over):
+    d = dict(cache=A, num_slots=8, slot_stride=2 * 128 * 128, slot_ids=A, cu=A, B=4, n_tok=90, H=2, dk=128,
+             dv=128, q=A, k=A, v=A, alpha=A, beta=A, out=A, ckpt_pos=None, ckpt=None, ws=A, ws_bytes=1 << 40,
+             dev_err=None, opts=None, stream=None)
+    d.update(over)
+    return kda.load_library().kda_prefill_chunked(*d.values())
+
+
+@needs_no_gpu
+def test_prefill_chunked_host_checks():
+    E = kda
+    lib = kda.load_library()
+    nbytes = ctypes.c_size_t(0)
+    assert lib.kda_prefill_chunked_workspace(4, 90, 2, 128, 128, ctypes.byref(nbytes)) == E.KDA_OK
+    # (ceil(90 / 32) + 2 * 4) chunks x 2 heads x (3 * 32 * 128 + 32 * 128 + 32 * 32 + 128) floats
+    assert nbytes.value == 11 * 2 * (3 * 32 * 128 + 32 * 128 + 32 * 32 + 128) * 4
+    assert lib.kda_prefill_chunked_workspace(4, 90, 2, 96, 128, ctypes.byref(nbytes)) == E.KDA_ERR_UNSUPPORTED
+    assert lib.kda_prefill_chunked_workspace(4, -1, 2, 128, 128, ctypes.byref(nbytes)) == E.KDA_ERR_INVALID
+    assert lib.kda_prefill_chunked_workspace(4, 90, 2, 128, 128, None) == E.KDA_ERR_INVALID
+    assert _prefill_chunked(B=0) == E.KDA_OK
+    assert _prefill_chunked(n_tok=0) == E.KDA_OK
+    assert _prefill_chunked(ws=None) == E.KDA_ERR_INVALID
+    assert _prefill_chunked(ws_bytes=1000) == E.KDA_ERR_INVALID              # workspace too small
+    assert _prefill_chunked(ws=A + 4) == E.KDA_ERR_ALIGN
+    assert _prefill_chunked(cu=None) == E.KDA_ERR_INVALID
+    assert _prefill_chunked(dk=96) == E.KDA_ERR_UNSUPPORTED
+    assert _prefill_chunked(opts=ctypes.byref(kda.kda_options(32, 0, 0))) == E.KDA_ERR_UNSUPPORTED
+    assert _prefill_chunked(opts=ctypes.byref(kda.kda_options(0, 0, 4))) == E.KDA_ERR_INVALID
+    assert _prefill_chunked(ckpt_pos=A, ckpt=None) == E.KDA_ERR_INVALID
+    assert _prefill_chunked(out=A + 2) == E.KDA_ERR_ALIGN
+    # passes every host check: only the launch fails without a device
+    assert _prefill_chunked(out=A + 2, opts=ctypes.byref(kda.kda_options(16, 0, E.KDA_OUT_BF16))) == E.KDA_ERR_HIP
 
 
 def _pack(**over):

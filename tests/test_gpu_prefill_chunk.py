@@ -1,0 +1,181 @@
+"""GPU parity of kda_prefill_chunked (the chunk form of prefill) against the CPU oracle.
+
+Outputs within 1e-4 relative L2 of the oracle's, final and checkpoint states
+within 1e-3 relative Frobenius; slot handling and device errors bit-exact. The
+rows cover empty prompts, prompts shorter than, equal to and just past one
+32-token chunk, long prompts, checkpoints before the prompt, inside a chunk,
+on a chunk boundary and at the end, padding rows and extreme decays. The chunk
+form also agrees with kda_prefill (the recurrent form) to 1e-5.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_98_amd as K
+import oracle
+import synth
+from gpu_util import (SENTINEL_BITS, bits, bf16, dev, f32, i32, log, raw_step_inputs, rel_l2, sentinel,
+                      step_inputs)
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 1e-4
+STATE_TOL = 1e-3
+
+
+def _run(w, cache_d, *, slots=None, pos=None, dev_err=None, raw=False, out_dtype=torch.float32, chunked=True,
+         x=None):
+    x = x if x is not None else (raw_step_inputs(w, 0) if raw else step_inputs(w, 0))
+    slots = w.slot_ids if slots is None else slots
+    out = sentinel((w.n_tok, w.H, w.dv))
+    if out_dtype != torch.float32:
+        out = torch.full((w.n_tok, w.H, w.dv), -1, dtype=torch.int16, device=dev()).view(out_dtype)
+    ckpt = sentinel((w.B, w.H, w.dv, w.dk)) if pos is not None else None
+    fn = K.kda_prefill_chunked if chunked else K.kda_prefill
+    fn(cache_d, i32(slots), i32(w.cu_seqlens), x["q"], x["k"], x["v"], x["alpha"], x["beta"], out,
+       ckpt_pos=None if pos is None else i32(pos), ckpt=ckpt, dev_err=dev_err, raw_inputs=raw)
+    return out, ckpt
+
+
+def _check(w, slots, pos, out, ckpt, cache_d, *, raw=False, alpha=None, tol_out=OUT_TOL):
+    cache_h = w.cache.copy()
+    a = alpha if alpha is not None else (w.a_raw[0] if raw else w.alpha[0])
+    ref_out, ref_ckpt, rc = oracle.prefill(cache_h, slots, w.cu_seqlens, w.q_raw[0] if raw else w.q[0],
+                                           w.k_raw[0] if raw else w.k[0], w.v[0], a,
+                                           w.b_raw[0] if raw else w.beta[0], ckpt_pos=pos, prologue=raw)
+    assert rc == 0
+    live_rows = [b for b in range(w.B) if slots[b] >= 0]
+    live = np.concatenate([np.arange(w.cu_seqlens[b], w.cu_seqlens[b + 1]) for b in live_rows] + [np.zeros(0, int)])
+    o = out.float().cpu().numpy()
+    err = rel_l2(o[live], ref_out[live]) if len(live) else 0.0
+    got = cache_d.cpu().numpy()
+    live_slots = slots[slots >= 0]
+    serr = rel_l2(got[live_slots], cache_h[live_slots])
+    log(f"  outputs rel-L2 {err:.3e}, states rel-Frobenius {serr:.3e}")
+    assert err <= tol_out and serr <= STATE_TOL
+    others = np.setdiff1d(np.arange(w.num_slots), live_slots)
+    assert np.array_equal(got[others].view(np.uint32), w.cache[others].view(np.uint32))
+    for b in range(w.B):
+        if slots[b] < 0:
+            rows = np.arange(w.cu_seqlens[b], w.cu_seqlens[b + 1])
+            if out.dtype == torch.float32:
+                assert np.all(bits(out)[rows] == SENTINEL_BITS), b
+    if ckpt is not None:
+        ck = ckpt.cpu().numpy()
+        for b in range(w.B):
+            if slots[b] >= 0 and pos[b] >= 0:
+                assert rel_l2(ck[b], ref_ckpt[b]) <= STATE_TOL, b
+            else:
+                assert np.all(bits(ckpt)[b] == SENTINEL_BITS), b
+    return ref_out
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (64, 128), (128, 64)])
+def test_chunked_prefill_matches_oracle(dk, dv):
+    seqlens = [40, 1, 77, 0, 16, 33, 5, 32, 64, 130]
+    w = synth.make(len(seqlens), 4, dk, dv, seqlens=seqlens, num_slots=13, state_std=0.05, seed=71)
+    slots = w.slot_ids.copy()
+    slots[6] = -1                                   # padding row with tokens
+    pos = np.array([13, 1, 77, 0, -1, 32, 2, 32, 31, 97], np.int32)
+    cache_d = f32(w.cache)
+    log(f"chunked prefill dk={dk} dv={dv}")
+    out, ckpt = _run(w, cache_d, slots=slots, pos=pos)
+    torch.cuda.synchronize()
+    _check(w, slots, pos, out, ckpt, cache_d)
+
+
+def test_chunked_prefill_without_checkpoints_and_against_recurrent_form():
+    seqlens = [300, 31, 65]
+    w = synth.make(3, 8, 128, 128, seqlens=seqlens, num_slots=4, state_std=0.05, seed=72)
+    cache_c, cache_r = f32(w.cache), f32(w.cache)
+    log("chunked vs recurrent prefill")
+    out_c, _ = _run(w, cache_c)
+    out_r, _ = _run(w, cache_r, chunked=False)
+    torch.cuda.synchronize()
+    assert rel_l2(out_c.cpu().numpy(), out_r.cpu().numpy()) <= 1e-5
+    assert rel_l2(cache_c.cpu().numpy(), cache_r.cpu().numpy()) <= 1e-5
+    _check(w, w.slot_ids, np.full(3, -1, np.int32), out_c, None, cache_c)
+
+
+def test_chunked_prefill_8k_prompt_checkpoint_at_7680():
+    w = synth.make_workload("prefill_8k")
+    pos = np.array([7680], np.int32)
+    cache_d = f32(w.cache)
+    log("chunked prefill 8000 tokens, checkpoint at 7680")
+    out, ckpt = _run(w, cache_d, pos=pos)
+    torch.cuda.synchronize()
+    ref_out = _check(w, w.slot_ids, pos, out, ckpt, cache_d)
+    o = out.cpu().numpy()
+    worst = max(rel_l2(o[t], ref_out[t]) for t in range(0, w.n_tok, 97))
+    log(f"  worst sampled token rel-L2 {worst:.3e}")
+    assert worst <= OUT_TOL
+
+
+def test_chunked_prefill_extreme_decays():
+    """Decays down to ~1e-14 and up to 1 - 1e-7 inside one chunk: no division, no NaN."""
+    w = synth.make(2, 4, 128, 128, seqlens=[70, 45], num_slots=3, state_std=0.05, seed=73)
+    a_raw = (w.a_raw[0] * 8.0).astype(np.float64)
+    alpha = np.exp(-np.logaddexp(0.0, a_raw)).astype(np.float32)
+    x = step_inputs(w, 0)
+    x["alpha"] = f32(alpha)
+    cache_d = f32(w.cache)
+    pos = np.array([33, 45], np.int32)
+    log(f"chunked prefill, alpha in [{alpha.min():.1e}, {alpha.max():.7f}]")
+    out, ckpt = _run(w, cache_d, pos=pos, x=x)
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(out.cpu().numpy())) and np.all(np.isfinite(cache_d.cpu().numpy()))
+    _check(w, w.slot_ids, pos, out, ckpt, cache_d, alpha=alpha)
+
+
+@pytest.mark.parametrize("raw,out_dtype", [(True, torch.float32), (False, torch.bfloat16), (True, torch.bfloat16)])
+def test_chunked_prefill_raw_inputs_and_bf16_output(raw, out_dtype):
+    w = synth.make(3, 4, 128, 128, seqlens=[50, 7, 96], num_slots=5, state_std=0.05, seed=74)
+    pos = np.array([20, 7, -1], np.int32)
+    cache_d = f32(w.cache)
+    log(f"chunked prefill raw={raw} out={out_dtype}")
+    out, ckpt = _run(w, cache_d, pos=pos, raw=raw, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    _check(w, w.slot_ids, pos, out, ckpt, cache_d, raw=raw,
+           tol_out=OUT_TOL if out_dtype == torch.float32 else 2.0 ** -8)
+    if out_dtype != torch.float32:
+        # the bf16 output is the rounded fp32 output of the same call
+        cache_f = f32(w.cache)
+        out_f, _ = _run(w, cache_f, pos=pos, raw=raw)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), synth.f32_to_bf16_bits(out_f.cpu().numpy()))
+
+
+def test_chunked_prefill_device_errors_and_empty_rows():
+    w = synth.make(4, 4, 128, 128, seqlens=[9, 40, 4, 0], num_slots=7, state_std=0.05, seed=75)
+    err = torch.zeros(1, dtype=torch.int32, device=dev())
+    cache_d = f32(w.cache)
+    slots = w.slot_ids.copy()
+    slots[2] = w.num_slots
+    pos = np.array([3, 41, 0, 0], np.int32)
+    log("chunked prefill device errors")
+    out, ckpt = _run(w, cache_d, slots=slots, pos=pos, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == K.KDA_DEVERR_SLOT | K.KDA_DEVERR_CKPT
+    got = cache_d.cpu().numpy()
+    assert np.array_equal(got[w.slot_ids[1]].view(np.uint32), w.cache[w.slot_ids[1]].view(np.uint32))
+    assert np.array_equal(got[w.slot_ids[3]].view(np.uint32), w.cache[w.slot_ids[3]].view(np.uint32))
+    rows1 = np.arange(w.cu_seqlens[1], w.cu_seqlens[2])
+    assert np.all(bits(out)[rows1] == SENTINEL_BITS)
+    ck = bits(ckpt)
+    assert np.array_equal(ck[3], w.cache[w.slot_ids[3]].view(np.uint32))   # empty row, checkpoint 0
+    assert np.all(ck[1] == SENTINEL_BITS) and np.all(ck[2] == SENTINEL_BITS)
+    cache_h = w.cache.copy()
+    okslots = slots.copy()
+    okslots[1] = okslots[2] = -1
+    ref_out, ref_ckpt, _ = oracle.prefill(cache_h, okslots, w.cu_seqlens, w.q[0], w.k[0], w.v[0], w.alpha[0],
+                                          w.beta[0], ckpt_pos=pos)
+    assert rel_l2(got[w.slot_ids[0]], cache_h[w.slot_ids[0]]) <= STATE_TOL
+    assert rel_l2(ckpt.cpu().numpy()[0], ref_ckpt[0]) <= STATE_TOL
+    # an empty call and a call with only a checkpoint before an empty prompt
+    e = synth.make(1, 4, 128, 128, seqlens=[0], num_slots=1, state_std=0.05, seed=76)
+    cache_e = f32(e.cache)
+    _, ck_e = _run(e, cache_e, pos=np.array([0], np.int32))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(ck_e)[0], e.cache[0].view(np.uint32))
+    assert np.array_equal(bits(cache_e), e.cache.view(np.uint32))
