@@ -49,7 +49,7 @@ template <int DK, int DV>
 struct ChunkWs {
   static constexpr int W = 0;               // [kCL][DK]  T [Gamma k]
   static constexpr int QD = W + kCL * DK;   // [kCL][DK]  Gamma q
-  static constexpr int KT = QD + kCL * DK;  // [DK][4][kCL / 4]  k_s R_s (decayed to the chunk end), by channel
+  static constexpr int KT = QD + kCL * DK;  // [kCL][DK]  k_s decayed to the chunk end
   static constexpr int U = KT + kCL * DK;   // [kCL][DV]  T v
   static constexpr int BM = U + kCL * DV;   // [kCL][4][kCL / 4]  B
   static constexpr int GL = BM + kCL * kCL; // [DK]  Gamma_L
@@ -57,10 +57,9 @@ struct ChunkWs {
   static_assert(FLOATS % 4 == 0, "float4 alignment of every (chunk, head)");
 };
 
-// [.][4][kCL / 4] layout of the KT and BM entries: element s of a row is at
+// BM rows are stored as [4][kCL / 4]: element s of a row sits at
 // (s % 4) * (kCL / 4) + s / 4, so the lane that feeds MFMA steps 0..7 with
 // entries g, 4 + g, ... reads two float4s.
-__device__ __forceinline__ int perm_col(int s) { return (s & 3) * (kCL / 4) + (s >> 2); }
 
 // Chunks of one row. nch = 0 for a row that does not run (padding, or any
 // device error; the state pass reports those).
@@ -108,9 +107,10 @@ __global__ __launch_bounds__(256) void prefill_chunk_prep_kernel(ChunkArgs a) {
   __shared__ float ab[kCL * DK];  // alpha, then [R k]
   __shared__ float vb[kCL * DV];
   __shared__ float bet[kCL];
-  __shared__ float Am[kCL * kCL];    // A (strictly lower)
-  __shared__ float Tm[kCL * kCL];    // T
-  __shared__ float bef[2 * DK];      // product of the sub-blocks before each sub-block
+  __shared__ float Am[kCL * kCL];          // A (strictly lower)
+  __shared__ float Tm[kCL * (kCL + 1)];    // T, rows padded by one float against bank conflicts
+  __shared__ float Bl[kCL * kCL];          // B, written out in one coalesced pass
+  __shared__ float bef[2 * DK];            // product of the sub-blocks before each sub-block
 
   const int c = blockIdx.x / a.H, h = blockIdx.x % a.H;
   // the row and chunk this workgroup prepares
@@ -127,30 +127,42 @@ __global__ __launch_bounds__(256) void prefill_chunk_prep_kernel(ChunkArgs a) {
   const int64_t row0 = (int64_t)a.cu[b] + t0;
   float *ws = a.ws + ((int64_t)c * a.H + h) * WS::FLOATS;
 
-  // stage the chunk; tokens past its end are k = q = v = 0, alpha = 1, beta = 0
-  for (int idx = threadIdx.x; idx < kCL * (DK / 4); idx += blockDim.x) {
-    const int t = idx / (DK / 4), i = (idx % (DK / 4)) * 4;
-    float4 kk = make_float4(0.0f, 0.0f, 0.0f, 0.0f), qq = kk, al = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+  // stage the chunk; tokens past its end are k = q = v = 0, alpha = 1, beta = 0.
+  // Every load is issued before the first LDS write.
+  constexpr int NK = kCL * (DK / 4) / 256, NVL = kCL * (DV / 4) / 256;
+  uint2 kr[NK], qr[NK], vr[NVL];
+  float4 ar[NK];
+#pragma unroll
+  for (int m = 0; m < NK; ++m) {
+    const int idx = threadIdx.x + 256 * m, t = idx / (DK / 4), i = (idx % (DK / 4)) * 4;
+    kr[m] = qr[m] = make_uint2(0u, 0u);
+    ar[m] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
     if (t < n) {
       const int64_t off = ((row0 + t) * a.H + h) * DK + i;
-      kk = unpack_bf16x4(*reinterpret_cast<const uint2 *>(a.k + off));
-      qq = unpack_bf16x4(*reinterpret_cast<const uint2 *>(a.q + off));
-      al = *reinterpret_cast<const float4 *>(a.alpha + off);
+      kr[m] = *reinterpret_cast<const uint2 *>(a.k + off);
+      qr[m] = *reinterpret_cast<const uint2 *>(a.q + off);
+      ar[m] = *reinterpret_cast<const float4 *>(a.alpha + off);
     }
-    *reinterpret_cast<float4 *>(kb + t * DK + i) = kk;
-    *reinterpret_cast<float4 *>(qb + t * DK + i) = qq;
-    *reinterpret_cast<float4 *>(ab + t * DK + i) = al;
   }
-  for (int idx = threadIdx.x; idx < kCL * DV; idx += blockDim.x) {
-    const int t = idx / DV, j = idx % DV;
-    vb[idx] = t < n ? bf16_to_f32(a.v[((row0 + t) * a.H + h) * DV + j]) : 0.0f;
+#pragma unroll
+  for (int m = 0; m < NVL; ++m) {
+    const int idx = threadIdx.x + 256 * m, t = idx / (DV / 4), j = (idx % (DV / 4)) * 4;
+    vr[m] = make_uint2(0u, 0u);
+    if (t < n) vr[m] = *reinterpret_cast<const uint2 *>(a.v + ((row0 + t) * a.H + h) * DV + j);
+  }
+#pragma unroll
+  for (int m = 0; m < NK; ++m) {
+    const int idx = threadIdx.x + 256 * m, t = idx / (DK / 4), i = (idx % (DK / 4)) * 4;
+    *reinterpret_cast<float4 *>(kb + t * DK + i) = unpack_bf16x4(kr[m]);
+    *reinterpret_cast<float4 *>(qb + t * DK + i) = unpack_bf16x4(qr[m]);
+    *reinterpret_cast<float4 *>(ab + t * DK + i) = ar[m];
+  }
+#pragma unroll
+  for (int m = 0; m < NVL; ++m) {
+    const int idx = threadIdx.x + 256 * m, t = idx / (DV / 4), j = (idx % (DV / 4)) * 4;
+    *reinterpret_cast<float4 *>(vb + t * DV + j) = unpack_bf16x4(vr[m]);
   }
   if ((int)threadIdx.x < kCL) bet[threadIdx.x] = (int)threadIdx.x < n ? a.beta[(row0 + threadIdx.x) * a.H + h] : 0.0f;
-  // B above the diagonal is zero
-  for (int idx = threadIdx.x; idx < kCL * kCL; idx += blockDim.x) {
-    const int t = idx / kCL, s = idx % kCL;
-    if (s > t) ws[WS::BM + t * kCL + perm_col(s)] = 0.0f;
-  }
   __syncthreads();
   if (a.raw) {
     prep_staged<DK>(kb, qb, ab, bet, n);
@@ -158,37 +170,49 @@ __global__ __launch_bounds__(256) void prefill_chunk_prep_kernel(ChunkArgs a) {
   }
 
   // inside each sub-block: A and B by running products. Row (s, 16 lanes) carries
-  // D(t, s) over its lane's CPT channels as t advances and sums over the row.
+  // D(t, s) over its lane's CPT channels as t advances and sums over the row; both
+  // sub-blocks at once.
   {
     const int s = threadIdx.x >> 4, cl = threadIdx.x & 15;
+    float d0[CPT], d1[CPT];
+    float pd0 = 0.0f, pd1 = 0.0f;
 #pragma unroll
-    for (int J = 0; J < 2; ++J) {
-      const int sg = J * kSB + s;
-      float d[CPT];
-      float pd = 0.0f;
+    for (int e = 0; e < CPT; ++e) {
+      const int c0 = s * DK + cl * CPT + e, c1 = (kSB + s) * DK + cl * CPT + e;
+      d0[e] = kb[c0];
+      d1[e] = kb[c1];
+      pd0 = __builtin_fmaf(qb[c0], d0[e], pd0);
+      pd1 = __builtin_fmaf(qb[c1], d1[e], pd1);
+    }
+    pd0 = row16_sum(pd0);
+    pd1 = row16_sum(pd1);
+    if (cl == 0) {
+      Bl[s * kCL + s] = pd0;
+      Bl[(kSB + s) * kCL + kSB + s] = pd1;
+    }
+#pragma unroll
+    for (int t = 1; t < kSB; ++t) {
+      const bool after = t > s;  // D(t, s) starts at k_s and takes alpha_t only past s
+      float pa0 = 0.0f, pb0 = 0.0f, pa1 = 0.0f, pb1 = 0.0f;
 #pragma unroll
       for (int e = 0; e < CPT; ++e) {
-        d[e] = kb[sg * DK + cl * CPT + e];
-        pd = __builtin_fmaf(qb[sg * DK + cl * CPT + e], d[e], pd);
+        const int c0 = t * DK + cl * CPT + e, c1 = (kSB + t) * DK + cl * CPT + e;
+        d0[e] = after ? d0[e] * ab[c0] : d0[e];
+        d1[e] = after ? d1[e] * ab[c1] : d1[e];
+        pa0 = __builtin_fmaf(kb[c0], d0[e], pa0);
+        pb0 = __builtin_fmaf(qb[c0], d0[e], pb0);
+        pa1 = __builtin_fmaf(kb[c1], d1[e], pa1);
+        pb1 = __builtin_fmaf(qb[c1], d1[e], pb1);
       }
-      pd = row16_sum(pd);
-      if (cl == 0) ws[WS::BM + sg * kCL + perm_col(sg)] = pd;
-      for (int t = s + 1; t < kSB; ++t) {
-        const int tg = J * kSB + t;
-        float pa = 0.0f, pb = 0.0f;
-#pragma unroll
-        for (int e = 0; e < CPT; ++e) {
-          const int ch = tg * DK + cl * CPT + e;
-          d[e] = d[e] * ab[ch];
-          pa = __builtin_fmaf(kb[ch], d[e], pa);
-          pb = __builtin_fmaf(qb[ch], d[e], pb);
-        }
-        pa = row16_sum(pa);
-        pb = row16_sum(pb);
-        if (cl == 0) {
-          Am[tg * kCL + sg] = pa;
-          ws[WS::BM + tg * kCL + perm_col(sg)] = pb;
-        }
+      pa0 = row16_sum(pa0);
+      pb0 = row16_sum(pb0);
+      pa1 = row16_sum(pa1);
+      pb1 = row16_sum(pb1);
+      if (cl == 0 && after) {
+        Am[t * kCL + s] = pa0;
+        Bl[t * kCL + s] = pb0;
+        Am[(kSB + t) * kCL + kSB + s] = pa1;
+        Bl[(kSB + t) * kCL + kSB + s] = pb1;
       }
     }
   }
@@ -222,12 +246,13 @@ __global__ __launch_bounds__(256) void prefill_chunk_prep_kernel(ChunkArgs a) {
       R = R * ab[s * DK + i];
       ab[s * DK + i] = kr;
       kb[s * DK + i] = kf[s];
-      ws[WS::KT + i * kCL + perm_col(s)] = s < kSB ? kr * G1 : kr;
+      ws[WS::KT + s * DK + i] = s < kSB ? kr * G1 : kr;
     }
   }
   __syncthreads();
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
   // across the sub-blocks: A (wave 0) and B (wave 1) for t in block 1, s in block 0,
   // [P k]_t . [R k]_s and [P q]_t . [R k]_s over DK on MFMA
   if (wave < 2) {
@@ -250,52 +275,90 @@ __global__ __launch_bounds__(256) void prefill_chunk_prep_kernel(ChunkArgs a) {
       if (wave == 0)
         Am[t * kCL + m] = acc[e];
       else
-        ws[WS::BM + t * kCL + perm_col(m)] = acc[e];
+        Bl[t * kCL + m] = acc[e];
     }
   }
   __syncthreads();
+  // B to the workspace in its row layout, zero above the diagonal
+  for (int idx = threadIdx.x; idx < kCL * kCL; idx += blockDim.x) {
+    const int t = idx / kCL, pc = idx % kCL, s = (pc % (kCL / 4)) * 4 + pc / (kCL / 4);
+    ws[WS::BM + idx] = s > t ? 0.0f : Bl[t * kCL + s];
+  }
 
-  // T = (I + Diag(beta) A)^-1 Diag(beta), one column per thread by forward substitution
-  if ((int)threadIdx.x < kCL) {
-    const int col = threadIdx.x;
-    float x[kCL];
+  // X = (I + Diag(beta) A)^-1 by 16 x 16 blocks: the two diagonal blocks by forward
+  // substitution (one column per thread), then X10 = -X11 (Diag(beta) A)10 X00.
+  // T = X Diag(beta) goes to Tm.
+  if ((int)threadIdx.x < 2 * kSB) {
+    const int J = threadIdx.x / kSB, col = threadIdx.x % kSB, o = J * kSB;
+    float x[kSB];
 #pragma unroll
-    for (int t = 0; t < kCL; ++t) {
+    for (int t = 0; t < kSB; ++t) {
       float acc = 0.0f;
 #pragma unroll
-      for (int s = 0; s < t; ++s) acc = __builtin_fmaf(Am[t * kCL + s], x[s], acc);
-      x[t] = t == col ? 1.0f : (t < col ? 0.0f : -bet[t] * acc);
+      for (int s2 = 0; s2 < t; ++s2) acc = __builtin_fmaf(Am[(o + t) * kCL + o + s2], x[s2], acc);
+      x[t] = t == col ? 1.0f : (t < col ? 0.0f : -bet[o + t] * acc);
     }
-    const float bc = bet[col];
 #pragma unroll
-    for (int t = 0; t < kCL; ++t) Tm[t * kCL + col] = x[t] * bc;
+    for (int t = 0; t < kSB; ++t) Tm[(o + t) * (kCL + 1) + o + col] = x[t];
+  }
+  __syncthreads();
+  {
+    const int t = threadIdx.x / kSB, col = threadIdx.x % kSB;  // one (t, col) of the 16 x 16 block each
+    float y = 0.0f;
+#pragma unroll
+    for (int s2 = 0; s2 < kSB; ++s2) y = __builtin_fmaf(Am[(kSB + t) * kCL + s2], Tm[s2 * (kCL + 1) + col], y);
+    Bl[t * kSB + col] = bet[kSB + t] * y;  // (Diag(beta) A)10 X00; B is already in the workspace
+  }
+  __syncthreads();
+  {
+    const int t = threadIdx.x / kSB, col = threadIdx.x % kSB;
+    float x10 = 0.0f;
+#pragma unroll
+    for (int u2 = 0; u2 < kSB; ++u2)
+      x10 = __builtin_fmaf(Tm[(kSB + t) * (kCL + 1) + kSB + u2], Bl[u2 * kSB + col], x10);
+    Tm[(kSB + t) * (kCL + 1) + col] = -x10;
+    Tm[t * (kCL + 1) + kSB + col] = 0.0f;
+  }
+  __syncthreads();
+  // T = X Diag(beta)
+  for (int idx = threadIdx.x; idx < kCL * kCL; idx += blockDim.x) {
+    const int t = idx / kCL, col = idx % kCL;
+    Tm[t * (kCL + 1) + col] *= bet[col];
   }
   __syncthreads();
 
   // W = T [Gamma k] and U = T V: 16 x 16 output tiles spread over the waves
-  constexpr int TW = DK / 16, TU = DV / 16, NT = 2 * (TW + TU);
-  for (int tile = wave; tile < NT; tile += 4) {
-    const int rt = tile & 1;
-    int ct = tile >> 1;
-    const bool isU = ct >= TW;
-    if (isU) ct -= TW;
-    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  constexpr int TW = DK / 16, TU = DV / 16;
+  for (int tile = wave; tile < 2 * TW; tile += 4) {
+    const int rt = tile & 1, ct = tile >> 1;
+    float av[kCL / 4], bv[kCL / 4];
 #pragma unroll
     for (int ks = 0; ks < kCL / 4; ++ks) {
       const int tok = 4 * ks + g;
-      const float av = Tm[(16 * rt + m) * kCL + tok];
-      const float bv = isU ? vb[tok * DV + 16 * ct + m]
-                           : kb[tok * DK + 16 * ct + m] * bef[(tok >= kSB ? DK : 0) + 16 * ct + m];
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+      av[ks] = Tm[(16 * rt + m) * (kCL + 1) + tok];
+      // [Gamma k] = [P k] times the product of the earlier sub-blocks (one for block 0)
+      bv[ks] = ks < kSB / 4 ? kb[tok * DK + 16 * ct + m] : kb[tok * DK + 16 * ct + m] * bef[DK + 16 * ct + m];
     }
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 16 * rt + 4 * g + e;
-      if (isU)
-        ws[WS::U + row * DV + 16 * ct + m] = acc[e];
-      else
-        ws[WS::W + row * DK + 16 * ct + m] = acc[e];
+    for (int ks = 0; ks < kCL / 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[ks], bv[ks], acc, 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ws[WS::W + (16 * rt + 4 * g + e) * DK + 16 * ct + m] = acc[e];
+  }
+  for (int tile = wave; tile < 2 * TU; tile += 4) {
+    const int rt = tile & 1, ct = tile >> 1;
+    float av[kCL / 4], bv[kCL / 4];
+#pragma unroll
+    for (int ks = 0; ks < kCL / 4; ++ks) {
+      const int tok = 4 * ks + g;
+      av[ks] = Tm[(16 * rt + m) * (kCL + 1) + tok];
+      bv[ks] = vb[tok * DV + 16 * ct + m];
     }
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < kCL / 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[ks], bv[ks], acc, 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ws[WS::U + (16 * rt + 4 * g + e) * DV + 16 * ct + m] = acc[e];
   }
 }
 
@@ -315,12 +378,32 @@ __device__ __forceinline__ void put_chunk_out(const ChunkArgs &a, int64_t idx, f
     a.out[idx] = y;
 }
 
+template <class WS>
+__device__ __forceinline__ const float *chunk_ws(const ChunkArgs &a, int c, int h) {
+  return a.ws + ((int64_t)c * a.H + h) * WS::FLOATS;
+}
+
+// A operands of W S0 and [Gamma q] S0 for one chunk: lane (j, g) supplies token
+// 16 rt + j at channels coff + 16 ct .. + 3.
+template <class WS, int DK, int NCT>
+__device__ __forceinline__ void load_wq(const float *w, int j, int coff, float4 (&wv)[2][NCT],
+                                        float4 (&qv)[2][NCT]) {
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int off = (16 * rt + j) * DK + coff + 16 * ct;
+      wv[rt][ct] = *reinterpret_cast<const float4 *>(w + WS::W + off);
+      qv[rt][ct] = *reinterpret_cast<const float4 *>(w + WS::QD + off);
+    }
+}
+
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void prefill_chunk_state_kernel(ChunkArgs a) {
   using WS = ChunkWs<DK, DV>;
   constexpr int CPW = DK / 4;    // key channels per wave
   constexpr int NCT = CPW / 16;  // 16-channel tiles per wave
-  __shared__ float part[4][2][kCL][16];  // per wave: W S and [Gamma q] S over its channels
+  __shared__ float part[4][2][kCL][16];  // per wave: W S0 and [Gamma q] S0 over its channels
   __shared__ float dl[kCL][16];          // delta
   __shared__ float o0[kCL][16];          // [Gamma q] S0
 
@@ -350,7 +433,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_state_kernel(ChunkArgs a) {
   }
   if (r.nch == 0 && ck != 0) return;
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
   const int n0 = 16 * u.tile;
   const int coff = CPW * wave + 4 * g;  // first channel of this lane in tile 0
   float *S = a.cache + (int64_t)slot * a.slot_stride + ((int64_t)u.h * DV + n0 + j) * DK + coff;
@@ -363,10 +447,33 @@ __global__ __launch_bounds__(256) void prefill_chunk_state_kernel(ChunkArgs a) {
     for (int ct = 0; ct < NCT; ++ct) st4<kVerifyStoreStream>(CK + 16 * ct, s[ct]);
   }
 
+  // W and [Gamma q] of the next chunk are read while this one computes; the other
+  // operands of a chunk are issued before its first product. Past the last chunk the
+  // last one is read again, so every load is unconditional and each wait knows how
+  // many loads follow the ones it needs.
+  float4 wv[2][NCT], qv[2][NCT];
+  if (r.nch > 0) load_wq<WS, DK, NCT>(chunk_ws<WS>(a, cbase, u.h), j, coff, wv, qv);
   for (int jc = 0; jc < r.nch; ++jc) {
     int t0, n;
     chunk_tokens(r, jc, t0, n);
-    const float *w = a.ws + ((int64_t)(cbase + jc) * a.H + u.h) * WS::FLOATS;
+    const float *w = chunk_ws<WS>(a, cbase + jc, u.h);
+    float uu[kCL * 16 / 256];
+#pragma unroll
+    for (int k = 0; k < kCL * 16 / 256; ++k) {
+      const int idx = threadIdx.x + 256 * k;
+      uu[k] = w[WS::U + (idx >> 4) * DV + n0 + (idx & 15)];
+    }
+    const float *brow = w + WS::BM + (16 * (wave & 1) + j) * kCL + g * (kCL / 4);
+    const float4 b0 = *reinterpret_cast<const float4 *>(brow);
+    const float4 b1 = *reinterpret_cast<const float4 *>(brow + 4);
+    float kt[NCT][8];
+    float4 gl[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      gl[ct] = *reinterpret_cast<const float4 *>(w + WS::GL + coff + 16 * ct);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) kt[ct][ks] = w[WS::KT + (4 * ks + g) * DK + CPW * wave + 16 * ct + j];
+    }
 
     // W S0 and [Gamma q] S0 over this wave's channels
     v4f pd[2], po[2];
@@ -376,19 +483,17 @@ __global__ __launch_bounds__(256) void prefill_chunk_state_kernel(ChunkArgs a) {
       po[rt] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        const int off = (16 * rt + j) * DK + coff + 16 * ct;
-        const float4 wv = *reinterpret_cast<const float4 *>(w + WS::W + off);
-        const float4 qv = *reinterpret_cast<const float4 *>(w + WS::QD + off);
-        pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv.x, s[ct].x, pd[rt], 0, 0, 0);
-        po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv.x, s[ct].x, po[rt], 0, 0, 0);
-        pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv.y, s[ct].y, pd[rt], 0, 0, 0);
-        po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv.y, s[ct].y, po[rt], 0, 0, 0);
-        pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv.z, s[ct].z, pd[rt], 0, 0, 0);
-        po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv.z, s[ct].z, po[rt], 0, 0, 0);
-        pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv.w, s[ct].w, pd[rt], 0, 0, 0);
-        po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv.w, s[ct].w, po[rt], 0, 0, 0);
+        pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[rt][ct].x, s[ct].x, pd[rt], 0, 0, 0);
+        po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[rt][ct].x, s[ct].x, po[rt], 0, 0, 0);
+        pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[rt][ct].y, s[ct].y, pd[rt], 0, 0, 0);
+        po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[rt][ct].y, s[ct].y, po[rt], 0, 0, 0);
+        pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[rt][ct].z, s[ct].z, pd[rt], 0, 0, 0);
+        po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[rt][ct].z, s[ct].z, po[rt], 0, 0, 0);
+        pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[rt][ct].w, s[ct].w, pd[rt], 0, 0, 0);
+        po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[rt][ct].w, s[ct].w, po[rt], 0, 0, 0);
       }
     }
+    load_wq<WS, DK, NCT>(chunk_ws<WS>(a, cbase + min(jc + 1, r.nch - 1), u.h), j, coff, wv, qv);
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -399,11 +504,12 @@ __global__ __launch_bounds__(256) void prefill_chunk_state_kernel(ChunkArgs a) {
     __syncthreads();
 
     // delta = U - W S0, and [Gamma q] S0, summed over the waves in a fixed order
-    for (int idx = threadIdx.x; idx < kCL * 16; idx += blockDim.x) {
-      const int t = idx >> 4, col = idx & 15;
+#pragma unroll
+    for (int k = 0; k < kCL * 16 / 256; ++k) {
+      const int idx = threadIdx.x + 256 * k, t = idx >> 4, col = idx & 15;
       const float sd = ((part[0][0][t][col] + part[1][0][t][col]) + part[2][0][t][col]) + part[3][0][t][col];
       const float so = ((part[0][1][t][col] + part[1][1][t][col]) + part[2][1][t][col]) + part[3][1][t][col];
-      dl[t][col] = w[WS::U + t * DV + n0 + col] - sd;
+      dl[t][col] = uu[k] - sd;
       o0[t][col] = so;
     }
     __syncthreads();
@@ -413,9 +519,6 @@ __global__ __launch_bounds__(256) void prefill_chunk_state_kernel(ChunkArgs a) {
       const int rt = wave;
       v4f acc = {o0[16 * rt + 4 * g][j], o0[16 * rt + 4 * g + 1][j], o0[16 * rt + 4 * g + 2][j],
                  o0[16 * rt + 4 * g + 3][j]};
-      const float *brow = w + WS::BM + (16 * rt + j) * kCL + g * (kCL / 4);
-      const float4 b0 = *reinterpret_cast<const float4 *>(brow);
-      const float4 b1 = *reinterpret_cast<const float4 *>(brow + 4);
       const float bm[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bm[ks], dl[4 * ks + g][j], acc, 0, 0, 0);
@@ -430,14 +533,9 @@ __global__ __launch_bounds__(256) void prefill_chunk_state_kernel(ChunkArgs a) {
     // S0 <- Diag(Gamma_L) S0 + Kt^T delta over this wave's channels
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      const float4 gl = *reinterpret_cast<const float4 *>(w + WS::GL + coff + 16 * ct);
-      v4f acc = {s[ct].x * gl.x, s[ct].y * gl.y, s[ct].z * gl.z, s[ct].w * gl.w};
-      const float *krow = w + WS::KT + (CPW * wave + 16 * ct + j) * kCL + g * (kCL / 4);
-      const float4 k0 = *reinterpret_cast<const float4 *>(krow);
-      const float4 k1 = *reinterpret_cast<const float4 *>(krow + 4);
-      const float kt[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+      v4f acc = {s[ct].x * gl[ct].x, s[ct].y * gl[ct].y, s[ct].z * gl[ct].z, s[ct].w * gl[ct].w};
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[ks], dl[4 * ks + g][j], acc, 0, 0, 0);
+      for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[ct][ks], dl[4 * ks + g][j], acc, 0, 0, 0);
       s[ct] = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
     if (ck > 0 && t0 + n == ck) {
