@@ -98,19 +98,51 @@ __device__ __forceinline__ void chunk_tokens(const ChunkRow &r, int j, int &t0, 
 // Precompute, one workgroup per (chunk, head)
 // ----------------------------------------------------------------------------
 
+// Raw-input preparation of staged tokens [0, n) held at row pitch PK: the
+// engine's per-row routines on one 16-lane row per token.
+template <int DK, int PK>
+__device__ __forceinline__ void prep_rows(float *k, float *q, float *al, float *beta, int n) {
+  constexpr int NV = DK / 64;
+  const int rows = blockDim.x >> 4, r = threadIdx.x & 15;
+  for (int t = threadIdx.x >> 4; t < n; t += rows) {
+    float4 kk[NV], qq[NV], aa[NV];
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      const int i = t * PK + 4 * r + 64 * e;
+      kk[e] = *reinterpret_cast<const float4 *>(k + i);
+      qq[e] = *reinterpret_cast<const float4 *>(q + i);
+      aa[e] = *reinterpret_cast<const float4 *>(al + i);
+    }
+    prep_normalize<NV>(kk, 1.0f);
+    prep_normalize<NV>(qq, 1.0f / __builtin_sqrtf((float)DK));
+    prep_decay<NV>(aa);
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      const int i = t * PK + 4 * r + 64 * e;
+      *reinterpret_cast<float4 *>(k + i) = kk[e];
+      *reinterpret_cast<float4 *>(q + i) = qq[e];
+      *reinterpret_cast<float4 *>(al + i) = aa[e];
+    }
+    if (r == 0) beta[t] = prep_beta(beta[t]);
+  }
+}
+
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void prefill_chunk_prep_kernel(ChunkArgs a) {
   using WS = ChunkWs<DK, DV>;
   constexpr int CPT = DK / 16;  // channels per lane when a 16-lane row spans DK
-  __shared__ float kb[kCL * DK];  // k, then [P k]
-  __shared__ float qb[kCL * DK];  // q, then [P q]
-  __shared__ float ab[kCL * DK];  // alpha, then [R k]
+  // Rows of k, q and alpha are padded by 4 floats: the MFMA operand reads of 16
+  // rows at once then start 4 banks apart and cover every bank once per 8 lanes.
+  constexpr int PK = DK + 4;
+  __shared__ float kb[kCL * PK];  // k, then [P k]
+  __shared__ float qb[kCL * PK];  // q, then [P q]
+  __shared__ float ab[kCL * PK];  // alpha, then [R k]
   __shared__ float vb[kCL * DV];
   __shared__ float bet[kCL];
-  __shared__ float Am[kCL * kCL];          // A (strictly lower)
-  __shared__ float Tm[kCL * (kCL + 1)];    // T, rows padded by one float against bank conflicts
-  __shared__ float Bl[kCL * kCL];          // B, written out in one coalesced pass
-  __shared__ float bef[2 * DK];            // product of the sub-blocks before each sub-block
+  __shared__ float Am[kCL * kCL];        // A (strictly lower)
+  __shared__ float Tm[kCL * (kCL + 1)];  // T, rows padded by one float against bank conflicts
+  __shared__ float Bl[kCL * kCL];        // B, written out in one coalesced pass
+  __shared__ float gb[2 * DK];           // product of each sub-block's decays
 
   const int c = blockIdx.x / a.H, h = blockIdx.x % a.H;
   // the row and chunk this workgroup prepares
@@ -150,35 +182,35 @@ __global__ __launch_bounds__(256) void prefill_chunk_prep_kernel(ChunkArgs a) {
     vr[m] = make_uint2(0u, 0u);
     if (t < n) vr[m] = *reinterpret_cast<const uint2 *>(a.v + ((row0 + t) * a.H + h) * DV + j);
   }
+  if ((int)threadIdx.x < kCL) bet[threadIdx.x] = (int)threadIdx.x < n ? a.beta[(row0 + threadIdx.x) * a.H + h] : 0.0f;
 #pragma unroll
   for (int m = 0; m < NK; ++m) {
     const int idx = threadIdx.x + 256 * m, t = idx / (DK / 4), i = (idx % (DK / 4)) * 4;
-    *reinterpret_cast<float4 *>(kb + t * DK + i) = unpack_bf16x4(kr[m]);
-    *reinterpret_cast<float4 *>(qb + t * DK + i) = unpack_bf16x4(qr[m]);
-    *reinterpret_cast<float4 *>(ab + t * DK + i) = ar[m];
+    *reinterpret_cast<float4 *>(kb + t * PK + i) = unpack_bf16x4(kr[m]);
+    *reinterpret_cast<float4 *>(qb + t * PK + i) = unpack_bf16x4(qr[m]);
+    *reinterpret_cast<float4 *>(ab + t * PK + i) = ar[m];
   }
 #pragma unroll
   for (int m = 0; m < NVL; ++m) {
     const int idx = threadIdx.x + 256 * m, t = idx / (DV / 4), j = (idx % (DV / 4)) * 4;
     *reinterpret_cast<float4 *>(vb + t * DV + j) = unpack_bf16x4(vr[m]);
   }
-  if ((int)threadIdx.x < kCL) bet[threadIdx.x] = (int)threadIdx.x < n ? a.beta[(row0 + threadIdx.x) * a.H + h] : 0.0f;
   __syncthreads();
   if (a.raw) {
-    prep_staged<DK>(kb, qb, ab, bet, n);
+    prep_rows<DK, PK>(kb, qb, ab, bet, n);
     __syncthreads();
   }
 
   // inside each sub-block: A and B by running products. Row (s, 16 lanes) carries
-  // D(t, s) over its lane's CPT channels as t advances and sums over the row; both
-  // sub-blocks at once.
+  // D(t, s) over its lane's channels cl + 16 e as t advances and sums over the row;
+  // both sub-blocks at once.
   {
     const int s = threadIdx.x >> 4, cl = threadIdx.x & 15;
     float d0[CPT], d1[CPT];
     float pd0 = 0.0f, pd1 = 0.0f;
 #pragma unroll
     for (int e = 0; e < CPT; ++e) {
-      const int c0 = s * DK + cl * CPT + e, c1 = (kSB + s) * DK + cl * CPT + e;
+      const int c0 = s * PK + cl + 16 * e, c1 = (kSB + s) * PK + cl + 16 * e;
       d0[e] = kb[c0];
       d1[e] = kb[c1];
       pd0 = __builtin_fmaf(qb[c0], d0[e], pd0);
@@ -196,7 +228,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_prep_kernel(ChunkArgs a) {
       float pa0 = 0.0f, pb0 = 0.0f, pa1 = 0.0f, pb1 = 0.0f;
 #pragma unroll
       for (int e = 0; e < CPT; ++e) {
-        const int c0 = t * DK + cl * CPT + e, c1 = (kSB + t) * DK + cl * CPT + e;
+        const int c0 = t * PK + cl + 16 * e, c1 = (kSB + t) * PK + cl + 16 * e;
         d0[e] = after ? d0[e] * ab[c0] : d0[e];
         d1[e] = after ? d1[e] * ab[c1] : d1[e];
         pa0 = __builtin_fmaf(kb[c0], d0[e], pa0);
@@ -218,46 +250,49 @@ __global__ __launch_bounds__(256) void prefill_chunk_prep_kernel(ChunkArgs a) {
   }
   __syncthreads();
 
-  // per key channel: [P k] and [P q] in place of k and q, [R k] in place of alpha,
-  // Gamma q and the keys decayed to the chunk end to the workspace
-  if ((int)threadIdx.x < DK) {
-    const int i = threadIdx.x;
-    float kf[kCL];
-    float P = 1.0f, G0 = 1.0f, G1 = 1.0f;
+  // per (key channel, sub-block), all threads: [P k] and [P q] in place of k and q and
+  // [R k] in place of alpha, for the thread's own sub-block
+  {
+    const int i = threadIdx.x % DK, J = threadIdx.x / DK;  // DK = 128: J in {0, 1}; DK = 64: J in 0..3
+    if (J < 2) {
+      const int o = J * kSB;
+      float kf[kSB];
+      float P = 1.0f;
 #pragma unroll
-    for (int t = 0; t < kCL; ++t) {
-      if (t == kSB) P = 1.0f;
-      P = P * ab[t * DK + i];
-      kf[t] = kb[t * DK + i] * P;
-      qb[t * DK + i] = qb[t * DK + i] * P;
-      if (t == kSB - 1) G0 = P;
-      if (t == kCL - 1) G1 = P;
-    }
-    bef[i] = 1.0f;
-    bef[DK + i] = G0;
-    ws[WS::GL + i] = G0 * G1;
+      for (int t = 0; t < kSB; ++t) {
+        P = P * ab[(o + t) * PK + i];
+        kf[t] = kb[(o + t) * PK + i] * P;
+        qb[(o + t) * PK + i] = qb[(o + t) * PK + i] * P;
+      }
+      gb[J * DK + i] = P;
+      float R = 1.0f;
 #pragma unroll
-    for (int t = 0; t < kCL; ++t) ws[WS::QD + t * DK + i] = t < kSB ? qb[t * DK + i] : qb[t * DK + i] * G0;
-    float R = 1.0f;
-#pragma unroll
-    for (int s = kCL - 1; s >= 0; --s) {
-      if (s == kSB - 1) R = 1.0f;
-      const float kr = kb[s * DK + i] * R;
-      R = R * ab[s * DK + i];
-      ab[s * DK + i] = kr;
-      kb[s * DK + i] = kf[s];
-      ws[WS::KT + s * DK + i] = s < kSB ? kr * G1 : kr;
+      for (int t = kSB - 1; t >= 0; --t) {
+        const float kr2 = kb[(o + t) * PK + i] * R;
+        R = R * ab[(o + t) * PK + i];
+        ab[(o + t) * PK + i] = kr2;
+        kb[(o + t) * PK + i] = kf[t];
+      }
     }
   }
   __syncthreads();
+  // Gamma q = [P q] x (earlier sub-blocks), keys decayed to the chunk end = [R k] x
+  // (later sub-blocks), Gamma_L, to the workspace in coalesced rows
+  for (int idx = threadIdx.x; idx < kCL * DK; idx += blockDim.x) {
+    const int t = idx / DK, i = idx % DK;
+    const float qf = qb[t * PK + i], kt = ab[t * PK + i];
+    ws[WS::QD + idx] = t < kSB ? qf : qf * gb[i];
+    ws[WS::KT + idx] = t < kSB ? kt * gb[DK + i] : kt;
+  }
+  if ((int)threadIdx.x < DK) ws[WS::GL + threadIdx.x] = gb[threadIdx.x] * gb[DK + threadIdx.x];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
   // across the sub-blocks: A (wave 0) and B (wave 1) for t in block 1, s in block 0,
   // [P k]_t . [R k]_s and [P q]_t . [R k]_s over DK on MFMA
   if (wave < 2) {
-    const float *arow = (wave == 0 ? kb : qb) + (kSB + m) * DK;  // A operand: row t = kSB + m
-    const float *brow = ab + m * DK;                             // B operand: column s = m
+    const float *arow = (wave == 0 ? kb : qb) + (kSB + m) * PK;  // A operand: row t = kSB + m
+    const float *brow = ab + m * PK;                             // B operand: column s = m
     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int cb = 0; cb < DK / 16; ++cb) {
@@ -337,7 +372,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_prep_kernel(ChunkArgs a) {
       const int tok = 4 * ks + g;
       av[ks] = Tm[(16 * rt + m) * (kCL + 1) + tok];
       // [Gamma k] = [P k] times the product of the earlier sub-blocks (one for block 0)
-      bv[ks] = ks < kSB / 4 ? kb[tok * DK + 16 * ct + m] : kb[tok * DK + 16 * ct + m] * bef[DK + 16 * ct + m];
+      bv[ks] = ks < kSB / 4 ? kb[tok * PK + 16 * ct + m] : kb[tok * PK + 16 * ct + m] * gb[16 * ct + m];
     }
     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
