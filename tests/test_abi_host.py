@@ -53,7 +53,9 @@ def test_query_variant_launch_shapes():
     assert q(1, 32, 128, 128) == (16, 256)          # 256 workgroups
     assert q(2, 32, 128, 128) == (32, 256)
     assert q(4, 32, 128, 128) == (64, 256)
-    assert q(16, 32, 128, 128) == (64, 256)         # 1024 workgroups
+    assert q(16, 32, 128, 128) == (128, 256)        # 512 heads: two 128-column workgroups per CU
+    assert q(12, 32, 128, 128) == (64, 256)         # 768 workgroups
+    assert q(32, 16, 128, 128) == (128, 256) and q(8, 64, 128, 128) == (128, 256)
     assert q(32, 32, 128, 128) == (4, 64)
     assert q(64, 32, 128, 128) == (4, 64)           # 32768 one-wave workgroups
     assert q(1, 4, 64, 64) == (16, 256)
