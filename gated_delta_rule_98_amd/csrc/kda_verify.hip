@@ -51,6 +51,10 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
   const Lane L = lane_geometry();
   const int W = C * L.slab;
   Staged<DK> st(reinterpret_cast<float *>(lds_dyn), a.T_max, W);
+  // the state tile is requested first, so its HBM latency overlaps the staging
+  float *S = a.cache + (int64_t)slot * a.slot_stride + ((int64_t)u.h * a.dv + (int64_t)u.tile * W) * DK;
+  float4 s[C][NV];
+  load_tile<DK, C, kVerifyLoadStream>(s, S, L);
 
   // stage the chunk's inputs; in replay mode also copy them to the buffer
   for (int idx = threadIdx.x; idx < Tb * (DK / 4); idx += blockDim.x) {
@@ -86,9 +90,6 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
     __syncthreads();
   }
 
-  float *S = a.cache + (int64_t)slot * a.slot_stride + ((int64_t)u.h * a.dv + (int64_t)u.tile * W) * DK;
-  float4 s[C][NV];
-  load_tile<DK, C, kVerifyLoadStream>(s, S, L);
   __shared__ float part[GATE ? kMaxT * kMaxWaves : 1];
   __shared__ float raw[GATE ? kMaxT * kMaxDv : 1];
 
@@ -177,6 +178,10 @@ __global__ __launch_bounds__(256) void commit_replay_kernel(Args a) {
   const Lane L = lane_geometry();
   const int W = C * L.slab;
   Staged<DK> st(reinterpret_cast<float *>(lds_dyn), a.T_max, W);
+  // the state tile is requested first, so its HBM latency overlaps the staging
+  float *S = a.cache + (int64_t)slot * a.slot_stride + ((int64_t)u.h * a.dv + (int64_t)u.tile * W) * DK;
+  float4 s[C][NV];
+  load_tile<DK, C, kCommitLoadStream>(s, S, L);
   for (int idx = threadIdx.x; idx < n * (DK / 4); idx += blockDim.x) {
     const int t = idx / (DK / 4), i = (idx % (DK / 4)) * 4;
     const int64_t d = (((int64_t)u.b * a.T_max + t) * a.H + u.h) * DK + i;
@@ -194,9 +199,6 @@ __global__ __launch_bounds__(256) void commit_replay_kernel(Args a) {
     __syncthreads();
   }
 
-  float *S = a.cache + (int64_t)slot * a.slot_stride + ((int64_t)u.h * a.dv + (int64_t)u.tile * W) * DK;
-  float4 s[C][NV];
-  load_tile<DK, C, kCommitLoadStream>(s, S, L);
   for (int t = 0; t < n; ++t) {
     float4 kk[NV], aa[NV];
 #pragma unroll
