@@ -295,6 +295,23 @@ __device__ __forceinline__ Unit unit_of_block(int ntile, int H) {
   return r;
 }
 
+// For kernels whose rows carry unequal work (varying token counts, rows that
+// skip): deal the (row, head) groups out to the XCDs in turn, so every XCD gets
+// an equal share of each row while a group's tiles still share one L2. Needs a
+// multiple of 8 groups; other counts use the contiguous numbering above.
+__device__ __forceinline__ Unit unit_of_block_rows(int ntile, int H, int B) {
+  const int G = B * H;
+  if (G & 7) return unit_of_block(ntile, H);
+  const int n = blockIdx.x;
+  const int local = n >> 3;
+  const int g = ((local / ntile) << 3) | (n & 7);
+  Unit r;
+  r.tile = local % ntile;
+  r.h = g % H;
+  r.b = g / H;
+  return r;
+}
+
 struct Lane {
   int r;     // position in the 16-lane row: key channels 4r..4r+3 (+ 64)
   int col0;  // tile-local value column of slab 0

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(Args a) {
   constexpr bool RAW = IO & kIoRaw, BF16 = IO & kIoBf16;
   constexpr int W = 16 * C;  // 4 waves x 4 columns x C slabs
   extern __shared__ float4 lds_dyn[];
-  const Unit u = unit_of_block(a.ntile, a.H);
+  const Unit u = unit_of_block_rows(a.ntile, a.H, a.B);
   const int32_t slot = a.slot_ids[u.b];
   if (slot < 0) return;
   if (slot >= a.num_slots) {

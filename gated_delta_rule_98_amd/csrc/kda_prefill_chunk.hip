@@ -442,7 +442,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_state_kernel(ChunkArgs a) {
   __shared__ float dl[kCL][16];          // delta
   __shared__ float o0[kCL][16];          // [Gamma q] S0
 
-  const Unit u = unit_of_block(a.ntile, a.H);
+  const Unit u = unit_of_block_rows(a.ntile, a.H, a.B);
   const int32_t slot = a.slot_ids[u.b];
   if (slot < 0) return;
   if (slot >= a.num_slots) {

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
   constexpr int NV = DK / 64;
   constexpr bool RAW = IO & kIoRaw, BF16 = IO & kIoBf16;
   extern __shared__ float4 lds_dyn[];
-  const Unit u = unit_of_block(a.ntile, a.H);
+  const Unit u = unit_of_block_rows(a.ntile, a.H, a.B);
   const int32_t slot = a.slot_ids[u.b];
   if (slot < 0) return;
   if (slot >= a.num_slots) {
@@ -171,7 +171,7 @@ template <int DK, int C>
 __global__ __launch_bounds__(256) void commit_replay_kernel(Args a) {
   constexpr int NV = DK / 64;
   extern __shared__ float4 lds_dyn[];
-  const Unit u = unit_of_block(a.ntile, a.H);
+  const Unit u = unit_of_block_rows(a.ntile, a.H, a.B);
   int32_t slot;
   const int n = commit_row(a, u, slot);
   if (n <= 0) return;
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256) void commit_replay_kernel(Args a) {
 template <int DK, int C>
 __global__ __launch_bounds__(256) void commit_copy_kernel(Args a) {
   constexpr int NV = DK / 64;
-  const Unit u = unit_of_block(a.ntile, a.H);
+  const Unit u = unit_of_block_rows(a.ntile, a.H, a.B);
   int32_t slot;
   const int n = commit_row(a, u, slot);
   if (n <= 0) return;

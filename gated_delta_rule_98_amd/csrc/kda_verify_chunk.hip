@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void verify_chunk_kernel(Args a) {
   constexpr int NCB = DK / 16;  // 16-channel blocks
   constexpr int CPT = DK / 16;  // channels per thread in the coupling pass
   extern __shared__ float4 lds_dyn[];
-  const Unit u = unit_of_block(a.ntile, a.H);
+  const Unit u = unit_of_block_rows(a.ntile, a.H, a.B);
   const int32_t slot = a.slot_ids[u.b];
   if (slot < 0) return;
   if (slot >= a.num_slots) {
