@@ -113,7 +113,7 @@ int launch(Kind kind, bool gate, int dk, const Launch &l, int64_t units, size_t 
   const void *fn = nullptr;
   switch (kind) {
     case KIND_DECODE: fn = decode_kernel_for(dk, l.C, gate, io); break;
-    case KIND_VERIFY: fn = verify_kernel_for(dk, l.C, gate, io); break;
+    case KIND_VERIFY: fn = verify_kernel_for(dk, l.C, gate, io, a.mode == KDA_PER_POSITION); break;
     case KIND_COMMIT_REPLAY: fn = gate ? nullptr : commit_replay_kernel_for(dk, l.C); break;
     case KIND_COMMIT_COPY: fn = gate ? nullptr : commit_copy_kernel_for(dk, l.C); break;
     case KIND_PREFILL: fn = gate ? nullptr : prefill_kernel_for(dk, l.C, io); break;

@@ -242,10 +242,11 @@ __device__ __forceinline__ void prep_decay(float4 (&a)[NV]) {
 
 __device__ __forceinline__ float prep_beta(float b) { return prep_sigmoid_neg(-b); }
 
-// In-place preparation of tokens [0, n) staged in LDS as float [t][DK] for k,
-// alpha (and q when non-null) and beta [t]: one 16-lane row per token. Must be
+// In-place preparation of tokens [0, n) staged in LDS as float [t][STRIDE]
+// (first DK used) for k, alpha (and q when non-null) and beta [t]: one 16-lane
+// row per token. Must be
 // reached by the whole workgroup between two barriers.
-template <int DK>
+template <int DK, int STRIDE = DK>
 __device__ __forceinline__ void prep_staged(float *k, float *q, float *al, float *beta, int n) {
   constexpr int NV = DK / 64;
   const int rows = blockDim.x >> 4, r = threadIdx.x & 15;
@@ -253,7 +254,7 @@ __device__ __forceinline__ void prep_staged(float *k, float *q, float *al, float
     float4 kk[NV], qq[NV], aa[NV];
 #pragma unroll
     for (int e = 0; e < NV; ++e) {
-      const int i = t * DK + 4 * r + 64 * e;
+      const int i = t * STRIDE + 4 * r + 64 * e;
       kk[e] = *reinterpret_cast<const float4 *>(k + i);
       aa[e] = *reinterpret_cast<const float4 *>(al + i);
       if (q) qq[e] = *reinterpret_cast<const float4 *>(q + i);
@@ -263,7 +264,7 @@ __device__ __forceinline__ void prep_staged(float *k, float *q, float *al, float
     if (q) prep_normalize<NV>(qq, 1.0f / __builtin_sqrtf((float)DK));
 #pragma unroll
     for (int e = 0; e < NV; ++e) {
-      const int i = t * DK + 4 * r + 64 * e;
+      const int i = t * STRIDE + 4 * r + 64 * e;
       *reinterpret_cast<float4 *>(k + i) = kk[e];
       *reinterpret_cast<float4 *>(al + i) = aa[e];
       if (q) *reinterpret_cast<float4 *>(q + i) = qq[e];
@@ -280,6 +281,27 @@ struct Unit {
   int b, h, tile;
 };
 
+// x / d and x % d for a uniform d: shifts when d is a power of two (tile counts
+// always are, head counts usually), so the unit numbering stays on the scalar
+// unit instead of an emulated division in vector registers.
+__device__ __forceinline__ void divmod_uniform(int x, int d, int &q, int &m) {
+  if ((d & (d - 1)) == 0) {
+    q = x >> __builtin_ctz(d);
+    m = x & (d - 1);
+  } else {
+    q = x / d;
+    m = x - q * d;
+  }
+}
+
+__device__ __forceinline__ Unit unit_of_index(int u, int ntile, int H) {
+  Unit r;
+  int bh;
+  divmod_uniform(u, ntile, bh, r.tile);
+  divmod_uniform(bh, H, r.b, r.h);
+  return r;
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup n runs on
 // XCD n % 8). Renumber them so each XCD gets a contiguous range of units: the
 // tiles of one head then share their L2 for the head's k, q, alpha and beta.
@@ -287,12 +309,7 @@ __device__ __forceinline__ Unit unit_of_block(int ntile, int H) {
   const int n = blockIdx.x, N = gridDim.x;
   const int xcd = n & 7, local = n >> 3, per = N >> 3, rem = N & 7;
   const int u = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
-  Unit r;
-  r.tile = u % ntile;
-  const int bh = u / ntile;
-  r.h = bh % H;
-  r.b = bh / H;
-  return r;
+  return unit_of_index(u, ntile, H);
 }
 
 // For kernels whose rows carry unequal work (varying token counts, rows that
@@ -300,15 +317,12 @@ __device__ __forceinline__ Unit unit_of_block(int ntile, int H) {
 // an equal share of each row while a group's tiles still share one L2. Needs a
 // multiple of 8 groups; other counts use the contiguous numbering above.
 __device__ __forceinline__ Unit unit_of_block_rows(int ntile, int H, int B) {
-  const int G = B * H;
-  if (G & 7) return unit_of_block(ntile, H);
+  if ((B * H) & 7) return unit_of_block(ntile, H);
   const int n = blockIdx.x;
-  const int local = n >> 3;
-  const int g = ((local / ntile) << 3) | (n & 7);
-  Unit r;
-  r.tile = local % ntile;
-  r.h = g % H;
-  r.b = g / H;
+  int j, tile;
+  divmod_uniform(n >> 3, ntile, j, tile);
+  Unit r = unit_of_index((j << 3) | (n & 7), 1, H);
+  r.tile = tile;
   return r;
 }
 
@@ -491,7 +505,7 @@ const void *io_variant(int io) {
 }
 
 const void *decode_kernel_for(int dk, int C, bool gate, int io);    // kda_decode.hip
-const void *verify_kernel_for(int dk, int C, bool gate, int io);    // kda_verify.hip
+const void *verify_kernel_for(int dk, int C, bool gate, int io, bool perpos);  // kda_verify.hip
 const void *commit_replay_kernel_for(int dk, int C);                // kda_verify.hip
 const void *commit_copy_kernel_for(int dk, int C);                  // kda_verify.hip
 const void *verify_chunk_kernel_for(int dk);                        // kda_verify_chunk.hip

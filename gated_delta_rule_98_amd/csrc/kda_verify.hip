@@ -6,27 +6,74 @@
 namespace kda {
 namespace {
 
-// LDS staging for a chunk of tokens: k, q, alpha as float [T_max][DK], the
-// tile's v as float [T_max][W], beta [T_max], and with the output gate the
-// tile's gate as float [T_max][W].
+// LDS staging for a chunk of tokens. Each token's k, alpha and q sit in one
+// record of 3 * DK floats, so a lane reaches all three from one pointer with
+// constant offsets and moves to the next token with one add. The tile's v is
+// [T_max][W] with each lane's C columns side by side (column col0 + c * slab
+// at col0 * C + c), beta is [T_max], and with the output gate the tile's gate
+// is [T_max][W] in column order.
 template <int DK>
 struct Staged {
-  float *k, *q, *a, *v, *beta, *g;
+  static constexpr int kRec = 3 * DK;
+  float *rec, *v, *beta, *g;
   __device__ Staged(float *base, int T_max, int W) {
-    k = base;
-    q = k + T_max * DK;
-    a = q + T_max * DK;
-    v = a + T_max * DK;
+    rec = base;
+    v = rec + T_max * kRec;
     beta = v + T_max * W;
     g = beta + T_max;
   }
+  __device__ float *k(int t) const { return rec + t * kRec; }
+  __device__ float *a(int t) const { return rec + t * kRec + DK; }
+  __device__ float *q(int t) const { return rec + t * kRec + 2 * DK; }
 };
 
+// Position of tile column jj in the staged v: the lane owning it reads its C
+// columns as one vector.
+template <int C>
+__device__ __forceinline__ int v_slot(int jj, int slab) {
+  return (jj % slab) * C + jj / slab;
+}
+
+// LDS pointers in the local address space: the token loops step them with
+// plain 32-bit adds and reach k, alpha and q through constant offsets.
+typedef __attribute__((address_space(3))) const float lds_float;
+typedef float lds_v2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ lds_float *to_lds(const float *p) { return (lds_float *)p; }
+__device__ __forceinline__ float4 lds_f4(lds_float *p) {
+  const v4f x = *(__attribute__((address_space(3))) const v4f *)p;
+  return make_float4(x.x, x.y, x.z, x.w);
+}
+
+// The C staged v values of this lane's columns for one token.
+template <int C>
+__device__ __forceinline__ void load_v(lds_float *p, float (&vj)[C]) {
+  if constexpr (C % 4 == 0) {
+#pragma unroll
+    for (int c = 0; c < C; c += 4) {
+      const float4 x = lds_f4(p + c);
+      vj[c] = x.x;
+      vj[c + 1] = x.y;
+      vj[c + 2] = x.z;
+      vj[c + 3] = x.w;
+    }
+  } else if constexpr (C == 2) {
+    const lds_v2 x = *(__attribute__((address_space(3))) const lds_v2 *)p;
+    vj[0] = x.x;
+    vj[1] = x.y;
+  } else {
+#pragma unroll
+    for (int c = 0; c < C; ++c) vj[c] = p[c];
+  }
+}
 
 // Speculative verify over a packed chunk: T_b tokens with the state in
 // registers; outputs per token; the committed slot stays untouched unless the
-// row is a single in-place token.
-template <int DK, int C, bool GATE, int IO>
+// row is a single in-place token. Lane r of each 16-lane row keeps token r's
+// outputs (the row's read-outs are equal in all its lanes), so outputs, and
+// the gate, are written once after the token loop. PERPOS instantiates the
+// per-position mode (each mode's loop alone keeps the register count down).
+template <int DK, int C, bool GATE, int IO, bool PERPOS>
 __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
   constexpr int NV = DK / 64;
   constexpr bool RAW = IO & kIoRaw, BF16 = IO & kIoBf16;
@@ -46,8 +93,7 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
   }
   if (Tb == 0) return;
   const bool inplace = Tb == 1 && a.t1_inplace;
-  const bool replay = !inplace && a.mode == KDA_REPLAY;
-  const bool perpos = !inplace && a.mode == KDA_PER_POSITION;
+  const bool replay = !inplace && !PERPOS;
   const Lane L = lane_geometry();
   const int W = C * L.slab;
   Staged<DK> st(reinterpret_cast<float *>(lds_dyn), a.T_max, W);
@@ -63,9 +109,9 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
     const uint2 kb = *reinterpret_cast<const uint2 *>(a.k + off);
     const uint2 qb = *reinterpret_cast<const uint2 *>(a.q + off);
     const float4 al = *reinterpret_cast<const float4 *>(a.alpha + off);
-    *reinterpret_cast<float4 *>(st.k + t * DK + i) = unpack_bf16x4(kb);
-    *reinterpret_cast<float4 *>(st.q + t * DK + i) = unpack_bf16x4(qb);
-    *reinterpret_cast<float4 *>(st.a + t * DK + i) = al;
+    *reinterpret_cast<float4 *>(st.k(t) + i) = unpack_bf16x4(kb);
+    *reinterpret_cast<float4 *>(st.q(t) + i) = unpack_bf16x4(qb);
+    *reinterpret_cast<float4 *>(st.a(t) + i) = al;
     if (replay && u.tile == 0) {
       const int64_t d = (((int64_t)u.b * a.T_max + t) * a.H + u.h) * DK + i;
       *reinterpret_cast<uint2 *>(a.rk + d) = kb;
@@ -75,7 +121,7 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
   for (int idx = threadIdx.x; idx < Tb * W; idx += blockDim.x) {
     const int t = idx / W, jj = idx % W;
     const uint16_t vb = a.v[((row0 + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj];
-    st.v[t * W + jj] = bf16_to_f32(vb);
+    st.v[t * W + v_slot<C>(jj, L.slab)] = bf16_to_f32(vb);
     if (replay) a.rv[(((int64_t)u.b * a.T_max + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj] = vb;
     if constexpr (GATE) st.g[t * W + jj] = bf16_to_f32(a.gate[((row0 + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj]);
   }
@@ -86,52 +132,67 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
   }
   __syncthreads();
   if constexpr (RAW) {
-    prep_staged<DK>(st.k, st.q, st.a, st.beta, Tb);
+    prep_staged<DK, Staged<DK>::kRec>(st.k(0), st.q(0), st.a(0), st.beta, Tb);
     __syncthreads();
   }
 
-  __shared__ float part[GATE ? kMaxT * kMaxWaves : 1];
-  __shared__ float raw[GATE ? kMaxT * kMaxDv : 1];
-
+  float keep[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) keep[c] = 0.0f;
+  const lds_float *pk = to_lds(st.rec) + 4 * L.r;
+  const lds_float *pv = to_lds(st.v) + L.col0 * C;
   for (int t = 0; t < Tb; ++t) {
     float4 kk[NV], qq[NV], aa[NV];
 #pragma unroll
     for (int e = 0; e < NV; ++e) {
-      const int i = t * DK + 4 * L.r + 64 * e;
-      kk[e] = *reinterpret_cast<const float4 *>(st.k + i);
-      qq[e] = *reinterpret_cast<const float4 *>(st.q + i);
-      aa[e] = *reinterpret_cast<const float4 *>(st.a + i);
+      kk[e] = lds_f4(pk + 64 * e);
+      aa[e] = lds_f4(pk + DK + 64 * e);
+      qq[e] = lds_f4(pk + 2 * DK + 64 * e);
     }
     float vj[C];
-#pragma unroll
-    for (int c = 0; c < C; ++c) vj[c] = st.v[t * W + L.col0 + c * L.slab];
+    load_v<C>(pv, vj);
     token_update<NV, C>(s, aa, kk, vj, st.beta[t]);
     float o[C];
     token_readout<NV, C>(s, qq, o);
-    const int64_t obase = ((row0 + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W;
-    if constexpr (GATE) {
-      // keep the raw read-out in LDS; the whole chunk is normalized after the loop
-      store_cols<C>(raw + t * kMaxDv, L, o);
-      gate_partial<C>(o, part + t * kMaxWaves);
-    } else {
-      store_out<C>(a, BF16, obase, L, o);
+    const bool mine = L.r == t;
+#pragma unroll
+    for (int c = 0; c < C; ++c) keep[c] = mine ? o[c] : keep[c];
+    if constexpr (PERPOS) {
+      if (!inplace) {
+        float *D = a.draft + ((((int64_t)u.b * a.T_max + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W) * DK;
+        store_tile<DK, C, kVerifyStoreStream>(D, s, L);
+      }
     }
-    if (perpos) {
-      float *D = a.draft + ((((int64_t)u.b * a.T_max + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W) * DK;
-      store_tile<DK, C, kVerifyStoreStream>(D, s, L);
-    }
+    pk += Staged<DK>::kRec;
+    pv += W;
   }
   if (inplace) store_tile<DK, C, kVerifyStoreStream>(S, s, L);
+  const int64_t obase = ((row0 + L.r) * a.H + u.h) * a.dv + (int64_t)u.tile * W + L.col0;
   if constexpr (GATE) {
-    // one barrier for the whole chunk, then each lane finishes its column per token
+    // the gate's sum of squares over the head: per lane, then over the wave's
+    // four rows (in the order (row 0 + row 1) + (row 2 + row 3)), then over the
+    // waves after one barrier
+    __shared__ float part[kMaxT * kMaxWaves];
+    float ss = keep[0] * keep[0];
+#pragma unroll
+    for (int c = 1; c < C; ++c) ss = __builtin_fmaf(keep[c], keep[c], ss);
+    ss = ss + __shfl_xor(ss, 16);
+    ss = ss + __shfl_xor(ss, 32);
+    if ((threadIdx.x & 63) < Tb) part[(threadIdx.x & 63) * kMaxWaves + (threadIdx.x >> 6)] = ss;
     __syncthreads();
-    if (L.r < C) {
-      const int j = L.col0 + L.r * L.slab;
-      const float wj = a.weight ? a.weight[j] : 1.0f;
-      for (int t = 0; t < Tb; ++t) {
-        const int64_t obase = ((row0 + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W;
-        put_out(a, BF16, obase + j, gate_apply(a, part + t * kMaxWaves, raw[t * kMaxDv + j], st.g[t * W + j], wj));
+    if (L.r < Tb) {
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int j = L.col0 + c * L.slab;
+        const float wj = a.weight ? a.weight[j] : 1.0f;
+        put_out(a, BF16, obase + c * L.slab,
+                gate_apply(a, part + L.r * kMaxWaves, keep[c], st.g[L.r * W + j], wj));
       }
+    }
+  } else {
+    if (L.r < Tb) {
+#pragma unroll
+      for (int c = 0; c < C; ++c) put_out(a, BF16, obase + c * L.slab, keep[c]);
     }
   }
 }
@@ -185,32 +246,35 @@ __global__ __launch_bounds__(256) void commit_replay_kernel(Args a) {
   for (int idx = threadIdx.x; idx < n * (DK / 4); idx += blockDim.x) {
     const int t = idx / (DK / 4), i = (idx % (DK / 4)) * 4;
     const int64_t d = (((int64_t)u.b * a.T_max + t) * a.H + u.h) * DK + i;
-    *reinterpret_cast<float4 *>(st.k + t * DK + i) = unpack_bf16x4(*reinterpret_cast<const uint2 *>(a.rk + d));
-    *reinterpret_cast<float4 *>(st.a + t * DK + i) = *reinterpret_cast<const float4 *>(a.ralpha + d);
+    *reinterpret_cast<float4 *>(st.k(t) + i) = unpack_bf16x4(*reinterpret_cast<const uint2 *>(a.rk + d));
+    *reinterpret_cast<float4 *>(st.a(t) + i) = *reinterpret_cast<const float4 *>(a.ralpha + d);
   }
   for (int idx = threadIdx.x; idx < n * W; idx += blockDim.x) {
     const int t = idx / W, jj = idx % W;
-    st.v[t * W + jj] = bf16_to_f32(a.rv[(((int64_t)u.b * a.T_max + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj]);
+    st.v[t * W + v_slot<C>(jj, L.slab)] =
+        bf16_to_f32(a.rv[(((int64_t)u.b * a.T_max + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj]);
   }
   if ((int)threadIdx.x < n) st.beta[threadIdx.x] = a.rbeta[((int64_t)u.b * a.T_max + threadIdx.x) * a.H + u.h];
   __syncthreads();
   if (a.raw) {
-    prep_staged<DK>(st.k, nullptr, st.a, st.beta, n);
+    prep_staged<DK, Staged<DK>::kRec>(st.k(0), nullptr, st.a(0), st.beta, n);
     __syncthreads();
   }
 
+  const lds_float *pk = to_lds(st.rec) + 4 * L.r;
+  const lds_float *pv = to_lds(st.v) + L.col0 * C;
   for (int t = 0; t < n; ++t) {
     float4 kk[NV], aa[NV];
 #pragma unroll
     for (int e = 0; e < NV; ++e) {
-      const int i = t * DK + 4 * L.r + 64 * e;
-      kk[e] = *reinterpret_cast<const float4 *>(st.k + i);
-      aa[e] = *reinterpret_cast<const float4 *>(st.a + i);
+      kk[e] = lds_f4(pk + 64 * e);
+      aa[e] = lds_f4(pk + DK + 64 * e);
     }
     float vj[C];
-#pragma unroll
-    for (int c = 0; c < C; ++c) vj[c] = st.v[t * W + L.col0 + c * L.slab];
+    load_v<C>(pv, vj);
     token_update<NV, C>(s, aa, kk, vj, st.beta[t]);
+    pk += Staged<DK>::kRec;
+    pv += W;
   }
   store_tile<DK, C, kCommitStoreStream>(S, s, L);
 }
@@ -239,26 +303,29 @@ size_t staged_bytes(int dk, int T_max, int W, bool gate) {
   return ((size_t)T_max * (3 * dk + W + 1 + (gate ? W : 0)) * sizeof(float) + 15) / 16 * 16;
 }
 
-template <int DK, int C, bool GATE>
+template <int DK, int C, bool GATE, bool PERPOS>
 struct verify_table {
   template <int IO>
-  static const void *get() { return (const void *)verify_kernel<DK, C, GATE, IO>; }
+  static const void *get() { return (const void *)verify_kernel<DK, C, GATE, IO, PERPOS>; }
 };
 
-template <int DK>
+template <int DK, bool PERPOS>
 const void *verify_for(int C, bool gate, int io) {
-  if (gate) return C == kGateSlabsVerify ? io_variant<verify_table<DK, kGateSlabsVerify, true>>(io) : nullptr;
+  if (gate)
+    return C == kGateSlabsVerify ? io_variant<verify_table<DK, kGateSlabsVerify, true, PERPOS>>(io) : nullptr;
   switch (C) {
-    case 1: return io_variant<verify_table<DK, 1, false>>(io);
-    case 2: return io_variant<verify_table<DK, 2, false>>(io);
-    case 4: return io_variant<verify_table<DK, 4, false>>(io);
-    case 8: return io_variant<verify_table<DK, 8, false>>(io);
+    case 1: return io_variant<verify_table<DK, 1, false, PERPOS>>(io);
+    case 2: return io_variant<verify_table<DK, 2, false, PERPOS>>(io);
+    case 4: return io_variant<verify_table<DK, 4, false, PERPOS>>(io);
+    case 8: return io_variant<verify_table<DK, 8, false, PERPOS>>(io);
   }
   return nullptr;
 }
 
-const void *verify_kernel_for(int dk, int C, bool gate, int io) {
-  return dk == 64 ? verify_for<64>(C, gate, io) : dk == 128 ? verify_for<128>(C, gate, io) : nullptr;
+const void *verify_kernel_for(int dk, int C, bool gate, int io, bool perpos) {
+  if (dk == 64) return perpos ? verify_for<64, true>(C, gate, io) : verify_for<64, false>(C, gate, io);
+  if (dk == 128) return perpos ? verify_for<128, true>(C, gate, io) : verify_for<128, false>(C, gate, io);
+  return nullptr;
 }
 
 template <int DK>
