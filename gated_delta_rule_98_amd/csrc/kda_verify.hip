@@ -31,7 +31,8 @@ struct Staged {
 // columns as one vector.
 template <int C>
 __device__ __forceinline__ int v_slot(int jj, int slab) {
-  return (jj % slab) * C + jj / slab;
+  const int sh = __builtin_ctz(slab);  // slab = 4 * waves, a power of two
+  return (jj & (slab - 1)) * C + (jj >> sh);
 }
 
 // LDS pointers in the local address space: the token loops step them with
@@ -118,12 +119,17 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
       *reinterpret_cast<float4 *>(a.ralpha + d) = al;
     }
   }
-  for (int idx = threadIdx.x; idx < Tb * W; idx += blockDim.x) {
-    const int t = idx / W, jj = idx % W;
-    const uint16_t vb = a.v[((row0 + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj];
-    st.v[t * W + v_slot<C>(jj, L.slab)] = bf16_to_f32(vb);
-    if (replay) a.rv[(((int64_t)u.b * a.T_max + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj] = vb;
-    if constexpr (GATE) st.g[t * W + jj] = bf16_to_f32(a.gate[((row0 + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj]);
+  {
+    // a thread keeps one tile column; blockDim.x is a multiple of W (both powers of two)
+    const int jj = threadIdx.x & (W - 1), sv = v_slot<C>(jj, L.slab);
+    const int tstep = blockDim.x >> __builtin_ctz(W);
+    for (int t = threadIdx.x >> __builtin_ctz(W); t < Tb; t += tstep) {
+      const int64_t col = ((row0 + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj;
+      const uint16_t vb = a.v[col];
+      st.v[t * W + sv] = bf16_to_f32(vb);
+      if (replay) a.rv[(((int64_t)u.b * a.T_max + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj] = vb;
+      if constexpr (GATE) st.g[t * W + jj] = bf16_to_f32(a.gate[col]);
+    }
   }
   if ((int)threadIdx.x < Tb) {
     const float bt = a.beta[(row0 + threadIdx.x) * a.H + u.h];
@@ -249,10 +255,11 @@ __global__ __launch_bounds__(256) void commit_replay_kernel(Args a) {
     *reinterpret_cast<float4 *>(st.k(t) + i) = unpack_bf16x4(*reinterpret_cast<const uint2 *>(a.rk + d));
     *reinterpret_cast<float4 *>(st.a(t) + i) = *reinterpret_cast<const float4 *>(a.ralpha + d);
   }
-  for (int idx = threadIdx.x; idx < n * W; idx += blockDim.x) {
-    const int t = idx / W, jj = idx % W;
-    st.v[t * W + v_slot<C>(jj, L.slab)] =
-        bf16_to_f32(a.rv[(((int64_t)u.b * a.T_max + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj]);
+  {
+    const int jj = threadIdx.x & (W - 1), sv = v_slot<C>(jj, L.slab);
+    const int tstep = blockDim.x >> __builtin_ctz(W);
+    for (int t = threadIdx.x >> __builtin_ctz(W); t < n; t += tstep)
+      st.v[t * W + sv] = bf16_to_f32(a.rv[(((int64_t)u.b * a.T_max + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj]);
   }
   if ((int)threadIdx.x < n) st.beta[threadIdx.x] = a.rbeta[((int64_t)u.b * a.T_max + threadIdx.x) * a.H + u.h];
   __syncthreads();
