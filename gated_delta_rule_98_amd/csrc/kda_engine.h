@@ -44,7 +44,7 @@ constexpr int kMaxDv = 128;
 // Slabs per lane when the output gate makes one workgroup own all dv columns
 // (waves = dv / (4 * slabs)); measured on MI355X.
 constexpr int kGateSlabsDecode = 2;
-constexpr int kGateSlabsVerify = 4;
+constexpr int kGateSlabsVerify = 2;
 
 struct Args {
   float *cache;

@@ -73,9 +73,9 @@ def test_query_variant_launch_shapes():
         q(1, 32, 128, 128, T_max=100, op=P, tile_w=64)
     # the output gate needs the whole head in one workgroup
     assert q(64, 32, 128, 128, epilogue=True) == (128, 1024)   # decode: 16 waves x 2 slabs
-    assert q(64, 32, 128, 128, T_max=4, epilogue=True, op=V) == (128, 512)
+    assert q(64, 32, 128, 128, T_max=4, epilogue=True, op=V) == (128, 1024)   # verify: 16 waves x 2 slabs
     assert q(64, 32, 128, 64, epilogue=True) == (64, 512)
-    assert q(64, 32, 128, 64, T_max=4, epilogue=True, op=V) == (64, 256)   # verify: 4 slabs
+    assert q(64, 32, 128, 64, T_max=4, epilogue=True, op=V) == (64, 512)
     for w, threads in ((4, 64), (8, 128), (16, 256), (32, 256), (64, 256), (128, 256)):
         assert q(3, 5, 128, 128, tile_w=w) == (w, threads)
     for bad in (dict(tile_w=24), dict(tile_w=256), dict(epilogue=True, tile_w=64)):
