@@ -98,43 +98,71 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
   const Lane L = lane_geometry();
   const int W = C * L.slab;
   Staged<DK> st(reinterpret_cast<float *>(lds_dyn), a.T_max, W);
-  // the state tile is requested first, so its HBM latency overlaps the staging
   float *S = a.cache + (int64_t)slot * a.slot_stride + ((int64_t)u.h * a.dv + (int64_t)u.tile * W) * DK;
+  // Vector loads complete in issue order. The first round of staging loads is
+  // issued before the state tile, so writing the staging to LDS waits for the
+  // inputs alone; each wave then waits for its own tile after the barrier
+  // instead of the whole workgroup waiting for its slowest tile.
+  const int nkq = Tb * (DK / 4);
+  const int jj = threadIdx.x & (W - 1), sv = v_slot<C>(jj, L.slab);  // blockDim.x is a multiple of W
+  const int tsh = __builtin_ctz(W), tstep = blockDim.x >> tsh, tv0 = threadIdx.x >> tsh;
+  auto kq_off = [&](int idx) { return ((row0 + idx / (DK / 4)) * a.H + u.h) * DK + (idx % (DK / 4)) * 4; };
+  auto v_off = [&](int t) { return ((row0 + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj; };
+  // (unconditional loads at clamped, in-bounds indices: straight-line code
+  // keeps the compiler from waiting for them before the state loads go out)
+  const int64_t off0 = kq_off(min((int)threadIdx.x, nkq - 1));
+  const uint2 kb0 = *reinterpret_cast<const uint2 *>(a.k + off0);
+  const uint2 qb0 = *reinterpret_cast<const uint2 *>(a.q + off0);
+  const float4 al0 = *reinterpret_cast<const float4 *>(a.alpha + off0);
+  const int64_t voff0 = v_off(min(tv0, Tb - 1));
+  const uint16_t vb0 = a.v[voff0];
+  const uint16_t gb0 = GATE ? a.gate[voff0] : (uint16_t)0;
+  const float bt0 = a.beta[(row0 + min((int)threadIdx.x, Tb - 1)) * a.H + u.h];
+  __builtin_amdgcn_sched_barrier(0);  // keep the issue order: inputs, then state
   float4 s[C][NV];
   load_tile<DK, C, kVerifyLoadStream>(s, S, L);
 
-  // stage the chunk's inputs; in replay mode also copy them to the buffer
-  for (int idx = threadIdx.x; idx < Tb * (DK / 4); idx += blockDim.x) {
+  // stage the chunk's inputs; in replay mode also copy them to the buffer. The
+  // copies of the first round go out at the end of the kernel: stores share the
+  // load counter, and a store issued behind the state loads can make a later
+  // wait (for a staging load, or for a register the store still reads) wait
+  // for the state too.
+  auto put_kq = [&](int idx, uint2 kb, uint2 qb, float4 al) {
     const int t = idx / (DK / 4), i = (idx % (DK / 4)) * 4;
-    const int64_t off = ((row0 + t) * a.H + u.h) * DK + i;
-    const uint2 kb = *reinterpret_cast<const uint2 *>(a.k + off);
-    const uint2 qb = *reinterpret_cast<const uint2 *>(a.q + off);
-    const float4 al = *reinterpret_cast<const float4 *>(a.alpha + off);
     *reinterpret_cast<float4 *>(st.k(t) + i) = unpack_bf16x4(kb);
     *reinterpret_cast<float4 *>(st.q(t) + i) = unpack_bf16x4(qb);
     *reinterpret_cast<float4 *>(st.a(t) + i) = al;
+  };
+  auto copy_kq = [&](int idx, uint2 kb, float4 al) {
     if (replay && u.tile == 0) {
+      const int t = idx / (DK / 4), i = (idx % (DK / 4)) * 4;
       const int64_t d = (((int64_t)u.b * a.T_max + t) * a.H + u.h) * DK + i;
       *reinterpret_cast<uint2 *>(a.rk + d) = kb;
       *reinterpret_cast<float4 *>(a.ralpha + d) = al;
     }
+  };
+  auto put_v = [&](int t, uint16_t vb, uint16_t gb) {
+    st.v[t * W + sv] = bf16_to_f32(vb);
+    if constexpr (GATE) st.g[t * W + jj] = bf16_to_f32(gb);
+  };
+  auto copy_v = [&](int t, uint16_t vb) {
+    if (replay) a.rv[(((int64_t)u.b * a.T_max + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj] = vb;
+  };
+  if ((int)threadIdx.x < nkq) put_kq(threadIdx.x, kb0, qb0, al0);
+  if (tv0 < Tb) put_v(tv0, vb0, gb0);
+  if ((int)threadIdx.x < Tb) st.beta[threadIdx.x] = bt0;
+  // further rounds (more than blockDim.x staging items)
+  for (int idx = threadIdx.x + blockDim.x; idx < nkq; idx += blockDim.x) {
+    const int64_t off = kq_off(idx);
+    const uint2 kb = *reinterpret_cast<const uint2 *>(a.k + off), qb = *reinterpret_cast<const uint2 *>(a.q + off);
+    const float4 al = *reinterpret_cast<const float4 *>(a.alpha + off);
+    put_kq(idx, kb, qb, al);
+    copy_kq(idx, kb, al);
   }
-  {
-    // a thread keeps one tile column; blockDim.x is a multiple of W (both powers of two)
-    const int jj = threadIdx.x & (W - 1), sv = v_slot<C>(jj, L.slab);
-    const int tstep = blockDim.x >> __builtin_ctz(W);
-    for (int t = threadIdx.x >> __builtin_ctz(W); t < Tb; t += tstep) {
-      const int64_t col = ((row0 + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj;
-      const uint16_t vb = a.v[col];
-      st.v[t * W + sv] = bf16_to_f32(vb);
-      if (replay) a.rv[(((int64_t)u.b * a.T_max + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj] = vb;
-      if constexpr (GATE) st.g[t * W + jj] = bf16_to_f32(a.gate[col]);
-    }
-  }
-  if ((int)threadIdx.x < Tb) {
-    const float bt = a.beta[(row0 + threadIdx.x) * a.H + u.h];
-    st.beta[threadIdx.x] = bt;
-    if (replay && u.tile == 0) a.rbeta[((int64_t)u.b * a.T_max + threadIdx.x) * a.H + u.h] = bt;
+  for (int t = tv0 + tstep; t < Tb; t += tstep) {
+    const uint16_t vb = a.v[v_off(t)];
+    put_v(t, vb, GATE ? a.gate[v_off(t)] : (uint16_t)0);
+    copy_v(t, vb);
   }
   __syncthreads();
   if constexpr (RAW) {
@@ -201,7 +229,27 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
       for (int c = 0; c < C; ++c) put_out(a, BF16, obase + c * L.slab, keep[c]);
     }
   }
+  // the first round's replay copies (see the staging above). With prepared
+  // inputs they are read back from LDS (each staged value came from a bf16 or
+  // fp32 input exactly; the bf16 ones return to their bits by truncation), so
+  // no register stays live across the token loop; raw inputs were prepared in
+  // place, so that variant keeps the raw values in registers.
+  if ((int)threadIdx.x < nkq) {
+    if constexpr (RAW) {
+      copy_kq(threadIdx.x, kb0, al0);
+    } else {
+      const int t = threadIdx.x / (DK / 4), i = (threadIdx.x % (DK / 4)) * 4;
+      const float4 kf = *reinterpret_cast<const float4 *>(st.k(t) + i);
+      const uint2 kb = {(__float_as_uint(kf.x) >> 16) | (__float_as_uint(kf.y) & 0xffff0000u),
+                        (__float_as_uint(kf.z) >> 16) | (__float_as_uint(kf.w) & 0xffff0000u)};
+      copy_kq(threadIdx.x, kb, *reinterpret_cast<const float4 *>(st.a(t) + i));
+    }
+  }
+  if (tv0 < Tb) copy_v(tv0, (uint16_t)(__float_as_uint(st.v[tv0 * W + sv]) >> 16));
+  if ((int)threadIdx.x < Tb && replay && u.tile == 0)
+    a.rbeta[((int64_t)u.b * a.T_max + threadIdx.x) * a.H + u.h] = RAW ? bt0 : st.beta[threadIdx.x];
 }
+
 
 // ----------------------------------------------------------------------------
 // Commit
