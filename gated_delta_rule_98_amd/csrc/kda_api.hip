@@ -40,8 +40,10 @@ bool dims_supported(int dk, int dv) { return (dk == 64 || dk == 128) && (dv == 6
 //    over the whole chip; once that would exceed 1024 workgroups the step is a
 //    pure stream and one-wave workgroups of 4 columns sustain the highest rate;
 //    at exactly 512 heads of 128 columns, 128-column tiles (two per CU);
-//  * verify and replay commit (T tokens per row, VALU-heavy): 32 columns while
-//    that gives at least 512 workgroups, narrower tiles below that;
+//  * verify (T tokens per row, VALU-heavy): 32 columns while that gives at
+//    least 256 workgroups, 16 below that, then 8;
+//  * replay commit: 32 columns from 2048 workgroups up, 16 columns down to 256
+//    workgroups, then 8;
 //  * per-position copy commit: 16 columns.
 int choose_width(Kind kind, int64_t rows, int H, int dv, bool gate, int requested, Launch *l) {
   if (gate) {
@@ -79,14 +81,20 @@ int choose_width(Kind kind, int64_t rows, int H, int dv, bool gate, int requeste
       if (dv == 128 && heads == 512) W = 128;
       break;
     case KIND_VERIFY:
-    case KIND_COMMIT_REPLAY:
       W = 8;
       for (int cand : {32, 16}) {
-        if (cand <= dv && heads * (dv / cand) >= 512) {
+        if (cand <= dv && heads * (dv / cand) >= 256) {
           W = cand;
           break;
         }
       }
+      break;
+    case KIND_COMMIT_REPLAY:
+      W = 8;
+      if (32 <= dv && heads * (dv / 32) >= 2048)
+        W = 32;
+      else if (16 <= dv && heads * (dv / 16) >= 256)
+        W = 16;
       break;
     case KIND_COMMIT_COPY:
     case KIND_PREFILL:
