@@ -361,6 +361,45 @@ def spec_verify(D, K, synth, reps):
     return res
 
 
+def spec_verify_small(D, K, synth, reps, batches=(1, 4)):
+    """Speculative verify at small batch: B rows of 8 draft tokens (H=32, d=128), replay mode,
+    verify and commit (5 accepted per row) timed in HIP graphs, 16 disjoint slot tables."""
+    torch = D.torch
+    res = {}
+    for B in batches:
+        T = 8
+        w = synth.make(B, 32, 128, 128, seqlens=[T] * B, num_slots=16 * B, state_std=0.02, seed=B,
+                       name=f"spec_b{B}")
+        cache = D.f(w.cache)
+        tables = [D.i(t) for t in w.slot_tables]
+        cu = D.i(w.cu_seqlens)
+        acc_h = np.full(B, 5, np.int32)
+        acc = D.i(acc_h)
+        x = dict(q=D.bf(w.q[0]), k=D.bf(w.k[0]), v=D.bf(w.v[0]), alpha=D.f(w.alpha[0]), beta=D.f(w.beta[0]))
+        out = torch.empty(w.n_tok, 32, 128, device=D.dev)
+        rbs = [_replay_bufs(torch, D.dev, B, T, 32, 128, 128) for _ in range(4)]
+
+        def verify(i):
+            K.kda_verify_chunk(cache, tables[i % len(tables)], cu, T, x["q"], x["k"], x["v"], x["alpha"], x["beta"],
+                               out, mode=0, replay=rbs[i % 4])
+
+        def commit(i):
+            K.kda_replay_commit(cache, tables[i % len(tables)], cu, acc, T, w.n_tok, mode=0, replay=rbs[i % 4])
+
+        for i in range(8):
+            verify(i)
+            commit(i)
+        v_ms = graph_ms(D, verify, reps)
+        c_ms = graph_ms(D, commit, reps)
+        vb = verify_bytes(w.n_tok, B, 32, 128, 128, 0, T)
+        cb = commit_bytes(acc_h, 32, 128, 128, 0)
+        res[f"b{B}"] = dict(verify_us=round(v_ms * 1e3, 3), commit_us=round(c_ms * 1e3, 3),
+                            verify_gbs=round(vb / v_ms / 1e6, 1), commit_gbs=round(cb / c_ms / 1e6, 1),
+                            tile_w=K.kda_query_variant(B, 32, 128, 128, T_max=T, op=K.KDA_OP_VERIFY)[0])
+        log(f"spec_verify B={B} T=8 (HIP graph): verify {v_ms * 1e3:.2f} us, commit {c_ms * 1e3:.2f} us")
+    return res
+
+
 def mixed(D, K, synth, reps):
     """40 single-token rows (in place) + 24 rows of 4 verified tokens, output gate, then the
     commit of the 24; 8 disjoint slot tables over the 512-slot cache, 2 replay buffers."""
@@ -560,6 +599,7 @@ def main():
             decode_batch_sweep=batch_sweep(D, K, synth, reps=256),
             b1_latency_1024_steps=b1_latency(D, K, synth),
             spec_verify_b16_t8=spec_verify(D, K, synth, reps=200),
+            spec_verify_small_batch=spec_verify_small(D, K, synth, reps=200),
             mixed_b64_gated=mixed(D, K, synth, reps=200),
             prefill_8k_checkpoint=prefill_8k(D, K, synth, reps=5),
             prefill_8k_checkpoint_chunked=prefill_8k(D, K, synth, reps=5, chunked=True),

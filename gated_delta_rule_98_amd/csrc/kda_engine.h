@@ -314,15 +314,44 @@ __device__ __forceinline__ Unit unit_of_block(int ntile, int H) {
 
 // For kernels whose rows carry unequal work (varying token counts, rows that
 // skip): deal the (row, head) groups out to the XCDs in turn, so every XCD gets
-// an equal share of each row while a group's tiles still share one L2. Needs a
-// multiple of 8 groups; other counts use the contiguous numbering above.
+// an equal share of each row while a group's tiles still share one L2. With a
+// multiple of 8 heads, XCD x takes heads x, x + 8, ... of every row, in an
+// order where the row varies fastest, so the groups resident at any moment mix
+// every kind of row: memory-bound single-token rows overlap VALU-bound
+// multi-token ones instead of running before them. Other head counts take
+// groups 8j + x in row order; counts of groups that are not a multiple of 8
+// use the contiguous numbering above.
 __device__ __forceinline__ Unit unit_of_block_rows(int ntile, int H, int B) {
   if ((B * H) & 7) return unit_of_block(ntile, H);
-  const int n = blockIdx.x;
+  const int n = blockIdx.x, xcd = n & 7;
   int j, tile;
   divmod_uniform(n >> 3, ntile, j, tile);
-  Unit r = unit_of_index((j << 3) | (n & 7), 1, H);
+  Unit r;
   r.tile = tile;
+  if ((H & 7) == 0) {
+    int jh;
+    divmod_uniform(j, B, jh, r.b);
+    r.h = (jh << 3) | xcd;
+  } else {
+    divmod_uniform((j << 3) | xcd, H, r.b, r.h);
+  }
+  return r;
+}
+
+// Verify's numbering: groups dealt to the XCDs in turn, head-major (group
+// 8j + x is head (8j + x) / B of row (8j + x) % B), so XCD x takes whole rows
+// x, x + 8, ... (each slot's heads together in HBM) and the rows it holds
+// alternate in its dispatch order. Measured on the mixed batch (40 single-token
+// rows then 24 four-token rows, output gate): 43.1 us against 45.5 us for the
+// numbering above and 46.4 us for row order. Counts of groups that are not a
+// multiple of 8 use the contiguous numbering.
+__device__ __forceinline__ Unit unit_of_block_headmajor(int ntile, int H, int B) {
+  if ((B * H) & 7) return unit_of_block(ntile, H);
+  const int n = blockIdx.x;
+  int j;
+  Unit r;
+  divmod_uniform(n >> 3, ntile, j, r.tile);
+  divmod_uniform((j << 3) | (n & 7), B, r.h, r.b);
   return r;
 }
 

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
   constexpr int NV = DK / 64;
   constexpr bool RAW = IO & kIoRaw, BF16 = IO & kIoBf16;
   extern __shared__ float4 lds_dyn[];
-  const Unit u = unit_of_block_rows(a.ntile, a.H, a.B);
+  const Unit u = unit_of_block_headmajor(a.ntile, a.H, a.B);
   const int32_t slot = a.slot_ids[u.b];
   if (slot < 0) return;
   if (slot >= a.num_slots) {

@@ -2,12 +2,15 @@
 
 Kernels whose rows carry unequal work (verify, both commits, both prefill
 forms) deal the (row, head) groups out to the 8 XCDs in turn when there is a
-multiple of 8 groups, and otherwise take contiguous ranges; the head count is
-split off with a shift when it is a power of two and with a division
-otherwise. These shapes reach every combination, with ragged rows, an empty
-row and a padding row, and each result is checked against the oracle:
-outputs within 1e-4 relative L2, states within 1e-3 relative Frobenius,
-untouched slots bit-exact.
+multiple of 8 groups, and otherwise take contiguous ranges. Verify numbers
+the groups head-major (split by the batch size); the commits and prefill
+deal heads x, x + 8, ... of every row to XCD x when the head count is a
+multiple of 8 (split by the batch size) and take groups in row order
+otherwise (split by the head count). Each split is a shift for a power of two
+and a division otherwise. These shapes reach every combination, with ragged
+rows, an empty row and a padding row, and each result is checked against the
+oracle: outputs within 1e-4 relative L2, states within 1e-3 relative
+Frobenius, untouched slots bit-exact.
 """
 
 import numpy as np
@@ -24,9 +27,11 @@ pytestmark = pytest.mark.gpu
 OUT_TOL = 1e-4
 STATE_TOL = 1e-3
 
-# (B, H): 24 groups dealt in turn with H = 3 and H = 6 (division), 24 and 16
-# with powers of two (shift), 15 and 21 in contiguous ranges
-SHAPES = [(8, 3), (4, 6), (6, 4), (2, 8), (5, 3), (7, 3)]
+# (B, H): 24 groups in row order with H = 3 and H = 6 (division) and H = 4
+# (shift); heads dealt with B = 2 (shift) and B = 3 (division); 15 and 21 in
+# contiguous ranges. Verify's head-major split divides by B = 6 and 3 and
+# shifts by the others.
+SHAPES = [(8, 3), (4, 6), (6, 4), (2, 8), (3, 16), (5, 3), (7, 3)]
 
 
 def _workload(B, H, seed, max_len=12):
