@@ -9,6 +9,9 @@
 namespace kda {
 
 constexpr int kChunkTokens = 32;  // tokens per chunk of the chunk form of prefill
+// Threads of a precompute workgroup (8 waves; measured on MI355X against 4 and
+// 16 at d = 128).
+constexpr int kChunkPrepThreads = 512;
 
 // Arguments of both chunk-prefill kernels.
 struct ChunkArgs {

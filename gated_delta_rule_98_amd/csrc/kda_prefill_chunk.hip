@@ -128,7 +128,7 @@ __device__ __forceinline__ void prep_rows(float *k, float *q, float *al, float *
 }
 
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void prefill_chunk_prep_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(kChunkPrepThreads) void prefill_chunk_prep_kernel(ChunkArgs a) {
   using WS = ChunkWs<DK, DV>;
   constexpr int CPT = DK / 16;  // channels per lane when a 16-lane row spans DK
   // Rows of k, q and alpha are padded by 4 floats: the MFMA operand reads of 16
@@ -161,12 +161,15 @@ __global__ __launch_bounds__(256) void prefill_chunk_prep_kernel(ChunkArgs a) {
 
   // stage the chunk; tokens past its end are k = q = v = 0, alpha = 1, beta = 0.
   // Every load is issued before the first LDS write.
-  constexpr int NK = kCL * (DK / 4) / 256, NVL = kCL * (DV / 4) / 256;
+  constexpr int NT = kChunkPrepThreads, NWAVES = NT / 64;
+  constexpr int NK = kCL * (DK / 4) / NT;  // staging rounds of k, q and alpha
+  constexpr int NVI = kCL * (DV / 4), NVL = (NVI + NT - 1) / NT;  // and of v
+  static_assert(NK >= 1 && kCL * (DK / 4) == NT * NK, "whole staging rounds of k, q and alpha");
   uint2 kr[NK], qr[NK], vr[NVL];
   float4 ar[NK];
 #pragma unroll
   for (int m = 0; m < NK; ++m) {
-    const int idx = threadIdx.x + 256 * m, t = idx / (DK / 4), i = (idx % (DK / 4)) * 4;
+    const int idx = threadIdx.x + NT * m, t = idx / (DK / 4), i = (idx % (DK / 4)) * 4;
     kr[m] = qr[m] = make_uint2(0u, 0u);
     ar[m] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
     if (t < n) {
@@ -178,22 +181,22 @@ __global__ __launch_bounds__(256) void prefill_chunk_prep_kernel(ChunkArgs a) {
   }
 #pragma unroll
   for (int m = 0; m < NVL; ++m) {
-    const int idx = threadIdx.x + 256 * m, t = idx / (DV / 4), j = (idx % (DV / 4)) * 4;
+    const int idx = threadIdx.x + NT * m, t = idx / (DV / 4), j = (idx % (DV / 4)) * 4;
     vr[m] = make_uint2(0u, 0u);
-    if (t < n) vr[m] = *reinterpret_cast<const uint2 *>(a.v + ((row0 + t) * a.H + h) * DV + j);
+    if (idx < NVI && t < n) vr[m] = *reinterpret_cast<const uint2 *>(a.v + ((row0 + t) * a.H + h) * DV + j);
   }
   if ((int)threadIdx.x < kCL) bet[threadIdx.x] = (int)threadIdx.x < n ? a.beta[(row0 + threadIdx.x) * a.H + h] : 0.0f;
 #pragma unroll
   for (int m = 0; m < NK; ++m) {
-    const int idx = threadIdx.x + 256 * m, t = idx / (DK / 4), i = (idx % (DK / 4)) * 4;
+    const int idx = threadIdx.x + NT * m, t = idx / (DK / 4), i = (idx % (DK / 4)) * 4;
     *reinterpret_cast<float4 *>(kb + t * PK + i) = unpack_bf16x4(kr[m]);
     *reinterpret_cast<float4 *>(qb + t * PK + i) = unpack_bf16x4(qr[m]);
     *reinterpret_cast<float4 *>(ab + t * PK + i) = ar[m];
   }
 #pragma unroll
   for (int m = 0; m < NVL; ++m) {
-    const int idx = threadIdx.x + 256 * m, t = idx / (DV / 4), j = (idx % (DV / 4)) * 4;
-    *reinterpret_cast<float4 *>(vb + t * DV + j) = unpack_bf16x4(vr[m]);
+    const int idx = threadIdx.x + NT * m, t = idx / (DV / 4), j = (idx % (DV / 4)) * 4;
+    if (idx < NVI) *reinterpret_cast<float4 *>(vb + t * DV + j) = unpack_bf16x4(vr[m]);
   }
   __syncthreads();
   if (a.raw) {
@@ -201,50 +204,37 @@ __global__ __launch_bounds__(256) void prefill_chunk_prep_kernel(ChunkArgs a) {
     __syncthreads();
   }
 
-  // inside each sub-block: A and B by running products. Row (s, 16 lanes) carries
-  // D(t, s) over its lane's channels cl + 16 e as t advances and sums over the row;
-  // both sub-blocks at once.
-  {
-    const int s = threadIdx.x >> 4, cl = threadIdx.x & 15;
-    float d0[CPT], d1[CPT];
-    float pd0 = 0.0f, pd1 = 0.0f;
+  // inside each sub-block: A and B by running products. Row (s, 16 lanes) of
+  // sub-block o carries D(t, s) over its lane's channels cl + 16 e as t advances
+  // and sums over the row; the 32 rows of 16 lanes cover both sub-blocks.
+  if ((int)threadIdx.x < 2 * kSB * 16) {
+    const int o = (threadIdx.x >> 8) * kSB, s = (threadIdx.x >> 4) & 15, cl = threadIdx.x & 15;
+    float d[CPT];
+    float pd = 0.0f;
 #pragma unroll
     for (int e = 0; e < CPT; ++e) {
-      const int c0 = s * PK + cl + 16 * e, c1 = (kSB + s) * PK + cl + 16 * e;
-      d0[e] = kb[c0];
-      d1[e] = kb[c1];
-      pd0 = __builtin_fmaf(qb[c0], d0[e], pd0);
-      pd1 = __builtin_fmaf(qb[c1], d1[e], pd1);
+      const int c0 = (o + s) * PK + cl + 16 * e;
+      d[e] = kb[c0];
+      pd = __builtin_fmaf(qb[c0], d[e], pd);
     }
-    pd0 = row16_sum(pd0);
-    pd1 = row16_sum(pd1);
-    if (cl == 0) {
-      Bl[s * kCL + s] = pd0;
-      Bl[(kSB + s) * kCL + kSB + s] = pd1;
-    }
+    pd = row16_sum(pd);
+    if (cl == 0) Bl[(o + s) * kCL + o + s] = pd;
 #pragma unroll
     for (int t = 1; t < kSB; ++t) {
       const bool after = t > s;  // D(t, s) starts at k_s and takes alpha_t only past s
-      float pa0 = 0.0f, pb0 = 0.0f, pa1 = 0.0f, pb1 = 0.0f;
+      float pa = 0.0f, pb = 0.0f;
 #pragma unroll
       for (int e = 0; e < CPT; ++e) {
-        const int c0 = t * PK + cl + 16 * e, c1 = (kSB + t) * PK + cl + 16 * e;
-        d0[e] = after ? d0[e] * ab[c0] : d0[e];
-        d1[e] = after ? d1[e] * ab[c1] : d1[e];
-        pa0 = __builtin_fmaf(kb[c0], d0[e], pa0);
-        pb0 = __builtin_fmaf(qb[c0], d0[e], pb0);
-        pa1 = __builtin_fmaf(kb[c1], d1[e], pa1);
-        pb1 = __builtin_fmaf(qb[c1], d1[e], pb1);
+        const int c0 = (o + t) * PK + cl + 16 * e;
+        d[e] = after ? d[e] * ab[c0] : d[e];
+        pa = __builtin_fmaf(kb[c0], d[e], pa);
+        pb = __builtin_fmaf(qb[c0], d[e], pb);
       }
-      pa0 = row16_sum(pa0);
-      pb0 = row16_sum(pb0);
-      pa1 = row16_sum(pa1);
-      pb1 = row16_sum(pb1);
+      pa = row16_sum(pa);
+      pb = row16_sum(pb);
       if (cl == 0 && after) {
-        Am[t * kCL + s] = pa0;
-        Bl[t * kCL + s] = pb0;
-        Am[(kSB + t) * kCL + kSB + s] = pa1;
-        Bl[(kSB + t) * kCL + kSB + s] = pb1;
+        Am[(o + t) * kCL + o + s] = pa;
+        Bl[(o + t) * kCL + o + s] = pb;
       }
     }
   }
@@ -253,7 +243,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_prep_kernel(ChunkArgs a) {
   // per (key channel, sub-block), all threads: [P k] and [P q] in place of k and q and
   // [R k] in place of alpha, for the thread's own sub-block
   {
-    const int i = threadIdx.x % DK, J = threadIdx.x / DK;  // DK = 128: J in {0, 1}; DK = 64: J in 0..3
+    const int i = threadIdx.x % DK, J = threadIdx.x / DK;  // sub-blocks J = 0, 1 (the other threads idle)
     if (J < 2) {
       const int o = J * kSB;
       float kf[kSB];
@@ -337,7 +327,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_prep_kernel(ChunkArgs a) {
     for (int t = 0; t < kSB; ++t) Tm[(o + t) * (kCL + 1) + o + col] = x[t];
   }
   __syncthreads();
-  {
+  if ((int)threadIdx.x < kSB * kSB) {
     const int t = threadIdx.x / kSB, col = threadIdx.x % kSB;  // one (t, col) of the 16 x 16 block each
     float y = 0.0f;
 #pragma unroll
@@ -345,7 +335,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_prep_kernel(ChunkArgs a) {
     Bl[t * kSB + col] = bet[kSB + t] * y;  // (Diag(beta) A)10 X00; B is already in the workspace
   }
   __syncthreads();
-  {
+  if ((int)threadIdx.x < kSB * kSB) {
     const int t = threadIdx.x / kSB, col = threadIdx.x % kSB;
     float x10 = 0.0f;
 #pragma unroll
@@ -364,7 +354,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_prep_kernel(ChunkArgs a) {
 
   // W = T [Gamma k] and U = T V: 16 x 16 output tiles spread over the waves
   constexpr int TW = DK / 16, TU = DV / 16;
-  for (int tile = wave; tile < 2 * TW; tile += 4) {
+  for (int tile = wave; tile < 2 * TW; tile += NWAVES) {
     const int rt = tile & 1, ct = tile >> 1;
     float av[kCL / 4], bv[kCL / 4];
 #pragma unroll
@@ -380,7 +370,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_prep_kernel(ChunkArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) ws[WS::W + (16 * rt + 4 * g + e) * DK + 16 * ct + m] = acc[e];
   }
-  for (int tile = wave; tile < 2 * TU; tile += 4) {
+  for (int tile = wave; tile < 2 * TU; tile += NWAVES) {
     const int rt = tile & 1, ct = tile >> 1;
     float av[kCL / 4], bv[kCL / 4];
 #pragma unroll
