@@ -75,8 +75,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise FileNotFoundError(
-            f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
-            "or `python gated_delta_rule_98_amd/build.py`")
+            f"{path} is missing: build it with `python gated_delta_rule_98_amd/build.py`")
     lib = ctypes.CDLL(path)
     P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.kda_decode_step.argtypes = [P, i64, i64, P, i32, i32, i32, i32, P, P, P, P, P, P, P, P, P, P]
