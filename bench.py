@@ -572,6 +572,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain device copies of 256 MiB (for counter scaling)")
+    ap.add_argument("--only", default="",
+                    help="comma-separated breakdown parts to run (default: all), e.g. spec_verify,mixed")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -595,18 +597,24 @@ def main():
     h = headline(D, K, synth, args.steps, args.warmup)
     breakdown = None
     if not args.no_breakdown:
-        breakdown = dict(
-            decode_batch_sweep=batch_sweep(D, K, synth, reps=256),
-            b1_latency_1024_steps=b1_latency(D, K, synth),
-            spec_verify_b16_t8=spec_verify(D, K, synth, reps=200),
-            spec_verify_small_batch=spec_verify_small(D, K, synth, reps=200),
-            mixed_b64_gated=mixed(D, K, synth, reps=200),
-            prefill_8k_checkpoint=prefill_8k(D, K, synth, reps=5),
-            prefill_8k_checkpoint_chunked=prefill_8k(D, K, synth, reps=5, chunked=True),
-            state_transfer_64x32_heads=state_transfer(D, K, synth, reps=100),
-            raw_inputs_decode=raw_inputs_decode(D, K, synth, reps=200),
-            headline_same_table_kernel_us=round(h["hot_ms"] * 1e3, 3),
+        parts = dict(
+            decode_batch_sweep=lambda: batch_sweep(D, K, synth, reps=256),
+            b1_latency_1024_steps=lambda: b1_latency(D, K, synth),
+            spec_verify_b16_t8=lambda: spec_verify(D, K, synth, reps=200),
+            spec_verify_small_batch=lambda: spec_verify_small(D, K, synth, reps=200),
+            mixed_b64_gated=lambda: mixed(D, K, synth, reps=200),
+            prefill_8k_checkpoint=lambda: prefill_8k(D, K, synth, reps=5),
+            prefill_8k_checkpoint_chunked=lambda: prefill_8k(D, K, synth, reps=5, chunked=True),
+            state_transfer_64x32_heads=lambda: state_transfer(D, K, synth, reps=100),
+            raw_inputs_decode=lambda: raw_inputs_decode(D, K, synth, reps=200),
         )
+        only = [p for p in args.only.split(",") if p]
+        unknown = [p for p in only if not any(name.startswith(p) for name in parts)]
+        if unknown:
+            print(f"unknown breakdown part(s) {unknown}; parts: {list(parts)}", file=sys.stderr)
+            sys.exit(2)
+        breakdown = {name: fn() for name, fn in parts.items() if not only or any(name.startswith(p) for p in only)}
+        breakdown["headline_same_table_kernel_us"] = round(h["hot_ms"] * 1e3, 3)
     if args.copy_calibration:
         copy_calibration(D)
     cpu = None if args.no_cpu_baseline else cpu_baseline(h["w"])
