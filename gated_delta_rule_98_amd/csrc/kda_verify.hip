@@ -106,18 +106,24 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
   const int nkq = Tb * (DK / 4);
   const int jj = threadIdx.x & (W - 1), sv = v_slot<C>(jj, L.slab);  // blockDim.x is a multiple of W
   const int tsh = __builtin_ctz(W), tstep = blockDim.x >> tsh, tv0 = threadIdx.x >> tsh;
-  auto kq_off = [&](int idx) { return ((row0 + idx / (DK / 4)) * a.H + u.h) * DK + (idx % (DK / 4)) * 4; };
-  auto v_off = [&](int t) { return ((row0 + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj; };
+  // Each array's part for this row and head starts at a uniform (scalar) base;
+  // threads add 32-bit offsets (a token's stride times at most 16 tokens).
+  const uint32_t kq_tok = (uint32_t)a.H * DK, v_tok = (uint32_t)a.H * a.dv;
+  const int64_t kq0 = (row0 * a.H + u.h) * DK, v0 = (row0 * a.H + u.h) * a.dv + (int64_t)u.tile * W;
+  const uint16_t *kbase = a.k + kq0, *qbase = a.q + kq0, *vbase = a.v + v0;
+  const float *abase = a.alpha + kq0, *bbase = a.beta + row0 * a.H + u.h;
+  auto kq_off = [&](int idx) { return (uint32_t)(idx / (DK / 4)) * kq_tok + (uint32_t)(idx % (DK / 4)) * 4; };
+  auto v_off = [&](int t) { return (uint32_t)t * v_tok + (uint32_t)jj; };
   // (unconditional loads at clamped, in-bounds indices: straight-line code
   // keeps the compiler from waiting for them before the state loads go out)
-  const int64_t off0 = kq_off(min((int)threadIdx.x, nkq - 1));
-  const uint2 kb0 = *reinterpret_cast<const uint2 *>(a.k + off0);
-  const uint2 qb0 = *reinterpret_cast<const uint2 *>(a.q + off0);
-  const float4 al0 = *reinterpret_cast<const float4 *>(a.alpha + off0);
-  const int64_t voff0 = v_off(min(tv0, Tb - 1));
-  const uint16_t vb0 = a.v[voff0];
-  const uint16_t gb0 = GATE ? a.gate[voff0] : (uint16_t)0;
-  const float bt0 = a.beta[(row0 + min((int)threadIdx.x, Tb - 1)) * a.H + u.h];
+  const uint32_t off0 = kq_off(min((int)threadIdx.x, nkq - 1));
+  const uint2 kb0 = *reinterpret_cast<const uint2 *>(kbase + off0);
+  const uint2 qb0 = *reinterpret_cast<const uint2 *>(qbase + off0);
+  const float4 al0 = *reinterpret_cast<const float4 *>(abase + off0);
+  const uint32_t voff0 = v_off(min(tv0, Tb - 1));
+  const uint16_t vb0 = vbase[voff0];
+  const uint16_t gb0 = GATE ? a.gate[v0 + voff0] : (uint16_t)0;
+  const float bt0 = bbase[(uint32_t)min((int)threadIdx.x, Tb - 1) * (uint32_t)a.H];
   __builtin_amdgcn_sched_barrier(0);  // keep the issue order: inputs, then state
   float4 s[C][NV];
   load_tile<DK, C, kVerifyLoadStream>(s, S, L);
@@ -133,12 +139,12 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
     *reinterpret_cast<float4 *>(st.q(t) + i) = unpack_bf16x4(qb);
     *reinterpret_cast<float4 *>(st.a(t) + i) = al;
   };
+  const int64_t r0 = (int64_t)u.b * a.T_max * a.H + u.h;  // replay buffer: row b, token 0, head h
   auto copy_kq = [&](int idx, uint2 kb, float4 al) {
     if (replay && u.tile == 0) {
-      const int t = idx / (DK / 4), i = (idx % (DK / 4)) * 4;
-      const int64_t d = (((int64_t)u.b * a.T_max + t) * a.H + u.h) * DK + i;
-      *reinterpret_cast<uint2 *>(a.rk + d) = kb;
-      *reinterpret_cast<float4 *>(a.ralpha + d) = al;
+      const uint32_t d = kq_off(idx);
+      *reinterpret_cast<uint2 *>(a.rk + r0 * DK + d) = kb;
+      *reinterpret_cast<float4 *>(a.ralpha + r0 * DK + d) = al;
     }
   };
   auto put_v = [&](int t, uint16_t vb, uint16_t gb) {
@@ -146,22 +152,22 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
     if constexpr (GATE) st.g[t * W + jj] = bf16_to_f32(gb);
   };
   auto copy_v = [&](int t, uint16_t vb) {
-    if (replay) a.rv[(((int64_t)u.b * a.T_max + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj] = vb;
+    if (replay) a.rv[r0 * a.dv + (int64_t)u.tile * W + v_off(t)] = vb;
   };
   if ((int)threadIdx.x < nkq) put_kq(threadIdx.x, kb0, qb0, al0);
   if (tv0 < Tb) put_v(tv0, vb0, gb0);
   if ((int)threadIdx.x < Tb) st.beta[threadIdx.x] = bt0;
   // further rounds (more than blockDim.x staging items)
   for (int idx = threadIdx.x + blockDim.x; idx < nkq; idx += blockDim.x) {
-    const int64_t off = kq_off(idx);
-    const uint2 kb = *reinterpret_cast<const uint2 *>(a.k + off), qb = *reinterpret_cast<const uint2 *>(a.q + off);
-    const float4 al = *reinterpret_cast<const float4 *>(a.alpha + off);
+    const uint32_t off = kq_off(idx);
+    const uint2 kb = *reinterpret_cast<const uint2 *>(kbase + off), qb = *reinterpret_cast<const uint2 *>(qbase + off);
+    const float4 al = *reinterpret_cast<const float4 *>(abase + off);
     put_kq(idx, kb, qb, al);
     copy_kq(idx, kb, al);
   }
   for (int t = tv0 + tstep; t < Tb; t += tstep) {
-    const uint16_t vb = a.v[v_off(t)];
-    put_v(t, vb, GATE ? a.gate[v_off(t)] : (uint16_t)0);
+    const uint16_t vb = vbase[v_off(t)];
+    put_v(t, vb, GATE ? a.gate[v0 + v_off(t)] : (uint16_t)0);
     copy_v(t, vb);
   }
   __syncthreads();
@@ -201,7 +207,16 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
     pv += W;
   }
   if (inplace) store_tile<DK, C, kVerifyStoreStream>(S, s, L);
-  const int64_t obase = ((row0 + L.r) * a.H + u.h) * a.dv + (int64_t)u.tile * W + L.col0;
+  // outputs: lane r writes token r's columns at uniform base v0 plus a 32-bit offset
+  float *out32 = a.out + v0;
+  uint16_t *out16 = reinterpret_cast<uint16_t *>(a.out) + v0;
+  const uint32_t ooff = (uint32_t)L.r * v_tok + (uint32_t)L.col0;
+  auto put_o = [&](uint32_t off, float y) {
+    if constexpr (BF16)
+      out16[off] = f32_to_bf16(y);
+    else
+      out32[off] = y;
+  };
   if constexpr (GATE) {
     // the gate's sum of squares over the head: per lane, then over the wave's
     // four rows (in the order (row 0 + row 1) + (row 2 + row 3)), then over the
@@ -219,14 +234,13 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
       for (int c = 0; c < C; ++c) {
         const int j = L.col0 + c * L.slab;
         const float wj = a.weight ? a.weight[j] : 1.0f;
-        put_out(a, BF16, obase + c * L.slab,
-                gate_apply(a, part + L.r * kMaxWaves, keep[c], st.g[L.r * W + j], wj));
+        put_o(ooff + c * L.slab, gate_apply(a, part + L.r * kMaxWaves, keep[c], st.g[L.r * W + j], wj));
       }
     }
   } else {
     if (L.r < Tb) {
 #pragma unroll
-      for (int c = 0; c < C; ++c) put_out(a, BF16, obase + c * L.slab, keep[c]);
+      for (int c = 0; c < C; ++c) put_o(ooff + c * L.slab, keep[c]);
     }
   }
   // the first round's replay copies (see the staging above). With prepared
@@ -247,7 +261,7 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
   }
   if (tv0 < Tb) copy_v(tv0, (uint16_t)(__float_as_uint(st.v[tv0 * W + sv]) >> 16));
   if ((int)threadIdx.x < Tb && replay && u.tile == 0)
-    a.rbeta[((int64_t)u.b * a.T_max + threadIdx.x) * a.H + u.h] = RAW ? bt0 : st.beta[threadIdx.x];
+    a.rbeta[r0 + (uint32_t)threadIdx.x * (uint32_t)a.H] = RAW ? bt0 : st.beta[threadIdx.x];
 }
 
 
