@@ -372,15 +372,19 @@ int kda_verify_chunk(float *cache, int64_t num_slots, int64_t slot_stride, const
   const int form = opts ? opts->verify_form : KDA_VERIFY_AUTO;
   if (form != KDA_VERIFY_AUTO && form != KDA_VERIFY_RECURRENT && form != KDA_VERIFY_CHUNKED)
     return KDA_ERR_INVALID;
-  const bool chunk_fits = mode == KDA_REPLAY && !t1_inplace && epi == nullptr && dv % kChunkW == 0 &&
-                          !a.raw && !a.out_bf16;
+  const bool chunk_fits = mode == KDA_REPLAY && !t1_inplace && epi == nullptr && !a.raw && !a.out_bf16;
   if (form == KDA_VERIFY_CHUNKED && (!chunk_fits || (opts && opts->tile_w != 0))) return KDA_ERR_UNSUPPORTED;
-  // Measured on MI355X (B=16, H=32, d=128, 8 drafts): the chunk form takes ~31 us against
-  // ~19 us token by token, so the automatic choice is the recurrent kernel.
-  const bool chunked = form == KDA_VERIFY_CHUNKED;
+  // Automatic choice, from graph-timed runs on MI355X at H = 32, d = 128 with every row
+  // holding T tokens: the chunk form is faster from 8 tokens once there are at least 512
+  // (row, head) groups (B = 16, T = 8: 12.0 against 15.1 us; B = 64, T = 8: 42.7 against
+  // 59.4 us); with fewer tokens or groups its longer per-group latency loses (B = 4,
+  // T = 8: 7.7 against 7.0 us; B = 64, T = 4: 40.3 against 37.9 us).
+  const bool chunked = form == KDA_VERIFY_CHUNKED ||
+                       (form == KDA_VERIFY_AUTO && chunk_fits && (!opts || opts->tile_w == 0) && T_max >= 8 &&
+                        (int64_t)B * H >= 512);
   Launch l;
   if (chunked) {
-    l = {kChunkW, 4, 0};
+    l = {dv, dv / 16, 0};
   } else {
     KDA_TRY(choose_width(KIND_VERIFY, B, H, dv, epi != nullptr, opts ? opts->tile_w : 0, &l));
   }
@@ -419,8 +423,8 @@ int kda_verify_chunk(float *cache, int64_t num_slots, int64_t slot_stride, const
   const int64_t units = (int64_t)B * H * a.ntile;
   if (chunked) {
     if (units > 0x7fffffff) return KDA_ERR_UNSUPPORTED;
-    const void *fn = verify_chunk_kernel_for(dk);
-    return launch_fn(fn, units, 256, chunk_lds_bytes(dk, T_max), a, stream);
+    const void *fn = verify_chunk_kernel_for(dk, dv, T_max);
+    return launch_fn(fn, units, 64 * l.waves, chunk_verify_lds_bytes(dk, dv, T_max), a, stream);
   }
   return launch(KIND_VERIFY, epi != nullptr, dk, l, units, staged_bytes(dk, T_max, l.W, epi != nullptr), a,
                 stream);

@@ -1,5 +1,5 @@
-// kda_chunk.h - interface of the chunk form of prefill (kda_prefill_chunk.hip)
-// to the C ABI in kda_api.hip.
+// kda_chunk.h - interface of the chunk forms of prefill (kda_prefill_chunk.hip)
+// and verify (kda_verify_chunk.hip) to the C ABI in kda_api.hip.
 
 #pragma once
 
@@ -32,5 +32,10 @@ size_t prefill_chunk_ws_floats(int dk, int dv);
 // Kernel handles: the per-chunk precompute and the sequential pass over chunks.
 const void *prefill_chunk_prep_kernel_for(int dk, int dv);
 const void *prefill_chunk_state_kernel_for(int dk, int dv);
+
+// Chunk form of verify: one workgroup of dv / 16 waves per (row, head), its
+// dynamic LDS bytes, and the kernel handle (dk, dv in {64, 128}, T_max <= 16).
+size_t chunk_verify_lds_bytes(int dk, int dv, int T_max);
+const void *verify_chunk_kernel_for(int dk, int dv, int T_max);
 
 }  // namespace kda

@@ -537,15 +537,11 @@ const void *decode_kernel_for(int dk, int C, bool gate, int io);    // kda_decod
 const void *verify_kernel_for(int dk, int C, bool gate, int io, bool perpos);  // kda_verify.hip
 const void *commit_replay_kernel_for(int dk, int C);                // kda_verify.hip
 const void *commit_copy_kernel_for(int dk, int C);                  // kda_verify.hip
-const void *verify_chunk_kernel_for(int dk);                        // kda_verify_chunk.hip
 const void *prefill_kernel_for(int dk, int C, int io);              // kda_prefill.hip
 const void *state_copy_kernel_for(bool pack);                       // kda_state.hip
 
 // Dynamic LDS bytes of the kernels that take it.
 size_t staged_bytes(int dk, int T_max, int W, bool gate);           // verify, replay commit
-size_t chunk_lds_bytes(int dk, int T_max);                          // chunk form of verify
 size_t prefill_lds_bytes(int dk, int W);                            // prefill
-
-constexpr int kChunkW = 64;  // value columns per workgroup of the chunk form of verify
 
 }  // namespace kda

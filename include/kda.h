@@ -128,9 +128,10 @@ typedef struct kda_replay_buf {
  *     commit, so it serves KDA_REPLAY rows that are not updated in place and
  *     have no output gate. Outputs agree with the recurrent form to rounding;
  *     replay buffers and committed states are identical.
- *   KDA_VERIFY_AUTO: the faster form on MI355X, currently the recurrent one
- *     (the chunk form's per-head coupling and triangular solve cost more than
- *     the MFMA products save at up to 16 tokens). */
+ *   KDA_VERIFY_AUTO: the faster form on MI355X: the chunk form where it applies,
+ *     with tile_w = 0, T_max >= 8 and B * H >= 512; the recurrent form
+ *     otherwise (fewer tokens or (row, head) groups leave the chunk form's
+ *     per-group latency exposed). */
 enum kda_verify_form { KDA_VERIFY_AUTO = 0, KDA_VERIFY_RECURRENT = 1, KDA_VERIFY_CHUNKED = 2 };
 
 /* Option flags (kda_options.flags, OR-ed).

@@ -277,10 +277,12 @@ def test_empty_chunk_is_a_no_op():
 
 
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
-def test_chunked_form_matches_oracle_and_recurrent_form(dk, dv):
+@pytest.mark.parametrize("seqlens", [[1, 2, 3, 5, 7, 8, 9, 11, 13, 15, 16, 4], [1, 2, 3, 5, 7, 8, 6, 4, 8]],
+                         ids=["upto16", "upto8"])
+def test_chunked_form_matches_oracle_and_recurrent_form(dk, dv, seqlens):
     """Replay-mode verify in chunk form (MFMA products with the committed state):
-    every length from 1 to 16, a padding row, decays spanning (0, 1)."""
-    seqlens = [1, 2, 3, 5, 7, 8, 9, 11, 13, 15, 16, 4]
+    ragged lengths with a padding row, decays spanning (0, 1). Up to 8 tokens the
+    kernel stacks keys and queries in one product; longer rows take two."""
     w = synth.make(len(seqlens), 6, dk, dv, seqlens=seqlens, num_slots=16, state_std=0.05, seed=51)
     slots = w.slot_ids.copy()
     slots[3] = -1
@@ -310,14 +312,16 @@ def test_chunked_form_matches_oracle_and_recurrent_form(dk, dv):
     assert rel_l2(outs[K.KDA_VERIFY_CHUNKED][live], outs[K.KDA_VERIFY_RECURRENT][live]) <= 1e-5
 
 
-def test_chunked_form_with_extreme_decays():
+@pytest.mark.parametrize("seqlens", [[16, 16, 9], [8, 8, 5]], ids=["upto16", "upto8"])
+def test_chunked_form_with_extreme_decays(seqlens):
     """Decays near 0 and exactly 1 in the same chunk: running products stay finite."""
-    w = synth.make(3, 4, 128, 128, seqlens=[16, 16, 9], num_slots=4, state_std=0.05, seed=52)
+    w = synth.make(3, 4, 128, 128, seqlens=seqlens, num_slots=4, state_std=0.05, seed=52)
     rng = np.random.Generator(np.random.PCG64(53))
     alpha = w.alpha.copy()
-    alpha[0, :16] = np.where(rng.random(alpha[0, :16].shape) < 0.3, 1e-30, alpha[0, :16])
-    alpha[0, 16:32] = 1.0
-    alpha[0, 32:] = 1e-7
+    c = w.cu_seqlens
+    alpha[0, c[0]:c[1]] = np.where(rng.random(alpha[0, c[0]:c[1]].shape) < 0.3, 1e-30, alpha[0, c[0]:c[1]])
+    alpha[0, c[1]:c[2]] = 1.0
+    alpha[0, c[2]:] = 1e-7
     w.alpha = alpha.astype(np.float32)
     ref_out, _, _, rc = _oracle_verify(w, K.KDA_REPLAY)
     assert rc == 0
@@ -328,6 +332,22 @@ def test_chunked_form_with_extreme_decays():
     o = out.cpu().numpy()
     assert np.all(np.isfinite(o))
     assert rel_l2(o, ref_out) <= OUT_TOL
+
+
+@pytest.mark.parametrize("B,T,expect", [(16, 8, K.KDA_VERIFY_CHUNKED), (4, 8, K.KDA_VERIFY_RECURRENT),
+                                         (16, 4, K.KDA_VERIFY_RECURRENT)])
+def test_auto_form_choice(B, T, expect):
+    """The automatic form is the chunk form from 8 tokens and 512 (row, head) groups,
+    the recurrent form below (both are deterministic, so the outputs match bit for bit)."""
+    w = synth.make(B, 32, 128, 128, seqlens=[T] * B, num_slots=B, state_std=0.05, seed=60 + B + T)
+    outs = {}
+    for form in (K.KDA_VERIFY_AUTO, expect):
+        cache_d = f32(w.cache)
+        log(f"auto form B={B} T={T}: form {form}")
+        out, _, _ = _verify(w, cache_d, K.KDA_REPLAY, form=form)
+        torch.cuda.synchronize()
+        outs[form] = bits(out)
+    assert np.array_equal(outs[K.KDA_VERIFY_AUTO], outs[expect])
 
 
 def test_chunked_form_rejected_where_it_does_not_apply():
