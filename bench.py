@@ -343,21 +343,24 @@ def spec_verify(D, K, synth, reps):
         res[name] = dict(verify_us=round(v_ms * 1e3, 3), verify_bytes=vb, verify_gbs=round(vb / v_ms / 1e6, 1),
                          commit_us=round(c_ms * 1e3, 3), commit_bytes=cb, commit_gbs=round(cb / c_ms / 1e6, 1),
                          verify_plus_commit_us=round(p_ms * 1e3, 3), total_bytes=vb + cb,
-                         tile_w=K.kda_query_variant(w.B, H, d, d, T_max=T, op=K.KDA_OP_VERIFY)[0])
+                         verify_form="automatic (chunk form at this shape)" if mode == 0 else "recurrent",
+                         recurrent_tile_w=K.kda_query_variant(w.B, H, d, d, T_max=T, op=K.KDA_OP_VERIFY)[0])
         log(f"spec_verify {name}: verify {v_ms * 1e3:.2f} us ({vb / v_ms / 1e6:.0f} GB/s), "
             f"commit {c_ms * 1e3:.2f} us ({cb / c_ms / 1e6:.0f} GB/s), verify+commit {p_ms * 1e3:.2f} us")
 
-    # the replay-mode verify in chunk form (MFMA products with the committed state), for comparison
-    def verify_chunked(i):
-        K.kda_verify_chunk(cache, tables[i % len(tables)], cu, T, x["q"], x["k"], x["v"], x["alpha"], x["beta"],
-                           out, mode=0, replay=rbs[i % 4], verify_form=K.KDA_VERIFY_CHUNKED)
-
-    for i in range(8):
-        verify_chunked(i)
-    ch_ms = graph_ms(D, verify_chunked, reps)
+    # replay-mode verify in each form explicitly: the automatic choice above is the chunk
+    # form (MFMA products with the committed state) at this shape
     vb = verify_bytes(w.n_tok, w.B, H, d, d, 0, T)
-    res["replay_chunked_form"] = dict(verify_us=round(ch_ms * 1e3, 3), verify_gbs=round(vb / ch_ms / 1e6, 1))
-    log(f"spec_verify replay, chunk form: verify {ch_ms * 1e3:.2f} us")
+    for form, name in ((K.KDA_VERIFY_CHUNKED, "chunk"), (K.KDA_VERIFY_RECURRENT, "recurrent")):
+        def verify_form(i, form=form):
+            K.kda_verify_chunk(cache, tables[i % len(tables)], cu, T, x["q"], x["k"], x["v"], x["alpha"],
+                               x["beta"], out, mode=0, replay=rbs[i % 4], verify_form=form)
+
+        for i in range(8):
+            verify_form(i)
+        f_ms = graph_ms(D, verify_form, reps)
+        res[f"replay_{name}_form"] = dict(verify_us=round(f_ms * 1e3, 3), verify_gbs=round(vb / f_ms / 1e6, 1))
+        log(f"spec_verify replay, {name} form: verify {f_ms * 1e3:.2f} us")
     return res
 
 

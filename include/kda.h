@@ -304,9 +304,11 @@ int kda_state_unpack(float *cache, int64_t num_slots, int64_t slot_stride,
  * these sizes (tile_w value columns per workgroup, threads per workgroup),
  * chosen from the batch size and head count when requested_tile_w == 0 (the
  * scheduling by batch size and per-GPU head count of "Hyper Optimizing Kimi K3
- * in vLLM", section "Finding time between operators"). Returns
- * KDA_ERR_UNSUPPORTED for shapes the library does not run, KDA_ERR_INVALID for
- * an unknown op or non-positive sizes.
+ * in vLLM", section "Finding time between operators"). For KDA_OP_VERIFY it is
+ * the shape of the recurrent form; where the automatic choice takes the chunk
+ * form instead (see kda_verify_form), that kernel runs dv columns and 4 * dv
+ * threads per workgroup. Returns KDA_ERR_UNSUPPORTED for shapes the library
+ * does not run, KDA_ERR_INVALID for an unknown op or non-positive sizes.
  */
 int kda_query_variant(int32_t op, int32_t B, int32_t H, int32_t dk, int32_t dv, int32_t T_max,
                       int32_t epilogue, int32_t requested_tile_w,
