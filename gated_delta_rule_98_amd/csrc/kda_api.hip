@@ -15,12 +15,14 @@ namespace {
 enum Kind { KIND_DECODE, KIND_VERIFY, KIND_COMMIT_REPLAY, KIND_COMMIT_COPY, KIND_PREFILL };
 
 struct Launch {
-  int W, waves, C;
+  int W, waves, C;  // C = 0: column pairs (decode_pair_kernel), one float4 per lane
 };
 
-// Legal tile widths and their (waves, slabs per lane).
+// Legal tile widths and their (waves, slabs per lane). Two columns per
+// workgroup is the column-pair layout of the single-token step at dk = 128.
 bool launch_of_width(int W, Launch *l) {
   switch (W) {
+    case 2: *l = {2, 1, 0}; return true;
     case 4: *l = {4, 1, 1}; return true;
     case 8: *l = {8, 2, 1}; return true;
     case 16: *l = {16, 4, 1}; return true;
@@ -38,14 +40,15 @@ bool dims_supported(int dk, int dv) { return (dk == 64 || dk == 128) && (dv == 6
 //  * single-token step: the widest tile (64, 32 or 16 columns) that still gives
 //    at least 256 workgroups, i.e. one per CU, so a small batch spreads its state
 //    over the whole chip; once that would exceed 1024 workgroups the step is a
-//    pure stream and one-wave workgroups of 4 columns sustain the highest rate;
+//    pure stream and one-wave workgroups sustain the highest rate: column pairs
+//    at dk = 128, 4 columns at dk = 64 (one float4 of state per lane either way);
 //    at exactly 512 heads of 128 columns, 128-column tiles (two per CU);
 //  * verify (T tokens per row, VALU-heavy): 32 columns while that gives at
 //    least 256 workgroups, 16 below that, then 8;
 //  * replay commit: 32 columns from 2048 workgroups up, 16 columns down to 256
 //    workgroups, then 8;
 //  * per-position copy commit: 16 columns.
-int choose_width(Kind kind, int64_t rows, int H, int dv, bool gate, int requested, Launch *l) {
+int choose_width(Kind kind, int64_t rows, int H, int dk, int dv, bool gate, int requested, Launch *l) {
   if (gate) {
     // the gate's RMS norm spans the whole head: one workgroup owns all dv columns,
     // with two slabs per lane (1024 threads at dv = 128) to keep registers low
@@ -63,6 +66,7 @@ int choose_width(Kind kind, int64_t rows, int H, int dv, bool gate, int requeste
   }
   if (requested != 0) {
     if (requested > dv || dv % requested != 0 || !launch_of_width(requested, l)) return KDA_ERR_UNSUPPORTED;
+    if (l->C == 0 && (kind != KIND_DECODE || dk != 128)) return KDA_ERR_UNSUPPORTED;
     return KDA_OK;
   }
   const int64_t heads = rows * H;
@@ -75,7 +79,7 @@ int choose_width(Kind kind, int64_t rows, int H, int dv, bool gate, int requeste
           break;
         }
       }
-      if (heads * (dv / W) > 1024) W = 4;
+      if (heads * (dv / W) > 1024) W = dk == 128 ? 2 : 4;
       // exactly two 128-column workgroups per CU (512 on MI355X's 256 CUs): measured
       // 7-9% faster than 64 columns at H = 16, 32 and 64
       if (dv == 128 && heads == 512) W = 128;
@@ -120,7 +124,9 @@ int launch(Kind kind, bool gate, int dk, const Launch &l, int64_t units, size_t 
   const int io = (a.raw ? kIoRaw : 0) | (a.out_bf16 ? kIoBf16 : 0);
   const void *fn = nullptr;
   switch (kind) {
-    case KIND_DECODE: fn = decode_kernel_for(dk, l.C, gate, io); break;
+    case KIND_DECODE:
+      fn = l.C == 0 ? (dk == 128 && !gate ? decode_pair_kernel_for(io) : nullptr) : decode_kernel_for(dk, l.C, gate, io);
+      break;
     case KIND_VERIFY: fn = verify_kernel_for(dk, l.C, gate, io, a.mode == KDA_PER_POSITION); break;
     case KIND_COMMIT_REPLAY: fn = gate ? nullptr : commit_replay_kernel_for(dk, l.C); break;
     case KIND_COMMIT_COPY: fn = gate ? nullptr : commit_copy_kernel_for(dk, l.C); break;
@@ -274,7 +280,7 @@ int kda_prefill(float *cache, int64_t num_slots, int64_t slot_stride, const int3
   }
   if (!aligned(cu_seqlens, 4) || (dev_err && !aligned(dev_err, 4))) return KDA_ERR_ALIGN;
   Launch l;
-  KDA_TRY(choose_width(KIND_PREFILL, B, H, dv, false, opts ? opts->tile_w : 0, &l));
+  KDA_TRY(choose_width(KIND_PREFILL, B, H, dk, dv, false, opts ? opts->tile_w : 0, &l));
 
   a.cache = cache;
   a.num_slots = num_slots;
@@ -319,7 +325,7 @@ int kda_decode_step(float *cache, int64_t num_slots, int64_t slot_stride, const 
   KDA_TRY(check_gate(epi));
   if (dev_err && !aligned(dev_err, 4)) return KDA_ERR_ALIGN;
   Launch l;
-  KDA_TRY(choose_width(KIND_DECODE, B, H, dv, epi != nullptr, opts ? opts->tile_w : 0, &l));
+  KDA_TRY(choose_width(KIND_DECODE, B, H, dk, dv, epi != nullptr, opts ? opts->tile_w : 0, &l));
 
   a.cache = cache;
   a.num_slots = num_slots;
@@ -386,7 +392,7 @@ int kda_verify_chunk(float *cache, int64_t num_slots, int64_t slot_stride, const
   if (chunked) {
     l = {dv, dv / 16, 0};
   } else {
-    KDA_TRY(choose_width(KIND_VERIFY, B, H, dv, epi != nullptr, opts ? opts->tile_w : 0, &l));
+    KDA_TRY(choose_width(KIND_VERIFY, B, H, dk, dv, epi != nullptr, opts ? opts->tile_w : 0, &l));
   }
 
   a.cache = cache;
@@ -453,7 +459,7 @@ int kda_replay_commit(float *cache, int64_t num_slots, int64_t slot_stride, cons
       (dev_err && !aligned(dev_err, 4)))
     return KDA_ERR_ALIGN;
   Launch l;
-  KDA_TRY(choose_width(mode == KDA_REPLAY ? KIND_COMMIT_REPLAY : KIND_COMMIT_COPY, B, H, dv, false,
+  KDA_TRY(choose_width(mode == KDA_REPLAY ? KIND_COMMIT_REPLAY : KIND_COMMIT_COPY, B, H, dk, dv, false,
                        opts ? opts->tile_w : 0, &l));
 
   a.cache = cache;
@@ -500,7 +506,7 @@ int kda_query_variant(int32_t op, int32_t B, int32_t H, int32_t dk, int32_t dv, 
   if (!dims_supported(dk, dv) || T_max < 1 || (kind != KIND_PREFILL && T_max > kMaxT)) return KDA_ERR_UNSUPPORTED;
   if (epilogue && kind != KIND_DECODE && kind != KIND_VERIFY) return KDA_ERR_INVALID;
   Launch l;
-  KDA_TRY(choose_width(kind, B, H, dv, epilogue != 0, requested_tile_w, &l));
+  KDA_TRY(choose_width(kind, B, H, dk, dv, epilogue != 0, requested_tile_w, &l));
   if (tile_w) *tile_w = l.W;
   if (threads) *threads = 64 * l.waves;
   return KDA_OK;

@@ -93,6 +93,41 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// Column pairs (the single-token step's stream shape at dk = 128): a column is
+// owned by 32 lanes, an even DPP row and the odd row after it; lane r of the
+// even row holds key channels 4r..4r+3 and lane r of the odd row 64+4r..64+4r+3,
+// one float4 each, so a wave covers two columns, one contiguous 1 KiB span.
+// gfx950's v_permlane16_swap exchanges rows 2m and 2m+1 of two registers; with
+// the same register twice, its first result holds the even row's value in both
+// rows and its second the odd row's.
+__device__ __forceinline__ float from_even_row(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]);
+}
+
+__device__ __forceinline__ float from_odd_row(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[1]);
+}
+
+// dot(s, x) over a column pair's 128 channels with the same operations, in the
+// same order, as row16_sum(lane_dot<2>(s, x)): the even row's four-term chain
+// moves to the odd row, which continues it over its own channels and runs the
+// butterfly; every lane receives the odd row's total. The even row's second
+// chain and butterfly are discarded.
+__device__ __forceinline__ float pair_dot(const float4 &s, const float4 &x) {
+  float p = s.x * x.x;
+  p = __builtin_fmaf(s.y, x.y, p);
+  p = __builtin_fmaf(s.z, x.z, p);
+  p = __builtin_fmaf(s.w, x.w, p);
+  p = from_even_row(p);
+  p = __builtin_fmaf(s.x, x.x, p);
+  p = __builtin_fmaf(s.y, x.y, p);
+  p = __builtin_fmaf(s.z, x.z, p);
+  p = __builtin_fmaf(s.w, x.w, p);
+  return from_odd_row(row16_sum(p));
+}
+
 // This lane's share of dot(s, x) over its key channels, in a fixed order.
 template <int NV>
 __device__ __forceinline__ float lane_dot(const float4 (&s)[NV], const float4 (&x)[NV]) {
@@ -534,6 +569,7 @@ const void *io_variant(int io) {
 }
 
 const void *decode_kernel_for(int dk, int C, bool gate, int io);    // kda_decode.hip
+const void *decode_pair_kernel_for(int io);                         // kda_decode.hip, dk = 128
 const void *verify_kernel_for(int dk, int C, bool gate, int io, bool perpos);  // kda_verify.hip
 const void *commit_replay_kernel_for(int dk, int C);                // kda_verify.hip
 const void *commit_copy_kernel_for(int dk, int C);                  // kda_verify.hip

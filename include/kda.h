@@ -41,9 +41,9 @@
  * reentrant. Within one call, slot ids must be distinct, and no output buffer
  * may overlap an input or another output.
  *
- * Rows and slots. slot_ids[b] < 0 marks a padding row: nothing is read or
- * written for it (its output rows keep their contents). A slot id >=
- * num_slots is a device-side error (below).
+ * Rows and slots. slot_ids[b] < 0 marks a padding row: its state is neither
+ * read nor written and its output rows keep their contents (its inputs may
+ * still be read). A slot id >= num_slots is a device-side error (below).
  *
  * Errors. Every entry point returns KDA_OK or a negative KDA_ERR_* code. The
  * host checks run before anything is enqueued; on an error nothing is
@@ -159,8 +159,9 @@ enum kda_flag { KDA_RAW_INPUTS = 1, KDA_OUT_BF16 = 2 };
 typedef struct kda_options {
     int32_t tile_w;      /* value columns per workgroup of the recurrent kernels: 0 = chosen from
                             (B, H); otherwise one of 4, 8, 16, 32, 64, 128 with tile_w <= dv (and
-                            tile_w == dv with the gate). Results are bit-identical for every legal
-                            width. */
+                            tile_w == dv with the gate), or 2 for kda_decode_step at dk = 128
+                            without the gate (column pairs). Results are bit-identical for every
+                            legal width. */
     int32_t verify_form; /* a kda_verify_form; KDA_VERIFY_CHUNKED where it does not apply is
                             KDA_ERR_UNSUPPORTED */
     int32_t flags;       /* kda_flag bits */

@@ -56,8 +56,19 @@ def test_query_variant_launch_shapes():
     assert q(16, 32, 128, 128) == (128, 256)        # 512 heads: two 128-column workgroups per CU
     assert q(12, 32, 128, 128) == (64, 256)         # 768 workgroups
     assert q(32, 16, 128, 128) == (128, 256) and q(8, 64, 128, 128) == (128, 256)
-    assert q(32, 32, 128, 128) == (4, 64)
-    assert q(64, 32, 128, 128) == (4, 64)           # 32768 one-wave workgroups
+    assert q(32, 32, 128, 128) == (2, 64)
+    assert q(64, 32, 128, 128) == (2, 64)           # 65536 one-wave workgroups of column pairs
+    assert q(64, 32, 64, 64) == (4, 64)             # dk = 64: 4 columns, one float4 per lane
+    assert q(64, 32, 64, 128) == (4, 64)
+    # column pairs: only the single-token step at dk = 128, without the gate
+    assert q(3, 5, 128, 128, tile_w=2) == (2, 64) and q(3, 5, 128, 64, tile_w=2) == (2, 64)
+    for bad in (dict(dk=64), dict(op=V, T_max=4), dict(op=CR, T_max=4), dict(op=CC, T_max=4),
+                dict(op=kda.KDA_OP_PREFILL, T_max=100), dict(epilogue=True)):
+        args = dict(B=3, H=5, dk=128, dv=128, tile_w=2)
+        args.update(bad)
+        with pytest.raises(kda.KdaError) as e:
+            q(**args)
+        assert e.value.status == kda.KDA_ERR_UNSUPPORTED, bad
     assert q(1, 4, 64, 64) == (16, 256)
     # verify / replay commit: 32 columns while >= 512 workgroups
     assert q(16, 32, 128, 128, T_max=8, op=V) == (32, 256)

@@ -89,8 +89,8 @@ def test_tile_widths_are_bit_identical(dk, dv):
     cache_ref = w.cache.copy()
     oracle.decode(cache_ref, w.slot_ids, w.q[0], w.k[0], w.v[0], w.alpha[0], w.beta[0])
     first = None
-    for tw in (4, 8, 16, 32, 64, 128):
-        if tw > dv:
+    for tw in (2, 4, 8, 16, 32, 64, 128):
+        if tw > dv or (tw == 2 and dk != 128):
             continue
         cache_d = f32(w.cache)
         out = sentinel((w.B, w.H, dv))
@@ -108,9 +108,10 @@ def test_tile_widths_are_bit_identical(dk, dv):
             assert np.array_equal(got[0], first[0]) and np.array_equal(got[1], first[1]), tw
 
 
-@pytest.mark.parametrize("tile_w", [0, 4])
+@pytest.mark.parametrize("tile_w", [0, 2, 4])
 def test_padding_and_out_of_range_slot(tile_w):
-    """Padding rows and a slot past the cache; tile_w=4 is the one-wave large-batch launch."""
+    """Padding rows and a slot past the cache; tile_w=2 (column pairs) and 4 are the one-wave
+    large-batch launches."""
     w = synth.make(7, 4, 128, 128, num_slots=12, state_std=0.05, seed=22)
     slots = w.slot_ids.copy()
     slots[2] = -1                     # padding row
@@ -179,15 +180,18 @@ def test_slot_offsets_beyond_2_pow_31_floats():
     for b, s in enumerate(far):
         big[s] = f32(w.cache[w.slot_ids[b]])
     x = step_inputs(w, 0)
-    out = torch.empty(w.B, w.H, w.dv, device=dev())
-    log("slot offsets beyond 2^31 floats")
-    K.kda_decode_step(big, i32(far), x["q"], x["k"], x["v"], x["alpha"], x["beta"], out)
-    torch.cuda.synchronize()
     cache_h = w.cache.copy()
     ref, rc = oracle.decode(cache_h, w.slot_ids, w.q[0], w.k[0], w.v[0], w.alpha[0], w.beta[0])
-    assert rel_l2(out.cpu().numpy(), ref) <= OUT_TOL
-    for b, s in enumerate(far):
-        assert rel_l2(big[s].cpu().numpy(), cache_h[w.slot_ids[b]]) <= STATE_TOL
+    for tw in (0, 2):   # the automatic width and column pairs
+        for b, s in enumerate(far):
+            big[s] = f32(w.cache[w.slot_ids[b]])
+        out = torch.empty(w.B, w.H, w.dv, device=dev())
+        log(f"slot offsets beyond 2^31 floats, tile_w={tw}")
+        K.kda_decode_step(big, i32(far), x["q"], x["k"], x["v"], x["alpha"], x["beta"], out, tile_w=tw)
+        torch.cuda.synchronize()
+        assert rel_l2(out.cpu().numpy(), ref) <= OUT_TOL
+        for b, s in enumerate(far):
+            assert rel_l2(big[s].cpu().numpy(), cache_h[w.slot_ids[b]]) <= STATE_TOL
     del big
     torch.cuda.empty_cache()
 
