@@ -303,11 +303,16 @@ def _replay_bufs(torch, dev, B, T, H, dk, dv):
                 alpha=torch.zeros(B, T, H, dk, device=dev), beta=torch.zeros(B, T, H, device=dev))
 
 
-def spec_verify(D, K, synth, reps):
-    """B=16 rows of 8 draft tokens. Each launch takes the next of 16 disjoint slot tables
-    (and of 4 replay / 2 per-position buffers), so state and buffers come from HBM."""
+def spec_verify(D, K, synth, reps, B=16):
+    """B rows of 8 draft tokens (B=16: the speculative-verify workload). Each launch takes the
+    next of the disjoint slot tables (16 at B=16, 4 at B=64) and of 4 replay / 2 per-position
+    buffers, so state and buffers come from HBM."""
     torch = D.torch
-    w = synth.make_workload("spec_verify")
+    if B == 16:
+        w = synth.make_workload("spec_verify")
+    else:
+        w = synth.make(B, 32, 128, 128, seqlens=[8] * B, num_slots=256, state_std=0.02, seed=B,
+                       name=f"spec_verify_b{B}")
     H, d, T = 32, 128, w.T_max
     cache = D.f(w.cache)
     tables = [D.i(t) for t in w.slot_tables]
@@ -345,7 +350,7 @@ def spec_verify(D, K, synth, reps):
                          verify_plus_commit_us=round(p_ms * 1e3, 3), total_bytes=vb + cb,
                          verify_form="automatic (chunk form at this shape)" if mode == 0 else "recurrent",
                          recurrent_tile_w=K.kda_query_variant(w.B, H, d, d, T_max=T, op=K.KDA_OP_VERIFY)[0])
-        log(f"spec_verify {name}: verify {v_ms * 1e3:.2f} us ({vb / v_ms / 1e6:.0f} GB/s), "
+        log(f"spec_verify B={w.B} {name}: verify {v_ms * 1e3:.2f} us ({vb / v_ms / 1e6:.0f} GB/s), "
             f"commit {c_ms * 1e3:.2f} us ({cb / c_ms / 1e6:.0f} GB/s), verify+commit {p_ms * 1e3:.2f} us")
 
     # replay-mode verify in each form explicitly: the automatic choice above is the chunk
@@ -360,7 +365,7 @@ def spec_verify(D, K, synth, reps):
             verify_form(i)
         f_ms = graph_ms(D, verify_form, reps)
         res[f"replay_{name}_form"] = dict(verify_us=round(f_ms * 1e3, 3), verify_gbs=round(vb / f_ms / 1e6, 1))
-        log(f"spec_verify replay, {name} form: verify {f_ms * 1e3:.2f} us")
+        log(f"spec_verify B={w.B} replay, {name} form: verify {f_ms * 1e3:.2f} us")
     return res
 
 
@@ -606,6 +611,7 @@ def main():
             decode_batch_sweep=lambda: batch_sweep(D, K, synth, reps=256),
             b1_latency_1024_steps=lambda: b1_latency(D, K, synth),
             spec_verify_b16_t8=lambda: spec_verify(D, K, synth, reps=200),
+            spec_verify_b64_t8=lambda: spec_verify(D, K, synth, reps=50, B=64),
             spec_verify_small_batch=lambda: spec_verify_small(D, K, synth, reps=200),
             mixed_b64_gated=lambda: mixed(D, K, synth, reps=200),
             prefill_8k_checkpoint=lambda: prefill_8k(D, K, synth, reps=5),

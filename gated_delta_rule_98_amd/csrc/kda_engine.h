@@ -409,9 +409,30 @@ __device__ __forceinline__ void report(int32_t *dev_err, const Unit &u, int bit)
   if (dev_err && u.tile == 0 && u.h == 0 && threadIdx.x == 0) atomicOr(dev_err, bit);
 }
 
-__device__ __forceinline__ bool row_range(const Args &a, int b, int64_t &row0, int &Tb) {
-  const int32_t c0 = a.cu[b], c1 = a.cu[b + 1];
-  if (c0 < 0 || c1 < c0 || c1 > a.n_tok || c1 - c0 > a.T_max) return false;
+// An empty statement that takes three wave-uniform values in scalar registers:
+// every use of them then follows it, so the loads that produce them are all
+// issued first and waited for once (without it the compiler may place a use,
+// and the wait it needs, between two of the loads).
+__device__ __forceinline__ void wait_uniform3(int32_t &x, int32_t &y, int32_t &z) {
+  asm volatile("" : "+s"(x), "+s"(y), "+s"(z));
+}
+
+// A row's slot id and packed token range, requested together and checked after
+// one wait (checked one at a time, each load waits behind the previous check's
+// branch: a chain of scalar round trips ahead of the state load). False for a
+// row to skip: padding (slot < 0, nothing reported), a slot past the cache or
+// a bad token range (reported to dev_err).
+__device__ __forceinline__ bool row_slot_range(const Args &a, const Unit &u, int32_t &slot, int64_t &row0,
+                                               int &Tb) {
+  slot = a.slot_ids[u.b];
+  int32_t c0 = a.cu[u.b], c1 = a.cu[u.b + 1];
+  wait_uniform3(slot, c0, c1);
+  const bool bad_slot = slot >= a.num_slots;
+  const bool bad_range = c0 < 0 || c1 < c0 || c1 > a.n_tok || c1 - c0 > a.T_max;
+  if (slot < 0 || bad_slot || bad_range) {
+    if (slot >= 0) report(a.dev_err, u, bad_slot ? KDA_DEVERR_SLOT : KDA_DEVERR_SEQLEN);
+    return false;
+  }
   row0 = c0;
   Tb = c1 - c0;
   return true;

@@ -80,22 +80,14 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
   constexpr bool RAW = IO & kIoRaw, BF16 = IO & kIoBf16;
   extern __shared__ float4 lds_dyn[];
   const Unit u = unit_of_block_headmajor(a.ntile, a.H, a.B);
-  const int32_t slot = a.slot_ids[u.b];
-  if (slot < 0) return;
-  if (slot >= a.num_slots) {
-    report(a.dev_err, u, KDA_DEVERR_SLOT);
-    return;
-  }
+  const Lane L = lane_geometry();
+  int32_t slot;
   int64_t row0;
   int Tb;
-  if (!row_range(a, u.b, row0, Tb)) {
-    report(a.dev_err, u, KDA_DEVERR_SEQLEN);
-    return;
-  }
+  if (!row_slot_range(a, u, slot, row0, Tb)) return;
   if (Tb == 0) return;
   const bool inplace = Tb == 1 && a.t1_inplace;
   const bool replay = !inplace && !PERPOS;
-  const Lane L = lane_geometry();
   const int W = C * L.slab;
   Staged<DK> st(reinterpret_cast<float *>(lds_dyn), a.T_max, W);
   float *S = a.cache + (int64_t)slot * a.slot_stride + ((int64_t)u.h * a.dv + (int64_t)u.tile * W) * DK;
@@ -272,23 +264,23 @@ __global__ __launch_bounds__(GATE ? 1024 : 256) void verify_kernel(Args a) {
 // Row checks shared by the commit kernels; returns the accepted length, or -1
 // when the row does not run.
 __device__ __forceinline__ int commit_row(const Args &a, const Unit &u, int32_t &slot) {
+  // The row's slot id, token range and accepted length are requested together
+  // and checked after one wait: checked one by one, each load waited behind
+  // the previous check's branch, a chain of scalar round trips ahead of the
+  // state load.
   slot = a.slot_ids[u.b];
-  if (slot < 0) return -1;
-  if (slot >= a.num_slots) {
-    report(a.dev_err, u, KDA_DEVERR_SLOT);
-    return -1;
-  }
-  int Tb = a.T_max;
+  int n = a.accepted[u.b];
+  int32_t c0 = 0, c1 = a.T_max;
   if (a.cu) {
-    int64_t row0;
-    if (!row_range(a, u.b, row0, Tb)) {
-      report(a.dev_err, u, KDA_DEVERR_SEQLEN);
-      return -1;
-    }
+    c0 = a.cu[u.b];
+    c1 = a.cu[u.b + 1];
   }
-  const int n = a.accepted[u.b];
-  if (n < 0 || n > Tb) {
-    report(a.dev_err, u, KDA_DEVERR_ACCEPTED);
+  wait_uniform3(slot, n, c0);
+  const bool bad_slot = slot >= a.num_slots;
+  const bool bad_range = c0 < 0 || c1 < c0 || c1 > a.n_tok || c1 - c0 > a.T_max;
+  const bool bad_n = n < 0 || n > c1 - c0;
+  if (slot < 0 || bad_slot || bad_range || bad_n) {
+    if (slot >= 0) report(a.dev_err, u, bad_slot ? KDA_DEVERR_SLOT : bad_range ? KDA_DEVERR_SEQLEN : KDA_DEVERR_ACCEPTED);
     return -1;
   }
   return n;
@@ -301,10 +293,10 @@ __global__ __launch_bounds__(256) void commit_replay_kernel(Args a) {
   constexpr int NV = DK / 64;
   extern __shared__ float4 lds_dyn[];
   const Unit u = unit_of_block_rows(a.ntile, a.H, a.B);
+  const Lane L = lane_geometry();
   int32_t slot;
   const int n = commit_row(a, u, slot);
   if (n <= 0) return;
-  const Lane L = lane_geometry();
   const int W = C * L.slab;
   Staged<DK> st(reinterpret_cast<float *>(lds_dyn), a.T_max, W);
   // the state tile is requested first, so its HBM latency overlaps the staging

@@ -89,18 +89,10 @@ __global__ __launch_bounds__(64 * NW, 4) void verify_chunk_kernel(Args a) {
   static_assert(2 * DK <= NT, "one decay thread per channel of k and q");
   extern __shared__ float4 lds_dyn[];
   const Unit u = unit_of_block_rows(1, a.H, a.B);
-  const int32_t slot = a.slot_ids[u.b];
-  if (slot < 0) return;
-  if (slot >= a.num_slots) {
-    report(a.dev_err, u, KDA_DEVERR_SLOT);
-    return;
-  }
+  int32_t slot;
   int64_t row0;
   int Tb;
-  if (!row_range(a, u.b, row0, Tb)) {
-    report(a.dev_err, u, KDA_DEVERR_SEQLEN);
-    return;
-  }
+  if (!row_slot_range(a, u, slot, row0, Tb)) return;
   if (Tb == 0) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int j = lane & 15, g = lane >> 4;
