@@ -128,7 +128,11 @@ int launch(Kind kind, bool gate, int dk, const Launch &l, int64_t units, size_t 
       fn = l.C == 0 ? (dk == 128 && !gate ? decode_pair_kernel_for(io) : nullptr) : decode_kernel_for(dk, l.C, gate, io);
       break;
     case KIND_VERIFY: fn = verify_kernel_for(dk, l.C, gate, io, a.mode == KDA_PER_POSITION); break;
-    case KIND_COMMIT_REPLAY: fn = gate ? nullptr : commit_replay_kernel_for(dk, l.C); break;
+    case KIND_COMMIT_REPLAY:
+      // staging before the state tile once the grid exceeds one round of resident
+      // workgroups (8 per CU at these shapes, 2048 on MI355X's 256 CUs)
+      fn = gate ? nullptr : commit_replay_kernel_for(dk, l.C, units > 2048);
+      break;
     case KIND_COMMIT_COPY: fn = gate ? nullptr : commit_copy_kernel_for(dk, l.C); break;
     case KIND_PREFILL: fn = gate ? nullptr : prefill_kernel_for(dk, l.C, io); break;
   }

@@ -592,7 +592,7 @@ const void *io_variant(int io) {
 const void *decode_kernel_for(int dk, int C, bool gate, int io);    // kda_decode.hip
 const void *decode_pair_kernel_for(int io);                         // kda_decode.hip, dk = 128
 const void *verify_kernel_for(int dk, int C, bool gate, int io, bool perpos);  // kda_verify.hip
-const void *commit_replay_kernel_for(int dk, int C);                // kda_verify.hip
+const void *commit_replay_kernel_for(int dk, int C, bool inputs_first);  // kda_verify.hip
 const void *commit_copy_kernel_for(int dk, int C);                  // kda_verify.hip
 const void *prefill_kernel_for(int dk, int C, int io);              // kda_prefill.hip
 const void *state_copy_kernel_for(bool pack);                       // kda_state.hip

@@ -288,7 +288,15 @@ __device__ __forceinline__ int commit_row(const Args &a, const Unit &u, int32_t 
 
 // ReplaySSM commit: reload the committed state, replay the first n buffered
 // tokens with the same column engine, store once.
-template <int DK, int C>
+//
+// Staging order. With FIRST, every thread's first item of each input (k and
+// alpha, v, beta) is requested before the state tile, at clamped, in-bounds
+// indices, so the staging writes wait for the inputs alone and each wave then
+// waits for its own tile in the token loop; otherwise the tile goes first and
+// its latency overlaps the staging loads. Measured on MI355X: inputs first is
+// faster once the grid takes more than one round of resident workgroups, and
+// slower when all of them fit at once (B = 16, T = 8).
+template <int DK, int C, bool FIRST>
 __global__ __launch_bounds__(256) void commit_replay_kernel(Args a) {
   constexpr int NV = DK / 64;
   extern __shared__ float4 lds_dyn[];
@@ -299,23 +307,43 @@ __global__ __launch_bounds__(256) void commit_replay_kernel(Args a) {
   if (n <= 0) return;
   const int W = C * L.slab;
   Staged<DK> st(reinterpret_cast<float *>(lds_dyn), a.T_max, W);
-  // the state tile is requested first, so its HBM latency overlaps the staging
   float *S = a.cache + (int64_t)slot * a.slot_stride + ((int64_t)u.h * a.dv + (int64_t)u.tile * W) * DK;
-  float4 s[C][NV];
-  load_tile<DK, C, kCommitLoadStream>(s, S, L);
-  for (int idx = threadIdx.x; idx < n * (DK / 4); idx += blockDim.x) {
+  const int tid = threadIdx.x, nkq = n * (DK / 4);
+  const int vsh = __builtin_ctz(W), tstep = blockDim.x >> vsh, tv = tid >> vsh;
+  const int jj = tid & (W - 1), sv = v_slot<C>(jj, L.slab);
+  const int64_t row_h = (int64_t)u.b * a.T_max * a.H + u.h;  // (row, token 0, head) in [B][T_max][H]
+  auto kq_at = [&](int idx) { return (row_h + (int64_t)(idx / (DK / 4)) * a.H) * DK + (idx % (DK / 4)) * 4; };
+  auto v_at = [&](int t) { return (row_h + (int64_t)t * a.H) * a.dv + (int64_t)u.tile * W + jj; };
+  auto put_kq = [&](int idx, uint2 kb, float4 al) {
     const int t = idx / (DK / 4), i = (idx % (DK / 4)) * 4;
-    const int64_t d = (((int64_t)u.b * a.T_max + t) * a.H + u.h) * DK + i;
-    *reinterpret_cast<float4 *>(st.k(t) + i) = unpack_bf16x4(*reinterpret_cast<const uint2 *>(a.rk + d));
-    *reinterpret_cast<float4 *>(st.a(t) + i) = *reinterpret_cast<const float4 *>(a.ralpha + d);
+    *reinterpret_cast<float4 *>(st.k(t) + i) = unpack_bf16x4(kb);
+    *reinterpret_cast<float4 *>(st.a(t) + i) = al;
+  };
+  float4 s[C][NV];
+  int idx1 = tid, tv1 = tv;  // first items the loops below still stage
+  if constexpr (FIRST) {
+    const int i0 = min(tid, nkq - 1);
+    const uint2 kb = *reinterpret_cast<const uint2 *>(a.rk + kq_at(i0));
+    const float4 al = *reinterpret_cast<const float4 *>(a.ralpha + kq_at(i0));
+    const uint16_t vb = a.rv[v_at(min(tv, n - 1))];
+    const float bt = a.rbeta[row_h + (int64_t)min(tid, n - 1) * a.H];
+    __builtin_amdgcn_sched_barrier(0);  // keep the issue order: inputs, then state
+    load_tile<DK, C, kCommitLoadStream>(s, S, L);
+    if (tid < nkq) put_kq(tid, kb, al);
+    if (tv < n) st.v[tv * W + sv] = bf16_to_f32(vb);
+    if (tid < n) st.beta[tid] = bt;
+    idx1 = tid + blockDim.x;
+    tv1 = tv + tstep;
+  } else {
+    load_tile<DK, C, kCommitLoadStream>(s, S, L);
   }
-  {
-    const int jj = threadIdx.x & (W - 1), sv = v_slot<C>(jj, L.slab);
-    const int tstep = blockDim.x >> __builtin_ctz(W);
-    for (int t = threadIdx.x >> __builtin_ctz(W); t < n; t += tstep)
-      st.v[t * W + sv] = bf16_to_f32(a.rv[(((int64_t)u.b * a.T_max + t) * a.H + u.h) * a.dv + (int64_t)u.tile * W + jj]);
+  for (int idx = idx1; idx < nkq; idx += blockDim.x)
+    put_kq(idx, *reinterpret_cast<const uint2 *>(a.rk + kq_at(idx)),
+           *reinterpret_cast<const float4 *>(a.ralpha + kq_at(idx)));
+  for (int t = tv1; t < n; t += tstep) st.v[t * W + sv] = bf16_to_f32(a.rv[v_at(t)]);
+  if constexpr (!FIRST) {
+    if (tid < n) st.beta[tid] = a.rbeta[row_h + (int64_t)tid * a.H];
   }
-  if ((int)threadIdx.x < n) st.beta[threadIdx.x] = a.rbeta[((int64_t)u.b * a.T_max + threadIdx.x) * a.H + u.h];
   __syncthreads();
   if (a.raw) {
     prep_staged<DK, Staged<DK>::kRec>(st.k(0), nullptr, st.a(0), st.beta, n);
@@ -340,7 +368,6 @@ __global__ __launch_bounds__(256) void commit_replay_kernel(Args a) {
   store_tile<DK, C, kCommitStoreStream>(S, s, L);
 }
 
-// Per-position commit: copy the state saved after the last accepted token.
 template <int DK, int C>
 __global__ __launch_bounds__(256) void commit_copy_kernel(Args a) {
   constexpr int NV = DK / 64;
@@ -389,23 +416,36 @@ const void *verify_kernel_for(int dk, int C, bool gate, int io, bool perpos) {
   return nullptr;
 }
 
-template <int DK>
-const void *commit_for(bool replay, int C) {
+template <int DK, bool FIRST>
+const void *commit_replay_for(int C) {
   switch (C) {
-    case 1: return replay ? (const void *)commit_replay_kernel<DK, 1> : (const void *)commit_copy_kernel<DK, 1>;
-    case 2: return replay ? (const void *)commit_replay_kernel<DK, 2> : (const void *)commit_copy_kernel<DK, 2>;
-    case 4: return replay ? (const void *)commit_replay_kernel<DK, 4> : (const void *)commit_copy_kernel<DK, 4>;
-    case 8: return replay ? (const void *)commit_replay_kernel<DK, 8> : (const void *)commit_copy_kernel<DK, 8>;
+    case 1: return (const void *)commit_replay_kernel<DK, 1, FIRST>;
+    case 2: return (const void *)commit_replay_kernel<DK, 2, FIRST>;
+    case 4: return (const void *)commit_replay_kernel<DK, 4, FIRST>;
+    case 8: return (const void *)commit_replay_kernel<DK, 8, FIRST>;
   }
   return nullptr;
 }
 
-const void *commit_replay_kernel_for(int dk, int C) {
-  return dk == 64 ? commit_for<64>(true, C) : dk == 128 ? commit_for<128>(true, C) : nullptr;
+template <int DK>
+const void *commit_copy_for(int C) {
+  switch (C) {
+    case 1: return (const void *)commit_copy_kernel<DK, 1>;
+    case 2: return (const void *)commit_copy_kernel<DK, 2>;
+    case 4: return (const void *)commit_copy_kernel<DK, 4>;
+    case 8: return (const void *)commit_copy_kernel<DK, 8>;
+  }
+  return nullptr;
+}
+
+const void *commit_replay_kernel_for(int dk, int C, bool inputs_first) {
+  if (dk == 64) return inputs_first ? commit_replay_for<64, true>(C) : commit_replay_for<64, false>(C);
+  if (dk == 128) return inputs_first ? commit_replay_for<128, true>(C) : commit_replay_for<128, false>(C);
+  return nullptr;
 }
 
 const void *commit_copy_kernel_for(int dk, int C) {
-  return dk == 64 ? commit_for<64>(false, C) : dk == 128 ? commit_for<128>(false, C) : nullptr;
+  return dk == 64 ? commit_copy_for<64>(C) : dk == 128 ? commit_copy_for<128>(C) : nullptr;
 }
 
 }  // namespace kda

@@ -123,6 +123,16 @@ def test_commit_equals_single_token_steps_bitwise():
             assert np.array_equal(bits(out), bits(dec_out))
         else:
             assert rel_l2(out.cpu().numpy(), dec_out.cpu().numpy()) <= 1e-5
+    # both staging orders of the replay commit: at this shape (16 rows x 32 heads) 32-column
+    # tiles give 2048 workgroups (state tile first), 16 and 8 columns 4096 and 8192 (inputs first)
+    cache_v = f32(w.cache)
+    _, rb, _ = _verify(w, cache_v, K.KDA_REPLAY)
+    for tw in (32, 16, 8):
+        cache_c = f32(w.cache)
+        log(f"replay commit, tile_w={tw}")
+        _commit(w, cache_c, K.KDA_REPLAY, acc, rb, None, tile_w=tw)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(cache_c), bits(steps_d)), tw
 
 
 def test_mixed_batch_inplace_gate_and_commit():
