@@ -433,7 +433,7 @@ int kda_verify_chunk(float *cache, int64_t num_slots, int64_t slot_stride, const
   const int64_t units = (int64_t)B * H * a.ntile;
   if (chunked) {
     if (units > 0x7fffffff) return KDA_ERR_UNSUPPORTED;
-    const void *fn = verify_chunk_kernel_for(dk, dv, T_max);
+    const void *fn = verify_chunk_kernel_for(dk, dv, T_max, units);
     return launch_fn(fn, units, 64 * l.waves, chunk_verify_lds_bytes(dk, dv, T_max), a, stream);
   }
   return launch(KIND_VERIFY, epi != nullptr, dk, l, units, staged_bytes(dk, T_max, l.W, epi != nullptr), a,

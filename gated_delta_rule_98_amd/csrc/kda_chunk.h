@@ -36,6 +36,6 @@ const void *prefill_chunk_state_kernel_for(int dk, int dv);
 // Chunk form of verify: one workgroup of dv / 16 waves per (row, head), its
 // dynamic LDS bytes, and the kernel handle (dk, dv in {64, 128}, T_max <= 16).
 size_t chunk_verify_lds_bytes(int dk, int dv, int T_max);
-const void *verify_chunk_kernel_for(int dk, int dv, int T_max);
+const void *verify_chunk_kernel_for(int dk, int dv, int T_max, int64_t groups);  // groups = B * H
 
 }  // namespace kda

@@ -81,7 +81,7 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-template <int DK, int NW, bool STACK>
+template <int DK, int NW, bool STACK, bool EARLY>
 __global__ __launch_bounds__(64 * NW, 4) void verify_chunk_kernel(Args a) {
   constexpr int NT = 64 * NW, W = 16 * NW, NCB = DK / 16;
   constexpr int R = STACK ? 8 : 16;  // token rows of each half of the A operand
@@ -128,15 +128,24 @@ __global__ __launch_bounds__(64 * NW, 4) void verify_chunk_kernel(Args a) {
     const int t = idx / (W / 4), c = (idx % (W / 4)) * 4;
     *reinterpret_cast<float4 *>(L.v + t * Lds::VS + c) = unpack_bf16x4(vb);
   };
-  if (tid < nkq) put_kq(tid, kb0, qb0, al0);
-  if (tid < nv) put_v(tid, vb0);
-  if (tid < Tb) L.beta[tid] = bt0;
-  __builtin_amdgcn_sched_barrier(0);
+  // The state goes out after the first round of inputs has been written
+  // (the default; within one round of resident workgroups, a block's inputs
+  // otherwise queue in HBM behind every other block's state) or, with EARLY
+  // (grids of several rounds, where that overlap pays), right behind the
+  // input requests.
   const float *Scol = a.cache + (int64_t)slot * a.slot_stride + (int64_t)u.h * a.dv * DK +
                       (uint32_t)((16 * wave + j) * DK + 4 * g);
   float4 sreg[NCB];
+  auto load_state = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) sreg[cb] = ld4<kVerifyLoadStream>(Scol + 16 * cb);
+    for (int cb = 0; cb < NCB; ++cb) sreg[cb] = ld4<kVerifyLoadStream>(Scol + 16 * cb);
+  };
+  if constexpr (EARLY) load_state();
+  if (tid < nkq) put_kq(tid, kb0, qb0, al0);
+  if (tid < nv) put_v(tid, vb0);
+  if (tid < Tb) L.beta[tid] = bt0;
+  if constexpr (!EARLY) load_state();
   for (int idx = tid + NT; idx < nkq; idx += NT) {
     const uint32_t off = kq_off(idx);
     put_kq(idx, *reinterpret_cast<const uint2 *>(kbase + off), *reinterpret_cast<const uint2 *>(qbase + off),
@@ -368,8 +377,12 @@ __global__ __launch_bounds__(64 * NW, 4) void verify_chunk_kernel(Args a) {
 }
 
 template <int DK, int NW>
-const void *pick(bool stack) {
-  return stack ? (const void *)verify_chunk_kernel<DK, NW, true> : (const void *)verify_chunk_kernel<DK, NW, false>;
+const void *pick(bool stack, bool early) {
+  if (early)
+    return stack ? (const void *)verify_chunk_kernel<DK, NW, true, true>
+                 : (const void *)verify_chunk_kernel<DK, NW, false, true>;
+  return stack ? (const void *)verify_chunk_kernel<DK, NW, true, false>
+               : (const void *)verify_chunk_kernel<DK, NW, false, false>;
 }
 
 }  // namespace
@@ -381,10 +394,14 @@ size_t chunk_verify_lds_bytes(int dk, int dv, int T_max) {
   return floats * sizeof(float);
 }
 
-const void *verify_chunk_kernel_for(int dk, int dv, int T_max) {
+const void *verify_chunk_kernel_for(int dk, int dv, int T_max, int64_t groups) {
   const bool stack = T_max <= 8;
-  if (dk == 64) return dv == 64 ? pick<64, 4>(stack) : dv == 128 ? pick<64, 8>(stack) : nullptr;
-  if (dk == 128) return dv == 64 ? pick<128, 4>(stack) : dv == 128 ? pick<128, 8>(stack) : nullptr;
+  // more than one round of resident workgroups: 16 waves per CU at these
+  // kernels' ~100-120 VGPRs, i.e. 4096 / NW workgroups on MI355X's 256 CUs
+  const int nw = dv / 16;
+  const bool early = groups > 4096 / nw;
+  if (dk == 64) return dv == 64 ? pick<64, 4>(stack, early) : dv == 128 ? pick<64, 8>(stack, early) : nullptr;
+  if (dk == 128) return dv == 64 ? pick<128, 4>(stack, early) : dv == 128 ? pick<128, 8>(stack, early) : nullptr;
   return nullptr;
 }
 

@@ -371,3 +371,41 @@ def test_chunked_form_rejected_where_it_does_not_apply():
         with pytest.raises(K.KdaError) as e:
             _verify(w, cache_d, mode, form=K.KDA_VERIFY_CHUNKED, **kw)
         assert e.value.status == K.KDA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64)])
+@pytest.mark.parametrize("tmax", [8, 16])
+def test_chunked_form_state_load_orders_agree(dk, dv, tmax):
+    """The chunk form issues the state behind the inputs' first writes within one round of
+    resident workgroups and right behind the input requests for larger grids; both orders give
+    the same bits. 16 live rows of 32 heads (512 groups: one round) against the same rows
+    followed by 32 padding rows (1536 groups)."""
+    rng = np.random.default_rng(61 + tmax)
+    seqlens = list(rng.integers(1, tmax + 1, 16)) + [1] * 32
+    seqlens[0] = tmax
+    w = synth.make(48, 32, dk, dv, seqlens=seqlens, num_slots=64, state_std=0.05, seed=62)
+    slots = w.slot_ids.copy()
+    slots[16:] = -1
+    x = step_inputs(w, 0)
+    n16 = int(w.cu_seqlens[16])
+    res = []
+    for B in (16, 48):
+        n_tok = n16 if B == 16 else w.n_tok
+        out = sentinel((n_tok, w.H, dv))
+        rb = replay_buffers(B, w.T_max, w.H, dk, dv)
+        cache_d = f32(w.cache)
+        log(f"chunk form, state load order: B={B} dk={dk} dv={dv} T_max={w.T_max}")
+        K.kda_verify_chunk(cache_d, i32(slots[:B]), i32(w.cu_seqlens[:B + 1]), w.T_max,
+                           *(x[n][:n_tok].contiguous() for n in ("q", "k", "v", "alpha", "beta")), out,
+                           mode=K.KDA_REPLAY, replay=rb, verify_form=K.KDA_VERIFY_CHUNKED)
+        torch.cuda.synchronize()
+        res.append((bits(out), {k: bits(v)[:16] for k, v in rb.items()}))
+        if B == 48:
+            assert np.all(res[-1][0][n16:] == SENTINEL_BITS)
+            assert np.array_equal(bits(cache_d), w.cache.view(np.uint32))
+    assert np.array_equal(res[0][0], res[1][0][:n16])
+    for k in res[0][1]:
+        assert np.array_equal(res[0][1][k], res[1][1][k]), k
+    ref_out, _, _, rc = _oracle_verify(w, K.KDA_REPLAY, slots=slots)
+    assert rc == 0
+    assert rel_l2(res[0][0].view(np.float32), ref_out[:n16]) <= OUT_TOL
