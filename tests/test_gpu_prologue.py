@@ -249,3 +249,30 @@ def test_bf16_output_is_rounded_fp32_output(raw):
     assert rc == 0
     got = synth.bf16_bits_to_f32(bits(outs[1]))
     assert rel_l2(got, ref) <= 2.0 ** -8
+
+
+def test_raw_replay_commit_both_staging_orders():
+    """Raw-input replay commit in both staging orders (the state tile first at 2048 workgroups,
+    the inputs first at 8192: 16 rows x 32 heads at 32 and 8 columns per workgroup): the same
+    bits, and the oracle's raw-input commit within the state tolerance."""
+    w = synth.make(16, 32, 128, 128, seqlens=[8] * 16, num_slots=20, state_std=0.02, seed=36)
+    x = raw_step_inputs(w, 0)
+    cu, acc = w.cu_seqlens, w.accepted
+    cache_v = f32(w.cache)
+    rb = replay_buffers(w.B, 8, w.H, w.dk, w.dv)
+    out = sentinel((w.n_tok, w.H, w.dv))
+    log("raw verify (replay mode) for the commit orders")
+    K.kda_verify_chunk(cache_v, i32(w.slot_ids), i32(cu), 8, x["q"], x["k"], x["v"], x["alpha"], x["beta"], out,
+                       mode=K.KDA_REPLAY, replay=rb, raw_inputs=True)
+    got = []
+    for tw in (32, 8):
+        cache_c = f32(w.cache)
+        log(f"raw replay commit, tile_w={tw}")
+        K.kda_replay_commit(cache_c, i32(w.slot_ids), i32(cu), i32(acc), 8, w.n_tok, mode=K.KDA_REPLAY, replay=rb,
+                            raw_inputs=True, tile_w=tw)
+        torch.cuda.synchronize()
+        got.append(bits(cache_c))
+    assert np.array_equal(got[0], got[1])
+    ref = w.cache.copy()
+    assert oracle.commit(ref, w.slot_ids, cu, acc, 8, w.k_raw[0], w.v[0], w.a_raw[0], w.b_raw[0], prologue=True) == 0
+    assert rel_l2(got[0].view(np.float32)[w.slot_ids], ref[w.slot_ids]) <= STATE_TOL
