@@ -128,11 +128,12 @@ __global__ __launch_bounds__(64 * NW, 4) void verify_chunk_kernel(Args a) {
     const int t = idx / (W / 4), c = (idx % (W / 4)) * 4;
     *reinterpret_cast<float4 *>(L.v + t * Lds::VS + c) = unpack_bf16x4(vb);
   };
-  // The state goes out after the first round of inputs has been written
-  // (the default; within one round of resident workgroups, a block's inputs
-  // otherwise queue in HBM behind every other block's state) or, with EARLY
-  // (grids of several rounds, where that overlap pays), right behind the
-  // input requests.
+  // With EARLY (grids of several rounds of resident workgroups), the state
+  // goes out right behind the input requests and is in flight over the decay,
+  // coupling and solve passes. Otherwise it is requested only before the state
+  // products: its registers are then not live over the passes (61 VGPRs
+  // against ~100, so twice the workgroups fit on a CU), and within one round a
+  // block's inputs do not queue in HBM behind every other block's state.
   const float *Scol = a.cache + (int64_t)slot * a.slot_stride + (int64_t)u.h * a.dv * DK +
                       (uint32_t)((16 * wave + j) * DK + 4 * g);
   float4 sreg[NCB];
@@ -145,7 +146,6 @@ __global__ __launch_bounds__(64 * NW, 4) void verify_chunk_kernel(Args a) {
   if (tid < nkq) put_kq(tid, kb0, qb0, al0);
   if (tid < nv) put_v(tid, vb0);
   if (tid < Tb) L.beta[tid] = bt0;
-  if constexpr (!EARLY) load_state();
   for (int idx = tid + NT; idx < nkq; idx += NT) {
     const uint32_t off = kq_off(idx);
     put_kq(idx, *reinterpret_cast<const uint2 *>(kbase + off), *reinterpret_cast<const uint2 *>(qbase + off),
@@ -314,6 +314,8 @@ __global__ __launch_bounds__(64 * NW, 4) void verify_chunk_kernel(Args a) {
   float vv[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) vv[r] = L.v[min(4 * g + r, last) * Lds::VS + col];
+
+  if constexpr (!EARLY) load_state();
 
   // U0 and O0 for the wave's 16 columns
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f}, accO = {0.0f, 0.0f, 0.0f, 0.0f};
