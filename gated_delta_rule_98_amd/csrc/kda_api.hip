@@ -385,13 +385,14 @@ int kda_verify_chunk(float *cache, int64_t num_slots, int64_t slot_stride, const
   const bool chunk_fits = mode == KDA_REPLAY && !t1_inplace && epi == nullptr && !a.raw && !a.out_bf16;
   if (form == KDA_VERIFY_CHUNKED && (!chunk_fits || (opts && opts->tile_w != 0))) return KDA_ERR_UNSUPPORTED;
   // Automatic choice, from graph-timed runs on MI355X at H = 32, d = 128 with every row
-  // holding T tokens: the chunk form is faster from 8 tokens once there are at least 512
-  // (row, head) groups (B = 16, T = 8: 12.0 against 15.1 us; B = 64, T = 8: 42.7 against
-  // 59.4 us); with fewer tokens or groups its longer per-group latency loses (B = 4,
-  // T = 8: 7.7 against 7.0 us; B = 64, T = 4: 40.3 against 37.9 us).
+  // holding T tokens: the chunk form is faster from 8 tokens once there are at least 256
+  // (row, head) groups (B = 8, T = 8: 7.9 against 9.3 us; B = 16, T = 8: 11.4 against
+  // 15.6 us; B = 16, T = 16: 17.6 against 26.3 us); with fewer tokens or groups its longer
+  // per-group latency loses (B = 4, T = 8: 7.4 against 6.7 us; B = 32, T = 4: 20.8 against
+  // 17.3 us).
   const bool chunked = form == KDA_VERIFY_CHUNKED ||
                        (form == KDA_VERIFY_AUTO && chunk_fits && (!opts || opts->tile_w == 0) && T_max >= 8 &&
-                        (int64_t)B * H >= 512);
+                        (int64_t)B * H >= 256);
   Launch l;
   if (chunked) {
     l = {dv, dv / 16, 0};
