@@ -39,7 +39,7 @@ FLAGS = [
 
 def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
     """Compile the library (always recompiles); return its path."""
-    tmp = out + ".tmp"
+    tmp = f"{out}.tmp{os.getpid()}"  # per process: concurrent builds never share a file
     cmd = [HIPCC, *FLAGS, *extra, f"-I{INCLUDE}", *SOURCES, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

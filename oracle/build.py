@@ -20,7 +20,7 @@ CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast
 
 def build(out: str = LIB, src: str = SRC, extra=()) -> str:
     """Build the oracle library; return its path. Always recompiles."""
-    tmp = out + ".tmp"
+    tmp = f"{out}.tmp{os.getpid()}"  # per process: concurrent builds never share a file
     cmd = ["gcc", *CFLAGS, *extra, src, "-o", tmp, "-lm", "-lpthread"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
