@@ -51,13 +51,20 @@ def _oracle_verify(w, mode, **kw):
                          w.q[0], w.k[0], w.v[0], w.alpha[0], w.beta[0], mode=mode, **kw)
 
 
-def test_spec_verify_both_modes_and_commit():
-    w = synth.make_workload("spec_verify")
+@pytest.mark.parametrize("B", [16, 64], ids=["b16", "b64"])
+def test_spec_verify_both_modes_and_commit(B):
+    """The speculative-verify workload (B=16) and the same at B=64, where the chunk form issues
+    its state with its inputs and the replay commit its inputs before the state."""
+    if B == 16:
+        w = synth.make_workload("spec_verify")
+    else:
+        w = synth.make(B, 32, 128, 128, seqlens=[8] * B, num_slots=256, state_std=0.02, seed=64,
+                       name="spec_verify_b64")
     acc = w.accepted
     results = {}
     for mode in (K.KDA_REPLAY, K.KDA_PER_POSITION):
         cache_d = f32(w.cache)
-        log(f"spec_verify: verify mode {mode}")
+        log(f"spec_verify B={w.B}: verify mode {mode}")
         out, rb, draft = _verify(w, cache_d, mode)
         torch.cuda.synchronize()
         assert np.array_equal(bits(cache_d), w.cache.view(np.uint32))   # verify wrote no slot
@@ -76,7 +83,7 @@ def test_spec_verify_both_modes_and_commit():
             derr = rel_l2(d, ref_draft)
             log(f"  per-position states rel-Frobenius {derr:.3e}")
             assert derr <= STATE_TOL
-        log(f"spec_verify: commit mode {mode}")
+        log(f"spec_verify B={w.B}: commit mode {mode}")
         _commit(w, cache_d, mode, acc, rb, draft)
         torch.cuda.synchronize()
         results[mode] = (bits(out), bits(cache_d))
