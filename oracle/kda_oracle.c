@@ -255,8 +255,9 @@ static int run_item(const call_t *c, int b, int h)
     double *v = (double *)malloc(sizeof(double) * (size_t)n * dv);
     double *be = (double *)malloc(sizeof(double) * (size_t)n);
     double *o = (double *)malloc(sizeof(double) * (size_t)n * dv);
-    const int per_position = c->kind == KIND_VERIFY && c->mode == ORACLE_PER_POSITION &&
-                             !(Tb == 1 && c->t1_inplace);
+    /* a single-token row of a mixed batch, updated in place (t1_inplace) */
+    const int inplace_row = c->kind == KIND_VERIFY && Tb == 1 && c->t1_inplace;
+    const int per_position = c->kind == KIND_VERIFY && c->mode == ORACLE_PER_POSITION && !inplace_row;
     double *S_tok = per_position ? (double *)malloc(sizeof(double) * (size_t)n * dk * dv) : NULL;
 
     for (int i = 0; i < dk; ++i)
@@ -315,19 +316,23 @@ static int run_item(const call_t *c, int b, int h)
         free(w);
     }
 
+    /* Where the row's state goes: a speculative row in per-position mode writes
+     * every draft position; the single-token steps (decode, in-place rows), the
+     * commit and the prefill write the slot; a speculative row in replay mode
+     * buffers its inputs and leaves the slot alone. */
     const int write_slot = c->kind == KIND_DECODE || c->kind == KIND_COMMIT || c->kind == KIND_PREFILL ||
-                           (c->kind == KIND_VERIFY && Tb == 1 && c->t1_inplace);
-    if (write_slot) {
-        for (int i = 0; i < dk; ++i)
-            for (int j = 0; j < dv; ++j)
-                c->cache[cache_index(c, slot, h, j, i)] = (float)S[i * dv + j];
-    } else if (per_position) {
+                           inplace_row;
+    if (per_position) {
         for (int64_t t = 0; t < n; ++t) {
             float *dst = c->draft + (((int64_t)b * c->T_max + t) * H + h) * (int64_t)dv * dk;
             for (int i = 0; i < dk; ++i)
                 for (int j = 0; j < dv; ++j)
                     dst[(int64_t)j * dk + i] = (float)S_tok[t * dk * dv + i * dv + j];
         }
+    } else if (write_slot) {
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j)
+                c->cache[cache_index(c, slot, h, j, i)] = (float)S[i * dv + j];
     } else if (c->kind == KIND_VERIFY) {
         /* replay buffer: exact copies of this row's per-token inputs */
         for (int64_t t = 0; t < n; ++t) {

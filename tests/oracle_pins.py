@@ -213,6 +213,27 @@ def check_prefill_brute(lib):
     assert np.array_equal(cache[w.slot_ids[0]], w.cache[w.slot_ids[0]])
     assert not np.array_equal(cache[w.slot_ids[2]], w.cache[w.slot_ids[2]])
 
+    # ckpt_pos < 0 asks for no export: that row's checkpoint keeps its contents,
+    # and its outputs and final state are those of the plain run
+    pos = np.array([-1, -1, 1, -5], np.int32)
+    cache = w.cache.copy()
+    out2, ckpt2, rc = oracle.prefill(cache, w.slot_ids, w.cu_seqlens, w.q[0], w.k[0], w.v[0], w.alpha[0],
+                                     w.beta[0], ckpt_pos=pos, lib=lib)
+    assert rc == 0
+    for b in range(w.B):
+        s = w.slot_ids[b]
+        for h in range(w.H):
+            S0 = w.cache[s, h].T.astype(np.float64)
+            states, outs = brute_run(S0, _unit_tokens(w, range(cu[b], cu[b + 1]), h))
+            for t in range(cu[b + 1] - cu[b]):
+                assert _rel(out2[cu[b] + t, h], to_float(outs[t])) <= 1e-6, (b, h, t)
+            final = to_float(states[-1]) if states else S0
+            assert _rel(cache[s, h].T, final) <= 1e-6, (b, h)
+            if pos[b] < 0:
+                assert np.all(np.isnan(ckpt2[b, h])), (b, h)
+            else:
+                assert _rel(ckpt2[b, h].T, to_float(states[pos[b] - 1])) <= 1e-6, (b, h)
+
 
 # ---------------------------------------------------------------- closed forms
 
@@ -444,6 +465,120 @@ def check_prologue_prepared_equivalence(lib):
         assert _rel(o1, o2) <= 1e-6, t
 
 
+def check_inplace_rows(lib):
+    """The single-token rows of a mixed batch ("Kimi K3 performance optimization in
+    vLLM", section "Zero-copy mixed KDA batching"): with t1_inplace, a row of one
+    token takes its step on the slot itself (exact brute force of the matrix form)
+    and leaves no replay or draft entry, while the multi-token rows keep their slots
+    and fill their buffers, in both modes. Without the flag every row is speculative."""
+    w = synth.make(5, 2, 3, 4, seqlens=[1, 3, 1, 2, 1], num_slots=7, state_std=0.5, seed=31)
+    cu, T_max, H = w.cu_seqlens, w.T_max, w.H
+    nan = np.array([0x7FC0DEAD], np.uint32).view(np.float32)[0]
+    ref = {}
+    for b in range(w.B):
+        for h in range(H):
+            S0 = w.cache[w.slot_ids[b], h].T.astype(np.float64)
+            ref[b, h] = brute_run(S0, _unit_tokens(w, range(cu[b], cu[b + 1]), h))
+    for inplace in (True, False):
+        for mode in (oracle.REPLAY, oracle.PER_POSITION):
+            cache = w.cache.copy()
+            rb = dict(rk=np.full((w.B, T_max, H, w.dk), 0xDEAD, np.uint16),
+                      rv=np.full((w.B, T_max, H, w.dv), 0xDEAD, np.uint16),
+                      ralpha=np.full((w.B, T_max, H, w.dk), nan, np.float32),
+                      rbeta=np.full((w.B, T_max, H), nan, np.float32))
+            draft = np.full((w.B, T_max, H, w.dv, w.dk), nan, np.float32)
+            out, rb, draft, rc = oracle.verify(cache, w.slot_ids, cu, T_max, w.q[0], w.k[0], w.v[0],
+                                               w.alpha[0], w.beta[0], mode=mode, t1_inplace=inplace,
+                                               replay=rb if mode == oracle.REPLAY else None,
+                                               draft=draft if mode == oracle.PER_POSITION else None, lib=lib)
+            assert rc == 0
+            for b in range(w.B):
+                s, Tb = w.slot_ids[b], cu[b + 1] - cu[b]
+                in_place = inplace and Tb == 1
+                for h in range(H):
+                    states, outs = ref[b, h]
+                    for t in range(Tb):
+                        assert _rel(out[cu[b] + t, h], to_float(outs[t])) <= 1e-6, (b, h, t)
+                    if in_place:
+                        assert _rel(cache[s, h].T, to_float(states[0])) <= 1e-6, (b, h, mode)
+                    else:
+                        assert np.array_equal(cache[s, h], w.cache[s, h]), (b, h, mode)
+                    for t in range(T_max):
+                        written = not in_place and t < Tb
+                        if mode == oracle.PER_POSITION:
+                            d = draft[b, t, h]
+                            if written:
+                                assert _rel(d.T, to_float(states[t])) <= 1e-6, (b, t, h)
+                            else:
+                                assert np.all(d.view(np.uint32) == 0x7FC0DEAD), (b, t, h)
+                        else:
+                            if written:
+                                r = cu[b] + t
+                                assert np.array_equal(rb["rk"][b, t, h], w.k[0][r, h])
+                                assert np.array_equal(rb["rv"][b, t, h], w.v[0][r, h])
+                                assert np.array_equal(rb["ralpha"][b, t, h], w.alpha[0][r, h])
+                                assert rb["rbeta"][b, t, h] == w.beta[0][r, h]
+                            else:
+                                assert np.all(rb["rk"][b, t, h] == 0xDEAD), (b, t, h)
+                                assert np.all(rb["rv"][b, t, h] == 0xDEAD), (b, t, h)
+                                assert np.all(rb["ralpha"][b, t, h].view(np.uint32) == 0x7FC0DEAD)
+                                assert rb["rbeta"][b, t, h].view(np.uint32) == 0x7FC0DEAD
+            untouched = np.setdiff1d(np.arange(w.num_slots), w.slot_ids)
+            assert np.array_equal(cache[untouched], w.cache[untouched])
+
+
+def check_gate_every_token(lib):
+    """The output gate ("Hyper Optimizing Kimi K3 in vLLM", section "Finding time
+    between operators") applies to the read-out of every token of a multi-token row.
+    Closed form: with k = q = e_0, beta = 1 and alpha_0 = 0, the decay erases key row
+    0 before each write, so the write stores v_t there exactly and the read-out is
+    o_t = v_t. With v_t = c_t * 1 and gate 0 the gated output is
+    sign(c_t) / sqrt(1 + eps / c_t^2) * w / 2, for every token t."""
+    rng = np.random.Generator(np.random.PCG64(32))
+    dk, dv, H = 4, 8, 2
+    lens = [4, 1, 3]
+    B, n_tok = len(lens), sum(lens)
+    cu = np.zeros(B + 1, np.int32)
+    cu[1:] = np.cumsum(lens)
+    c = np.array([3.0, -0.5, 2.0, -1.25, 0.75, 1.5, -4.0, 0.25])[:n_tok]
+    e0 = np.zeros(dk, np.float32)
+    e0[0] = 1.0
+    q = np.tile(_bf(e0), (n_tok, H, 1))
+    v = _bf(np.broadcast_to(c[:, None, None], (n_tok, H, dv)))
+    alpha = rng.uniform(0.25, 1.0, (n_tok, H, dk)).astype(np.float32)
+    alpha[:, :, 0] = 0.0
+    beta = np.ones((n_tok, H), np.float32)
+    gate = np.zeros((n_tok, H, dv), np.uint16)            # bf16 +0
+    weight = rng.uniform(0.5, 2.0, dv).astype(np.float32)
+    eps = 1e-6
+    cache0 = (rng.standard_normal((4, H, dv, dk)) * 0.3).astype(np.float32)
+    slots = np.array([2, 0, 3], np.int32)
+    for mode in (oracle.REPLAY, oracle.PER_POSITION):
+        plain, _, _, rc = oracle.verify(cache0.copy(), slots, cu, max(lens), q, q, v, alpha, beta,
+                                        mode=mode, lib=lib)
+        assert rc == 0
+        assert np.array_equal(plain, np.broadcast_to(c[:, None, None], plain.shape).astype(np.float32))
+        gated, _, _, rc = oracle.verify(cache0.copy(), slots, cu, max(lens), q, q, v, alpha, beta,
+                                        mode=mode, gate=gate, weight=weight, eps=eps, lib=lib)
+        assert rc == 0
+        for t in range(n_tok):
+            expect = math.copysign(1.0, c[t]) / math.sqrt(1.0 + eps / (c[t] * c[t])) * weight * 0.5
+            for h in range(H):
+                assert _rel(gated[t, h], expect) <= 1e-7, (t, h)
+    # random inputs: every token's gated output is the gate applied to its own read-out
+    w = synth.make(3, 2, 8, 16, seqlens=[3, 1, 4], num_slots=4, state_std=0.3, gate=True, seed=33)
+    plain, _, _, _ = oracle.verify(w.cache.copy(), w.slot_ids, w.cu_seqlens, w.T_max, w.q[0], w.k[0],
+                                   w.v[0], w.alpha[0], w.beta[0], lib=lib)
+    gated, _, _, _ = oracle.verify(w.cache.copy(), w.slot_ids, w.cu_seqlens, w.T_max, w.q[0], w.k[0],
+                                   w.v[0], w.alpha[0], w.beta[0], gate=w.gate[0], eps=1e-6, lib=lib)
+    gf = synth.bf16_bits_to_f32(w.gate[0]).astype(np.float64)
+    for r in range(w.n_tok):
+        for h in range(w.H):
+            o = plain[r, h].astype(np.float64)
+            rms = math.sqrt(float(np.mean(o * o)) + 1e-6)
+            assert _rel(gated[r, h], o / rms / (1.0 + np.exp(-gf[r, h]))) <= 1e-6, (r, h)
+
+
 # ---------------------------------------------------------------- structure
 
 def check_commit_equals_steps(lib):
@@ -584,4 +719,5 @@ CHECKS = [
     check_linearity, check_gate_closed_form, check_commit_equals_steps,
     check_column_permutation, check_slot_handling, check_fp32_state_storage, check_bounded_state,
     check_prologue_closed_form, check_prologue_prepared_equivalence,
+    check_inplace_rows, check_gate_every_token,
 ]

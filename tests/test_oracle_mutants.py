@@ -57,6 +57,19 @@ MUTANTS = [
     ("prologue_alpha_as_sigmoid", "exp(-log1p(exp(alpha[i])))", "1.0 / (1.0 + exp(-alpha[i]))", 1),
     ("prologue_beta_sign", "1.0 / (1.0 + exp(-*beta))", "1.0 / (1.0 + exp(*beta))", 1),
     ("prologue_ignored", "if (c->prologue)", "if (0)", 1),
+    ("inplace_rows_not_written", "const int inplace_row = c->kind == KIND_VERIFY && Tb == 1 && c->t1_inplace;",
+     "const int inplace_row = 0;", 1),
+    ("inplace_flag_ignored_for_perpos", "c->mode == ORACLE_PER_POSITION && !inplace_row;",
+     "c->mode == ORACLE_PER_POSITION;", 1),
+    ("inplace_slot_not_written", "c->kind == KIND_PREFILL ||\n                           inplace_row;",
+     "c->kind == KIND_PREFILL;", 1),
+    ("inplace_ignores_token_count", "c->kind == KIND_VERIFY && Tb == 1 && c->t1_inplace;",
+     "c->kind == KIND_VERIFY && Tb >= 1 && c->t1_inplace;", 1),
+    ("gate_only_first_token", "if (c->gate) {", "if (c->gate && t == 0) {", 1),
+    ("gate_only_single_token_rows", "if (c->gate) {", "if (c->gate && n == 1) {", 1),
+    ("ckpt_negative_exports_start", "ckpt_at = c->ckpt_pos[b];",
+     "ckpt_at = c->ckpt_pos[b] < 0 ? 0 : c->ckpt_pos[b];", 1),
+    ("ckpt_negative_is_error", "if (ckpt_at > Tb)", "if (ckpt_at > Tb || ckpt_at < 0)", 1),
 ]
 
 RUNNER = r"""
