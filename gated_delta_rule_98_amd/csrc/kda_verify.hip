@@ -277,7 +277,9 @@ __device__ __forceinline__ int commit_row(const Args &a, const Unit &u, int32_t 
   }
   wait_uniform3(slot, n, c0);
   const bool bad_slot = slot >= a.num_slots;
-  const bool bad_range = c0 < 0 || c1 < c0 || c1 > a.n_tok || c1 - c0 > a.T_max;
+  // Without cu_seqlens every row's range is [0, T_max): it indexes no packed
+  // array (the commit reads only its buffers), so n_tok does not bound it.
+  const bool bad_range = a.cu && (c0 < 0 || c1 < c0 || c1 > a.n_tok || c1 - c0 > a.T_max);
   const bool bad_n = n < 0 || n > c1 - c0;
   if (slot < 0 || bad_slot || bad_range || bad_n) {
     if (slot >= 0) report(a.dev_err, u, bad_slot ? KDA_DEVERR_SLOT : bad_range ? KDA_DEVERR_SEQLEN : KDA_DEVERR_ACCEPTED);

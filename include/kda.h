@@ -211,8 +211,9 @@ int kda_verify_chunk(float *cache, int64_t num_slots, int64_t slot_stride,
  *   mode KDA_REPLAY:       reload the slot, replay the buffered inputs of rb, store once
  *   mode KDA_PER_POSITION: copy draft[b][accepted_len[b] - 1] into the slot
  * Both modes leave bit-identical slots, equal bit for bit to accepted_len[b]
- * successive kda_decode_step calls. cu_seqlens (may be NULL: then T_b = T_max)
- * bounds accepted_len.
+ * successive kda_decode_step calls. cu_seqlens bounds accepted_len by each
+ * row's token count T_b (a bad range sets KDA_DEVERR_SEQLEN, as in verify). It
+ * may be NULL: then T_b = T_max for every row and n_tok is not used.
  */
 int kda_replay_commit(float *cache, int64_t num_slots, int64_t slot_stride,
                       const int32_t *slot_ids, const int32_t *cu_seqlens,

@@ -56,6 +56,39 @@ def rel_l2(a, b) -> float:
     return float(np.linalg.norm(a - b) / nb)
 
 
+def _worst_group(a, b, group_axes: int) -> float:
+    """Largest relative L2 error over the sub-arrays formed by the last ``group_axes`` axes."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    if a.ndim <= group_axes or a.size == 0:
+        return rel_l2(a, b)
+    n = int(np.prod(a.shape[a.ndim - group_axes:]))
+    a = a.reshape(-1, n)
+    b = b.reshape(-1, n)
+    num = np.linalg.norm(a - b, axis=1)
+    den = np.linalg.norm(b, axis=1)
+    err = np.where(den < 1e-30, num, num / np.maximum(den, 1e-300))
+    return float(err.max())
+
+
+def out_rel(a, b, name: str = "") -> float:
+    """Error of outputs shaped [..., dv]: the larger of the whole-array relative L2 and the worst
+    single (token, head) vector's, so that one wrong head cannot hide in the norm of thousands."""
+    whole, worst = rel_l2(a, b), _worst_group(a, b, 1)
+    if name:
+        log(f"  {name}: rel-L2 {whole:.3e}, worst (token, head) {worst:.3e}")
+    return max(whole, worst)
+
+
+def state_rel(a, b, name: str = "") -> float:
+    """Error of states shaped [..., dv, dk]: the larger of the whole-array relative Frobenius
+    error and the worst single head's."""
+    whole, worst = rel_l2(a, b), _worst_group(a, b, 2)
+    if name:
+        log(f"  {name}: rel-Frobenius {whole:.3e}, worst head {worst:.3e}")
+    return max(whole, worst)
+
+
 def step_inputs(w, step: int):
     """Device tensors of one step's token arrays."""
     d = dict(q=bf16(w.q[step]), k=bf16(w.k[step]), v=bf16(w.v[step]),

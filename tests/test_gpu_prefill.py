@@ -12,7 +12,7 @@ import torch
 import gated_delta_rule_98_amd as K
 import oracle
 import synth
-from gpu_util import SENTINEL_BITS, bits, dev, f32, i32, log, rel_l2, sentinel, step_inputs
+from gpu_util import SENTINEL_BITS, bits, dev, f32, i32, log, out_rel, state_rel, sentinel, step_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -49,19 +49,19 @@ def test_prefill_matches_oracle(dk, dv):
     assert rc == 0
     live = np.concatenate([np.arange(w.cu_seqlens[b], w.cu_seqlens[b + 1]) for b in range(w.B) if b != 6])
     pad = np.arange(w.cu_seqlens[6], w.cu_seqlens[7])
-    err = rel_l2(out.cpu().numpy()[live], ref_out[live])
-    log(f"  outputs rel-L2 {err:.3e}")
+    err = out_rel(out.cpu().numpy()[live], ref_out[live])
+    log(f"  outputs rel-L2 (worst of whole, per head) {err:.3e}")
     assert err <= OUT_TOL
     assert np.all(bits(out)[pad] == SENTINEL_BITS)
     got = cache_d.cpu().numpy()
     live_slots = slots[slots >= 0]
-    assert rel_l2(got[live_slots], cache_h[live_slots]) <= STATE_TOL
+    assert state_rel(got[live_slots], cache_h[live_slots]) <= STATE_TOL
     others = np.setdiff1d(np.arange(w.num_slots), live_slots)
     assert np.array_equal(got[others].view(np.uint32), w.cache[others].view(np.uint32))
     ck = ckpt.cpu().numpy()
     for b in range(w.B):
         if slots[b] >= 0 and pos[b] >= 0:
-            assert rel_l2(ck[b], ref_ckpt[b]) <= STATE_TOL, b
+            assert state_rel(ck[b], ref_ckpt[b]) <= STATE_TOL, b
         else:
             assert np.all(bits(ckpt)[b] == SENTINEL_BITS), b     # no export: untouched
 
@@ -90,7 +90,7 @@ def test_prefill_states_equal_decode_steps_bitwise():
     ck = bits(ckpt)
     for b in range(w.B):
         assert np.array_equal(ck[b], snaps[int(pos[b])][w.slot_ids[b]]), b
-    assert rel_l2(out.cpu().numpy(), dec_out.cpu().numpy()) <= 1e-5
+    assert out_rel(out.cpu().numpy(), dec_out.cpu().numpy()) <= 1e-5
 
 
 def test_prefill_resume_from_checkpoint_is_bitwise_identical():
@@ -134,11 +134,11 @@ def test_prefill_8k_prompt_checkpoint_at_7680():
                                            w.alpha[0], w.beta[0], ckpt_pos=pos)
     assert rc == 0
     o = out.cpu().numpy()
-    err = rel_l2(o, ref_out)
-    worst = max(rel_l2(o[t], ref_out[t]) for t in range(0, w.n_tok, 97))
-    serr = rel_l2(cache_d.cpu().numpy(), cache_h)
-    cerr = rel_l2(ckpt.cpu().numpy(), ref_ckpt)
-    log(f"  outputs rel-L2 {err:.3e} (worst sampled token {worst:.3e}), final state {serr:.3e}, checkpoint {cerr:.3e}")
+    err = out_rel(o, ref_out)
+    worst = max(out_rel(o[t], ref_out[t]) for t in range(0, w.n_tok, 97))
+    serr = state_rel(cache_d.cpu().numpy(), cache_h)
+    cerr = state_rel(ckpt.cpu().numpy(), ref_ckpt)
+    log(f"  outputs rel-L2 (worst of whole, per head) {err:.3e} (worst sampled token {worst:.3e}), final state {serr:.3e}, checkpoint {cerr:.3e}")
     assert err <= OUT_TOL and worst <= OUT_TOL and serr <= STATE_TOL and cerr <= STATE_TOL
 
 

@@ -15,7 +15,7 @@ import torch
 import gated_delta_rule_98_amd as K
 import oracle
 import synth
-from gpu_util import (SENTINEL_BITS, bits, bf16, dev, f32, i32, log, raw_step_inputs, rel_l2, sentinel,
+from gpu_util import (SENTINEL_BITS, bits, bf16, dev, f32, i32, log, raw_step_inputs, out_rel, state_rel, sentinel,
                       step_inputs)
 
 pytestmark = pytest.mark.gpu
@@ -48,11 +48,11 @@ def _check(w, slots, pos, out, ckpt, cache_d, *, raw=False, alpha=None, tol_out=
     live_rows = [b for b in range(w.B) if slots[b] >= 0]
     live = np.concatenate([np.arange(w.cu_seqlens[b], w.cu_seqlens[b + 1]) for b in live_rows] + [np.zeros(0, int)])
     o = out.float().cpu().numpy()
-    err = rel_l2(o[live], ref_out[live]) if len(live) else 0.0
+    err = out_rel(o[live], ref_out[live]) if len(live) else 0.0
     got = cache_d.cpu().numpy()
     live_slots = slots[slots >= 0]
-    serr = rel_l2(got[live_slots], cache_h[live_slots])
-    log(f"  outputs rel-L2 {err:.3e}, states rel-Frobenius {serr:.3e}")
+    serr = state_rel(got[live_slots], cache_h[live_slots])
+    log(f"  outputs rel-L2 (worst of whole, per head) {err:.3e}, states rel-Frobenius (worst of whole, per head) {serr:.3e}")
     assert err <= tol_out and serr <= STATE_TOL
     others = np.setdiff1d(np.arange(w.num_slots), live_slots)
     assert np.array_equal(got[others].view(np.uint32), w.cache[others].view(np.uint32))
@@ -65,7 +65,7 @@ def _check(w, slots, pos, out, ckpt, cache_d, *, raw=False, alpha=None, tol_out=
         ck = ckpt.cpu().numpy()
         for b in range(w.B):
             if slots[b] >= 0 and pos[b] >= 0:
-                assert rel_l2(ck[b], ref_ckpt[b]) <= STATE_TOL, b
+                assert state_rel(ck[b], ref_ckpt[b]) <= STATE_TOL, b
             else:
                 assert np.all(bits(ckpt)[b] == SENTINEL_BITS), b
     return ref_out
@@ -93,8 +93,8 @@ def test_chunked_prefill_without_checkpoints_and_against_recurrent_form():
     out_c, _ = _run(w, cache_c)
     out_r, _ = _run(w, cache_r, chunked=False)
     torch.cuda.synchronize()
-    assert rel_l2(out_c.cpu().numpy(), out_r.cpu().numpy()) <= 1e-5
-    assert rel_l2(cache_c.cpu().numpy(), cache_r.cpu().numpy()) <= 1e-5
+    assert out_rel(out_c.cpu().numpy(), out_r.cpu().numpy()) <= 1e-5
+    assert state_rel(cache_c.cpu().numpy(), cache_r.cpu().numpy()) <= 1e-5
     _check(w, w.slot_ids, np.full(3, -1, np.int32), out_c, None, cache_c)
 
 
@@ -107,8 +107,8 @@ def test_chunked_prefill_8k_prompt_checkpoint_at_7680():
     torch.cuda.synchronize()
     ref_out = _check(w, w.slot_ids, pos, out, ckpt, cache_d)
     o = out.cpu().numpy()
-    worst = max(rel_l2(o[t], ref_out[t]) for t in range(0, w.n_tok, 97))
-    log(f"  worst sampled token rel-L2 {worst:.3e}")
+    worst = max(out_rel(o[t], ref_out[t]) for t in range(0, w.n_tok, 97))
+    log(f"  worst sampled token rel-L2 (worst of whole, per head) {worst:.3e}")
     assert worst <= OUT_TOL
 
 
@@ -170,8 +170,8 @@ def test_chunked_prefill_device_errors_and_empty_rows():
     okslots[1] = okslots[2] = -1
     ref_out, ref_ckpt, _ = oracle.prefill(cache_h, okslots, w.cu_seqlens, w.q[0], w.k[0], w.v[0], w.alpha[0],
                                           w.beta[0], ckpt_pos=pos)
-    assert rel_l2(got[w.slot_ids[0]], cache_h[w.slot_ids[0]]) <= STATE_TOL
-    assert rel_l2(ckpt.cpu().numpy()[0], ref_ckpt[0]) <= STATE_TOL
+    assert state_rel(got[w.slot_ids[0]], cache_h[w.slot_ids[0]]) <= STATE_TOL
+    assert state_rel(ckpt.cpu().numpy()[0], ref_ckpt[0]) <= STATE_TOL
     # an empty call and a call with only a checkpoint before an empty prompt
     e = synth.make(1, 4, 128, 128, seqlens=[0], num_slots=1, state_std=0.05, seed=76)
     cache_e = f32(e.cache)

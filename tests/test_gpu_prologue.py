@@ -20,7 +20,7 @@ import torch
 import gated_delta_rule_98_amd as K
 import oracle
 import synth
-from gpu_util import (bits, dev, f32, i32, log, raw_step_inputs, rel_l2, replay_buffers, sentinel,
+from gpu_util import (bits, dev, f32, i32, log, raw_step_inputs, out_rel, state_rel, replay_buffers, sentinel,
                       step_inputs)
 
 pytestmark = pytest.mark.gpu
@@ -65,9 +65,9 @@ def test_decode_raw_inputs_match_oracle_and_widths_agree(dk, dv):
         log(f"raw decode dk={dk} dv={dv} tile_w={tile_w}: {w.steps} steps")
         cache_d, outs = _decode_run(w, tile_w)
         got = cache_d.cpu().numpy()
-        worst = max(rel_l2(outs[s].cpu().numpy(), ref_outs[s]) for s in range(w.steps))
-        serr = rel_l2(got[w.slot_ids], ref_cache[w.slot_ids])
-        log(f"  worst step rel-L2 {worst:.3e}, state rel-Frobenius {serr:.3e}")
+        worst = max(out_rel(outs[s].cpu().numpy(), ref_outs[s]) for s in range(w.steps))
+        serr = state_rel(got[w.slot_ids], ref_cache[w.slot_ids])
+        log(f"  worst step rel-L2 (worst of whole, per head) {worst:.3e}, state rel-Frobenius (worst of whole, per head) {serr:.3e}")
         assert worst <= OUT_TOL and serr <= STATE_TOL
         untouched = np.setdiff1d(np.arange(w.num_slots), w.slot_ids)
         assert np.array_equal(got[untouched].view(np.uint32), w.cache[untouched].view(np.uint32))
@@ -83,9 +83,9 @@ def test_b1_latency_raw_inputs_1024_steps():
     cache_d, outs = _decode_run(w)
     ref_cache, ref_outs = _oracle_decode_run(w)
     outs_h = outs.cpu().numpy()
-    worst = max(rel_l2(outs_h[s], ref_outs[s]) for s in range(w.steps))
-    serr = rel_l2(cache_d.cpu().numpy(), ref_cache)
-    log(f"  worst step rel-L2 {worst:.3e}, state rel-Frobenius after 1024 steps {serr:.3e}")
+    worst = max(out_rel(outs_h[s], ref_outs[s]) for s in range(w.steps))
+    serr = state_rel(cache_d.cpu().numpy(), ref_cache)
+    log(f"  worst step rel-L2 (worst of whole, per head) {worst:.3e}, state rel-Frobenius (worst of whole, per head) after 1024 steps {serr:.3e}")
     assert worst <= OUT_TOL and serr <= STATE_TOL
 
 
@@ -149,13 +149,13 @@ def test_raw_inputs_states_bit_identical_across_ops():
     c = bits(ckpt)
     for b in range(w.B):
         assert np.array_equal(c[b], per_pos[acc[b] - 1][b]), b
-    assert rel_l2(out_f.cpu().numpy(), dec_out.cpu().numpy()) <= 1e-5
+    assert out_rel(out_f.cpu().numpy(), dec_out.cpu().numpy()) <= 1e-5
     # and all of it against the oracle's raw-input mode
     ref_out, ref_ckpt, rc = oracle.prefill(w.cache.copy(), w.slot_ids, cu, w.q_raw[0], w.k_raw[0], w.v[0],
                                            w.a_raw[0], w.b_raw[0], ckpt_pos=acc, prologue=True)
     assert rc == 0
-    assert rel_l2(out_f.cpu().numpy(), ref_out) <= OUT_TOL
-    assert rel_l2(ckpt.cpu().numpy(), ref_ckpt) <= STATE_TOL
+    assert out_rel(out_f.cpu().numpy(), ref_out) <= OUT_TOL
+    assert state_rel(ckpt.cpu().numpy(), ref_ckpt) <= STATE_TOL
 
 
 def test_raw_inputs_with_output_gate():
@@ -175,9 +175,9 @@ def test_raw_inputs_with_output_gate():
                                   w.a_raw[0], w.b_raw[0], mode=oracle.REPLAY, t1_inplace=True, gate=w.gate[0],
                                   weight=weight, eps=1e-6, prologue=True)
     assert rc == 0
-    err = rel_l2(out.cpu().numpy(), ref)
-    serr = rel_l2(cache_d.cpu().numpy(), cache_h)
-    log(f"  outputs rel-L2 {err:.3e}, in-place states rel-Frobenius {serr:.3e}")
+    err = out_rel(out.cpu().numpy(), ref)
+    serr = state_rel(cache_d.cpu().numpy(), cache_h)
+    log(f"  outputs rel-L2 (worst of whole, per head) {err:.3e}, in-place states rel-Frobenius (worst of whole, per head) {serr:.3e}")
     assert err <= OUT_TOL and serr <= STATE_TOL
     # gated single-token step
     w1 = synth.make(6, 4, 128, 128, num_slots=6, state_std=0.02, gate=True, seed=34)
@@ -192,8 +192,8 @@ def test_raw_inputs_with_output_gate():
     ref, rc = oracle.decode(cache_h, w1.slot_ids, w1.q_raw[0], w1.k_raw[0], w1.v[0], w1.a_raw[0], w1.b_raw[0],
                             gate=w1.gate[0], weight=weight, eps=1e-6, prologue=True)
     assert rc == 0
-    assert rel_l2(out.cpu().numpy(), ref) <= OUT_TOL
-    assert rel_l2(cache_d.cpu().numpy(), cache_h) <= STATE_TOL
+    assert out_rel(out.cpu().numpy(), ref) <= OUT_TOL
+    assert state_rel(cache_d.cpu().numpy(), cache_h) <= STATE_TOL
 
 
 def _bf16_of(t: torch.Tensor) -> np.ndarray:
@@ -248,7 +248,7 @@ def test_bf16_output_is_rounded_fp32_output(raw):
                                 prologue=raw)
     assert rc == 0
     got = synth.bf16_bits_to_f32(bits(outs[1]))
-    assert rel_l2(got, ref) <= 2.0 ** -8
+    assert out_rel(got, ref) <= 2.0 ** -8
 
 
 def test_raw_replay_commit_both_staging_orders():
@@ -275,4 +275,4 @@ def test_raw_replay_commit_both_staging_orders():
     assert np.array_equal(got[0], got[1])
     ref = w.cache.copy()
     assert oracle.commit(ref, w.slot_ids, cu, acc, 8, w.k_raw[0], w.v[0], w.a_raw[0], w.b_raw[0], prologue=True) == 0
-    assert rel_l2(got[0].view(np.float32)[w.slot_ids], ref[w.slot_ids]) <= STATE_TOL
+    assert state_rel(got[0].view(np.float32)[w.slot_ids], ref[w.slot_ids]) <= STATE_TOL

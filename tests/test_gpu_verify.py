@@ -15,7 +15,7 @@ import torch
 import gated_delta_rule_98_amd as K
 import oracle
 import synth
-from gpu_util import (SENTINEL_BITS, bits, dev, f32, i32, log, rel_l2, replay_buffers, sentinel,
+from gpu_util import (SENTINEL_BITS, bits, dev, f32, i32, log, out_rel, state_rel, replay_buffers, sentinel,
                       step_inputs)
 
 pytestmark = pytest.mark.gpu
@@ -70,8 +70,8 @@ def test_spec_verify_both_modes_and_commit(B):
         assert np.array_equal(bits(cache_d), w.cache.view(np.uint32))   # verify wrote no slot
         ref_out, ref_rb, ref_draft, rc = _oracle_verify(w, mode)
         assert rc == 0
-        err = rel_l2(out.cpu().numpy(), ref_out)
-        log(f"  outputs rel-L2 {err:.3e}")
+        err = out_rel(out.cpu().numpy(), ref_out)
+        log(f"  outputs rel-L2 (worst of whole, per head) {err:.3e}")
         assert err <= OUT_TOL
         if mode == K.KDA_REPLAY:
             assert np.array_equal(bits(rb["k"]), ref_rb["rk"])
@@ -80,8 +80,8 @@ def test_spec_verify_both_modes_and_commit(B):
             assert np.array_equal(bits(rb["beta"]), ref_rb["rbeta"].view(np.uint32))
         else:
             d = draft.cpu().numpy()
-            derr = rel_l2(d, ref_draft)
-            log(f"  per-position states rel-Frobenius {derr:.3e}")
+            derr = state_rel(d, ref_draft)
+            log(f"  per-position states rel-Frobenius (worst of whole, per head) {derr:.3e}")
             assert derr <= STATE_TOL
         log(f"spec_verify B={w.B}: commit mode {mode}")
         _commit(w, cache_d, mode, acc, rb, draft)
@@ -89,14 +89,14 @@ def test_spec_verify_both_modes_and_commit(B):
         results[mode] = (bits(out), bits(cache_d))
     # both modes: the same committed slot bits; outputs agree to rounding (replay mode
     # computes them in chunk form, per-position mode token by token)
-    assert rel_l2(results[0][0].view(np.float32), results[1][0].view(np.float32)) <= 1e-5
+    assert out_rel(results[0][0].view(np.float32), results[1][0].view(np.float32)) <= 1e-5
     assert np.array_equal(results[0][1], results[1][1])
     cache_h = w.cache.copy()
     assert oracle.commit(cache_h, w.slot_ids, w.cu_seqlens, acc, w.T_max, w.k[0], w.v[0], w.alpha[0],
                          w.beta[0]) == 0
     got = results[0][1].view(np.float32)
-    serr = rel_l2(got[w.slot_ids], cache_h[w.slot_ids])
-    log(f"  committed states rel-Frobenius {serr:.3e}")
+    serr = state_rel(got[w.slot_ids], cache_h[w.slot_ids])
+    log(f"  committed states rel-Frobenius (worst of whole, per head) {serr:.3e}")
     assert serr <= STATE_TOL
     untouched = np.setdiff1d(np.arange(w.num_slots), w.slot_ids)
     assert np.array_equal(results[0][1][untouched], w.cache[untouched].view(np.uint32))
@@ -129,7 +129,7 @@ def test_commit_equals_single_token_steps_bitwise():
         if form == K.KDA_VERIFY_RECURRENT:
             assert np.array_equal(bits(out), bits(dec_out))
         else:
-            assert rel_l2(out.cpu().numpy(), dec_out.cpu().numpy()) <= 1e-5
+            assert out_rel(out.cpu().numpy(), dec_out.cpu().numpy()) <= 1e-5
     # both staging orders of the replay commit: at this shape (16 rows x 32 heads) 32-column
     # tiles give 2048 workgroups (state tile first), 16 and 8 columns 4096 and 8192 (inputs first)
     cache_v = f32(w.cache)
@@ -156,13 +156,13 @@ def test_mixed_batch_inplace_gate_and_commit():
                                            w.alpha[0], w.beta[0], mode=oracle.REPLAY, t1_inplace=True,
                                            gate=w.gate[0], weight=weight, eps=1e-6)
     assert rc == 0
-    err = rel_l2(out.cpu().numpy(), ref_out)
-    log(f"  gated outputs rel-L2 {err:.3e}")
+    err = out_rel(out.cpu().numpy(), ref_out)
+    log(f"  gated outputs rel-L2 (worst of whole, per head) {err:.3e}")
     assert err <= OUT_TOL
     got = cache_d.cpu().numpy()
     singles = w.slot_ids[:40]
     multi = w.slot_ids[40:]
-    assert rel_l2(got[singles], cache_h[singles]) <= STATE_TOL
+    assert state_rel(got[singles], cache_h[singles]) <= STATE_TOL
     assert np.array_equal(got[multi].view(np.uint32), w.cache[multi].view(np.uint32))
     # replay rows only for the multi-token rows; single rows leave the buffer alone
     rk = bits(rb["k"])
@@ -174,8 +174,8 @@ def test_mixed_batch_inplace_gate_and_commit():
     assert oracle.commit(cache_h, w.slot_ids, w.cu_seqlens, acc, w.T_max, w.k[0], w.v[0], w.alpha[0],
                          w.beta[0]) == 0
     got = cache_d.cpu().numpy()
-    serr = rel_l2(got[w.slot_ids], cache_h[w.slot_ids])
-    log(f"  committed states rel-Frobenius {serr:.3e}")
+    serr = state_rel(got[w.slot_ids], cache_h[w.slot_ids])
+    log(f"  committed states rel-Frobenius (worst of whole, per head) {serr:.3e}")
     assert serr <= STATE_TOL
     untouched = np.setdiff1d(np.arange(w.num_slots), w.slot_ids)
     assert np.array_equal(got[untouched].view(np.uint32), w.cache[untouched].view(np.uint32))
@@ -200,20 +200,20 @@ def test_ragged_rows_both_modes(dk, dv):
         live = np.concatenate([np.arange(w.cu_seqlens[b], w.cu_seqlens[b + 1]) for b in range(7) if b != 4])
         pad_rows = np.arange(w.cu_seqlens[4], w.cu_seqlens[5])
         assert np.all(bits(out)[pad_rows] == SENTINEL_BITS)
-        assert rel_l2(o[live], ref_out[live]) <= OUT_TOL
+        assert out_rel(o[live], ref_out[live]) <= OUT_TOL
         _commit(w, cache_d, mode, acc, rb, draft, slots=slots)
         torch.cuda.synchronize()
         res[mode] = (bits(out), bits(cache_d))
     o0, o1 = res[0][0].view(np.float32), res[1][0].view(np.float32)
     live_rows = ~np.isnan(o1).any(axis=(1, 2))
-    assert rel_l2(o0[live_rows], o1[live_rows]) <= 1e-5
+    assert out_rel(o0[live_rows], o1[live_rows]) <= 1e-5
     assert np.array_equal(res[0][0][~live_rows], res[1][0][~live_rows])     # padding rows untouched
     assert np.array_equal(res[0][1], res[1][1])
     cache_h = w.cache.copy()
     assert oracle.commit(cache_h, slots, w.cu_seqlens, acc, w.T_max, w.k[0], w.v[0], w.alpha[0], w.beta[0]) == 0
     got = res[0][1].view(np.float32)
     live_slots = slots[[0, 2, 3, 5, 6]]
-    assert rel_l2(got[live_slots], cache_h[live_slots]) <= STATE_TOL
+    assert state_rel(got[live_slots], cache_h[live_slots]) <= STATE_TOL
     assert np.array_equal(res[0][1][slots[1]], w.cache[slots[1]].view(np.uint32))   # accepted 0
     others = np.setdiff1d(np.arange(w.num_slots), live_slots)
     assert np.array_equal(res[0][1][others], w.cache[others].view(np.uint32))
@@ -253,7 +253,7 @@ def test_device_errors_skip_only_their_rows():
     for b in range(w.B):
         lo, hi = cu_bad[b], cu_bad[b + 1]
         if lo >= 0 and hi >= lo and hi - lo <= w.T_max and hi <= w.n_tok:
-            assert rel_l2(out.cpu().numpy()[lo:hi], ref_out[lo:hi]) <= OUT_TOL
+            assert out_rel(out.cpu().numpy()[lo:hi], ref_out[lo:hi]) <= OUT_TOL
     # accepted length past the row: bit 4, that slot unchanged, the others committed
     cache_d = f32(w.cache)
     out, rb, _ = _verify(w, cache_d, K.KDA_REPLAY)
@@ -268,7 +268,7 @@ def test_device_errors_skip_only_their_rows():
     got = cache_d.cpu().numpy()
     assert np.array_equal(got[w.slot_ids[1]].view(np.uint32), w.cache[w.slot_ids[1]].view(np.uint32))
     ok = w.slot_ids[[0, 2, 3]]
-    assert rel_l2(got[ok], cache_h[ok]) <= STATE_TOL
+    assert state_rel(got[ok], cache_h[ok]) <= STATE_TOL
     # slot past the cache in verify and commit: bit 1
     slots = w.slot_ids.copy()
     slots[3] = w.num_slots
@@ -314,8 +314,8 @@ def test_chunked_form_matches_oracle_and_recurrent_form(dk, dv, seqlens):
         out, rb, _ = _verify(w, cache_d, K.KDA_REPLAY, slots=slots, form=form)
         torch.cuda.synchronize()
         o = out.cpu().numpy()
-        err = rel_l2(o[live], ref_out[live])
-        log(f"  outputs rel-L2 vs oracle {err:.3e}")
+        err = out_rel(o[live], ref_out[live])
+        log(f"  outputs rel-L2 (worst of whole, per head) vs oracle {err:.3e}")
         assert err <= OUT_TOL
         assert np.all(bits(out)[pad] == SENTINEL_BITS)
         assert np.array_equal(bits(cache_d), w.cache.view(np.uint32))
@@ -326,7 +326,7 @@ def test_chunked_form_matches_oracle_and_recurrent_form(dk, dv, seqlens):
                     n = w.seqlens[b]
                     assert np.array_equal(got[b, :n], ref_rb[rk][b, :n])
         outs[form] = o
-    assert rel_l2(outs[K.KDA_VERIFY_CHUNKED][live], outs[K.KDA_VERIFY_RECURRENT][live]) <= 1e-5
+    assert out_rel(outs[K.KDA_VERIFY_CHUNKED][live], outs[K.KDA_VERIFY_RECURRENT][live]) <= 1e-5
 
 
 @pytest.mark.parametrize("seqlens", [[16, 16, 9], [8, 8, 5]], ids=["upto16", "upto8"])
@@ -348,7 +348,7 @@ def test_chunked_form_with_extreme_decays(seqlens):
     torch.cuda.synchronize()
     o = out.cpu().numpy()
     assert np.all(np.isfinite(o))
-    assert rel_l2(o, ref_out) <= OUT_TOL
+    assert out_rel(o, ref_out) <= OUT_TOL
 
 
 @pytest.mark.parametrize("B,T,expect", [(16, 8, K.KDA_VERIFY_CHUNKED), (8, 8, K.KDA_VERIFY_CHUNKED),
@@ -415,4 +415,82 @@ def test_chunked_form_state_load_orders_agree(dk, dv, tmax):
         assert np.array_equal(res[0][1][k], res[1][1][k]), k
     ref_out, _, _, rc = _oracle_verify(w, K.KDA_REPLAY, slots=slots)
     assert rc == 0
-    assert rel_l2(res[0][0].view(np.float32), ref_out[:n16]) <= OUT_TOL
+    assert out_rel(res[0][0].view(np.float32), ref_out[:n16]) <= OUT_TOL
+
+
+@pytest.mark.parametrize("mode", [0, 1], ids=["replay", "per_position"])
+def test_commit_without_cu_seqlens_equals_steps(mode):
+    """kda_replay_commit with cu_seqlens NULL takes T_b = T_max for every row and ignores
+    n_tok (the commit reads only its buffers): with n_tok = 0 the committed slots equal
+    accepted_len[b] single-token steps bit for bit."""
+    w = synth.make_workload("spec_verify")
+    acc = w.accepted
+    x = step_inputs(w, 0)
+    steps_d = f32(w.cache)
+    for t in range(w.T_max):
+        r = torch.from_numpy((w.cu_seqlens[:-1] + t).astype(np.int64)).to(dev())
+        tok = {n: x[n][r].contiguous() for n in ("q", "k", "v", "alpha", "beta")}
+        masked = np.where(acc > t, w.slot_ids, -1).astype(np.int32)
+        log(f"single-token step {t}")
+        K.kda_decode_step(steps_d, i32(masked), tok["q"], tok["k"], tok["v"], tok["alpha"], tok["beta"],
+                          torch.empty(w.B, w.H, w.dv, device=dev()))
+    cache_d = f32(w.cache)
+    log(f"verify mode {mode}, then commit with cu_seqlens NULL and n_tok 0")
+    _, rb, draft = _verify(w, cache_d, mode)
+    err = torch.zeros(1, dtype=torch.int32, device=dev())
+    K.kda_replay_commit(cache_d, i32(w.slot_ids), None, i32(acc), w.T_max, 0, mode=mode, replay=rb, draft=draft,
+                        dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert np.array_equal(bits(cache_d), bits(steps_d))
+    # an accepted length past T_max is still caught without cu_seqlens
+    bad = acc.copy()
+    bad[3] = w.T_max + 1
+    cache_b = f32(w.cache)
+    K.kda_replay_commit(cache_b, i32(w.slot_ids), None, i32(bad), w.T_max, 0, mode=mode, replay=rb, draft=draft,
+                        dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == K.KDA_DEVERR_ACCEPTED
+    got = bits(cache_b)
+    assert np.array_equal(got[w.slot_ids[3]], w.cache[w.slot_ids[3]].view(np.uint32))
+    others = np.delete(w.slot_ids, 3)
+    assert np.array_equal(got[others], bits(steps_d)[others])
+
+
+def test_mixed_batch_shuffled_order():
+    """The mixed batch's stress order: 40 single-token rows and 24 four-token rows interleaved
+    at random, single-token rows in place, output gate with a random weight, then the commit,
+    against the oracle; untouched slots bit-exact."""
+    rng = np.random.Generator(np.random.PCG64(41))
+    lens = np.array([1] * 40 + [4] * 24)[rng.permutation(64)]
+    w = synth.make(64, 32, 128, 128, seqlens=lens, num_slots=512, state_std=0.02, gate=True, seed=42,
+                   name="mixed_shuffled")
+    weight = rng.uniform(0.5, 2.0, w.dv).astype(np.float32)
+    acc = w.accepted.copy()               # 0 for the single-token rows
+    cache_d = f32(w.cache)
+    log("mixed shuffled: verify with in-place singles, gate, weight")
+    out, rb, _ = _verify(w, cache_d, K.KDA_REPLAY, t1_inplace=True, gate=True, weight=f32(weight))
+    torch.cuda.synchronize()
+    cache_h = w.cache.copy()
+    ref_out, ref_rb, _, rc = oracle.verify(cache_h, w.slot_ids, w.cu_seqlens, w.T_max, w.q[0], w.k[0], w.v[0],
+                                           w.alpha[0], w.beta[0], mode=oracle.REPLAY, t1_inplace=True,
+                                           gate=w.gate[0], weight=weight, eps=1e-6)
+    assert rc == 0
+    assert out_rel(out.cpu().numpy(), ref_out, "gated outputs") <= OUT_TOL
+    single = lens == 1
+    got = cache_d.cpu().numpy()
+    assert state_rel(got[w.slot_ids[single]], cache_h[w.slot_ids[single]], "in-place states") <= STATE_TOL
+    multi = w.slot_ids[~single]
+    assert np.array_equal(got[multi].view(np.uint32), w.cache[multi].view(np.uint32))
+    rk = bits(rb["k"])
+    assert np.array_equal(rk[~single], ref_rb["rk"][~single])
+    assert np.all(rk[single] == 0)
+    log("mixed shuffled: commit")
+    _commit(w, cache_d, K.KDA_REPLAY, acc, rb, None)
+    torch.cuda.synchronize()
+    assert oracle.commit(cache_h, w.slot_ids, w.cu_seqlens, acc, w.T_max, w.k[0], w.v[0], w.alpha[0],
+                         w.beta[0]) == 0
+    got = cache_d.cpu().numpy()
+    assert state_rel(got[w.slot_ids], cache_h[w.slot_ids], "committed states") <= STATE_TOL
+    untouched = np.setdiff1d(np.arange(w.num_slots), w.slot_ids)
+    assert np.array_equal(got[untouched].view(np.uint32), w.cache[untouched].view(np.uint32))
