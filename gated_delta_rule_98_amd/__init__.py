@@ -13,6 +13,7 @@ from .kda import (  # noqa: F401
     KDA_ERR_ALIGN,
     KDA_ERR_HIP,
     KDA_ERR_INVALID,
+    KDA_ERR_TOO_LARGE,
     KDA_ERR_UNSUPPORTED,
     KDA_OK,
     KDA_OP_COMMIT_COPY,
@@ -27,11 +28,13 @@ from .kda import (  # noqa: F401
     KDA_VERIFY_AUTO,
     KDA_VERIFY_CHUNKED,
     KDA_VERIFY_RECURRENT,
+    KDA_NOALLOC_SCRATCH_BYTES,
     LIB_PATH,
     KdaError,
     kda_decode_step,
     kda_prefill,
     kda_prefill_chunked,
+    kda_prefill_chunked_noalloc,
     kda_prefill_chunked_workspace,
     kda_query_variant,
     kda_replay_commit,

@@ -5,10 +5,18 @@
 
 #include <string.h>
 
+#include <mutex>
+
 #include "kda_chunk.h"
 #include "kda_engine.h"
 
 using namespace kda;
+
+// Static scratch of kda_prefill_chunked_noalloc: the chunk-prefill workspace for
+// callers that cannot allocate. Every GPU the library runs on holds its own copy
+// until the process ends. Host code never uses this name as an address: the
+// per-device address comes from hipGetSymbolAddress (scratch_for_current_device).
+static __device__ __align__(256) float scratch[KDA_NOALLOC_SCRATCH_BYTES / sizeof(float)];
 
 namespace {
 
@@ -187,6 +195,26 @@ int check_replay_buf(const kda_replay_buf *rb) {
 
 }  // namespace
 
+// Device address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+int scratch_for_current_device(void **ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return KDA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return KDA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KDA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return KDA_OK;
+}
+
 // Chunks the chunk form of prefill can meet: each row is cut at most once (at
 // its checkpoint) and then into chunks, so at most ceil(n_tok / L) + 2 B.
 int64_t prefill_chunk_bound(int64_t B, int64_t n_tok) {
@@ -262,6 +290,21 @@ int kda_prefill_chunked(float *cache, int64_t num_slots, int64_t slot_stride, co
   const hipError_t e = hipLaunchKernel(prefill_chunk_state_kernel_for(dk, dv), dim3((unsigned)state_blocks),
                                        dim3(256), args, 0, (hipStream_t)stream);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_prefill_chunked_noalloc(float *cache, int64_t num_slots, int64_t slot_stride, const int32_t *slot_ids,
+                                const int32_t *cu_seqlens, int32_t B, int32_t n_tok, int32_t H, int32_t dk,
+                                int32_t dv, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                const float *alpha, const float *beta, void *out, const int32_t *ckpt_pos,
+                                float *ckpt, int32_t *dev_err, const kda_options *opts, void *stream) {
+  size_t need = 0;
+  KDA_TRY(kda_prefill_chunked_workspace(B, n_tok, H, dk, dv, &need));
+  if (B == 0 || (n_tok == 0 && !ckpt_pos)) return KDA_OK;
+  if (need > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_TOO_LARGE;
+  void *ws = nullptr;
+  KDA_TRY(scratch_for_current_device(&ws));
+  return kda_prefill_chunked(cache, num_slots, slot_stride, slot_ids, cu_seqlens, B, n_tok, H, dk, dv, q, k, v,
+                             alpha, beta, out, ckpt_pos, ckpt, ws, KDA_NOALLOC_SCRATCH_BYTES, dev_err, opts, stream);
 }
 
 int kda_prefill(float *cache, int64_t num_slots, int64_t slot_stride, const int32_t *slot_ids,
@@ -571,6 +614,7 @@ const char *kda_status_str(int32_t status) {
     case KDA_ERR_UNSUPPORTED: return "unsupported shape or launch width";
     case KDA_ERR_ALIGN: return "misaligned pointer or stride";
     case KDA_ERR_HIP: return "HIP launch failed";
+    case KDA_ERR_TOO_LARGE: return "the call needs more than the library's static scratch holds";
   }
   return "unknown status";
 }

@@ -23,6 +23,9 @@ KDA_ERR_INVALID = -1
 KDA_ERR_UNSUPPORTED = -2
 KDA_ERR_ALIGN = -3
 KDA_ERR_HIP = -4
+KDA_ERR_TOO_LARGE = -5
+
+KDA_NOALLOC_SCRATCH_BYTES = 256 << 20   # the library's static workspace of kda_prefill_chunked_noalloc
 
 KDA_REPLAY = 0
 KDA_PER_POSITION = 1
@@ -91,6 +94,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_prefill_chunked.argtypes = [P, i64, i64, P, P, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P,
                                         P, ctypes.c_size_t, P, P, P]
     lib.kda_prefill_chunked.restype = ctypes.c_int
+    lib.kda_prefill_chunked_noalloc.argtypes = [P, i64, i64, P, P, i32, i32, i32, i32, i32, P, P, P, P, P, P,
+                                                P, P, P, P, P]
+    lib.kda_prefill_chunked_noalloc.restype = ctypes.c_int
     lib.kda_prefill_chunked_workspace.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.kda_prefill_chunked_workspace.restype = ctypes.c_int
     for name in ("kda_state_pack", "kda_state_unpack"):
@@ -356,13 +362,8 @@ def kda_prefill_chunked_workspace(B: int, n_tok: int, H: int, dk: int, dv: int) 
     return n.value
 
 
-def kda_prefill_chunked(cache: torch.Tensor, slot_ids: torch.Tensor, cu_seqlens: torch.Tensor, q, k, v, alpha,
-                        beta, out: torch.Tensor, *, ckpt_pos: Optional[torch.Tensor] = None,
-                        ckpt: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                        dev_err: Optional[torch.Tensor] = None, tile_w: int = 0, raw_inputs: bool = False,
-                        stream=None) -> None:
-    """Chunk form of kda_prefill: same arguments plus a device workspace (any dtype, at least
-    kda_prefill_chunked_workspace() bytes); None allocates one for the call."""
+def _prefill_chunked_checks(cache, slot_ids, cu_seqlens, q, k, v, alpha, beta, out, ckpt_pos, ckpt, dev_err):
+    """Shape and dtype checks shared by both chunk-prefill calls; returns (B, n_tok, H, dk, dv, ns, stride)."""
     ns, stride, H, dv, dk = _cache(cache)
     _dev(slot_ids, "slot_ids", (torch.int32,), 1)
     _dev(cu_seqlens, "cu_seqlens", (torch.int32,), 1)
@@ -387,6 +388,18 @@ def kda_prefill_chunked(cache: torch.Tensor, slot_ids: torch.Tensor, cu_seqlens:
         _shape(ckpt, "ckpt", (B, H, dv, dk))
     if dev_err is not None:
         _dev(dev_err, "dev_err", (torch.int32,))
+    return B, n_tok, H, dk, dv, ns, stride
+
+
+def kda_prefill_chunked(cache: torch.Tensor, slot_ids: torch.Tensor, cu_seqlens: torch.Tensor, q, k, v, alpha,
+                        beta, out: torch.Tensor, *, ckpt_pos: Optional[torch.Tensor] = None,
+                        ckpt: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                        dev_err: Optional[torch.Tensor] = None, tile_w: int = 0, raw_inputs: bool = False,
+                        stream=None) -> None:
+    """Chunk form of kda_prefill: same arguments plus a device workspace (any dtype, at least
+    kda_prefill_chunked_workspace() bytes); None allocates one for the call."""
+    B, n_tok, H, dk, dv, ns, stride = _prefill_chunked_checks(cache, slot_ids, cu_seqlens, q, k, v, alpha, beta,
+                                                              out, ckpt_pos, ckpt, dev_err)
     if workspace is None:
         workspace = torch.empty(kda_prefill_chunked_workspace(B, n_tok, H, dk, dv), dtype=torch.uint8,
                                 device=cache.device)
@@ -399,6 +412,23 @@ def kda_prefill_chunked(cache: torch.Tensor, slot_ids: torch.Tensor, cu_seqlens:
         _ptr(dev_err), _ref(_opts(tile_w, 0, _flags(raw_inputs, out))), _stream(stream))
     if rc != KDA_OK:
         raise KdaError(rc, "kda_prefill_chunked")
+
+
+def kda_prefill_chunked_noalloc(cache: torch.Tensor, slot_ids: torch.Tensor, cu_seqlens: torch.Tensor, q, k, v,
+                                alpha, beta, out: torch.Tensor, *, ckpt_pos: Optional[torch.Tensor] = None,
+                                ckpt: Optional[torch.Tensor] = None, dev_err: Optional[torch.Tensor] = None,
+                                tile_w: int = 0, raw_inputs: bool = False, stream=None) -> None:
+    """kda_prefill_chunked on the library's static per-GPU workspace: nothing is allocated
+    (KdaError KDA_ERR_TOO_LARGE past KDA_NOALLOC_SCRATCH_BYTES). Calls that overlap on one GPU race."""
+    B, n_tok, H, dk, dv, ns, stride = _prefill_chunked_checks(cache, slot_ids, cu_seqlens, q, k, v, alpha, beta,
+                                                              out, ckpt_pos, ckpt, dev_err)
+    rc = load_library().kda_prefill_chunked_noalloc(
+        cache.data_ptr(), ns, stride, slot_ids.data_ptr(), cu_seqlens.data_ptr(), B, n_tok, H, dk, dv,
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), alpha.data_ptr(), beta.data_ptr(), out.data_ptr(),
+        _ptr(ckpt_pos), _ptr(ckpt), _ptr(dev_err), _ref(_opts(tile_w, 0, _flags(raw_inputs, out))),
+        _stream(stream))
+    if rc != KDA_OK:
+        raise KdaError(rc, "kda_prefill_chunked_noalloc")
 
 
 def _state_copy(name, cache, slot_ids, buf, heads, cols, dev_err, stream):

@@ -77,7 +77,9 @@ enum kda_status {
     KDA_ERR_ALIGN = -3,       /* cache / alpha / draft / replay alpha not 16-byte aligned, slot_stride
                                  not a multiple of 4, bf16 input arrays not 8-byte aligned, out / beta
                                  not 4-byte aligned (bf16 out: 2-byte) */
-    KDA_ERR_HIP = -4          /* the HIP runtime rejected a launch */
+    KDA_ERR_HIP = -4,         /* the HIP runtime rejected a launch */
+    KDA_ERR_TOO_LARGE = -5    /* kda_prefill_chunked_noalloc: the call needs more workspace than
+                                 KDA_NOALLOC_SCRATCH_BYTES */
 };
 
 enum kda_mode { KDA_REPLAY = 0, KDA_PER_POSITION = 1 };
@@ -275,6 +277,32 @@ int kda_prefill_chunked(float *cache, int64_t num_slots, int64_t slot_stride,
  * (written to *bytes): about 2.1 KB per (token, head) at dk = dv = 128. */
 int kda_prefill_chunked_workspace(int32_t B, int32_t n_tok, int32_t H, int32_t dk, int32_t dv,
                                   size_t *bytes);
+
+/*
+ * kda_prefill_chunked without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The workspace is a static device array of
+ * KDA_NOALLOC_SCRATCH_BYTES owned by the library: each GPU the library runs on
+ * holds its own copy until the process ends, and the call allocates nothing.
+ * Arguments, layouts, flags, results and device errors are kda_prefill_chunked's.
+ * A call whose kda_prefill_chunked_workspace() size exceeds
+ * KDA_NOALLOC_SCRATCH_BYTES returns KDA_ERR_TOO_LARGE and enqueues nothing (at
+ * H = 32, dk = dv = 128 and B = 1 the limit is a prompt of about 3,700 tokens).
+ * Every call on one GPU uses that GPU's one array: calls that can overlap on
+ * one GPU (other streams, other host threads) race and must be serialized by
+ * the caller. The array keeps the last call's contents; nothing in it needs to
+ * start at zero. The first call on each device looks the array's device
+ * address up (hipGetSymbolAddress) with that device current.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+int kda_prefill_chunked_noalloc(float *cache, int64_t num_slots, int64_t slot_stride,
+                                const int32_t *slot_ids, const int32_t *cu_seqlens,
+                                int32_t B, int32_t n_tok, int32_t H, int32_t dk, int32_t dv,
+                                const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                const float *alpha, const float *beta, void *out,
+                                const int32_t *ckpt_pos, float *ckpt, int32_t *dev_err,
+                                const kda_options *opts, void *stream);
 
 /*
  * State transfer for prefill/decode disaggregation and offload ("Kimi K3

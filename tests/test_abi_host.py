@@ -27,6 +27,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert set(declared_functions()) == {"kda_decode_step", "kda_verify_chunk", "kda_replay_commit",
                                          "kda_prefill", "kda_prefill_chunked", "kda_prefill_chunked_workspace",
+                                         "kda_prefill_chunked_noalloc",
                                          "kda_state_pack", "kda_state_unpack",
                                          "kda_query_variant", "kda_status_str"}
 
@@ -115,7 +116,7 @@ def test_query_variant_launch_shapes():
 
 def test_status_strings():
     assert kda.kda_status_str(0) == "ok"
-    for code in (-1, -2, -3, -4):
+    for code in (-1, -2, -3, -4, -5):
         assert kda.kda_status_str(code) not in ("ok", "unknown status")
     assert kda.kda_status_str(7) == "unknown status"
 
@@ -291,6 +292,33 @@ def test_prefill_chunked_host_checks():
     assert _prefill_chunked(out=A + 2) == E.KDA_ERR_ALIGN
     # passes every host check: only the launch fails without a device
     assert _prefill_chunked(out=A + 2, opts=ctypes.byref(kda.kda_options(16, 0, E.KDA_OUT_BF16))) == E.KDA_ERR_HIP
+
+
+def _prefill_noalloc(**over):
+    d = dict(cache=A, num_slots=8, slot_stride=2 * 128 * 128, slot_ids=A, cu=A, B=4, n_tok=90, H=2, dk=128,
+             dv=128, q=A, k=A, v=A, alpha=A, beta=A, out=A, ckpt_pos=None, ckpt=None, dev_err=None, opts=None,
+             stream=None)
+    d.update(over)
+    return kda.load_library().kda_prefill_chunked_noalloc(*d.values())
+
+
+@needs_no_gpu
+def test_prefill_chunked_noalloc_host_checks():
+    """The static-scratch variant: the size limit and the argument checks come before any
+    device call; a call that passes them needs the device (the scratch address lookup)."""
+    E = kda
+    per_chunk_head = (3 * 32 * 128 + 32 * 128 + 32 * 32 + 128) * 4
+    limit_chunks = E.KDA_NOALLOC_SCRATCH_BYTES // (32 * per_chunk_head)      # chunks at H = 32
+    fits = (limit_chunks - 2) * 32                                          # tokens of one row (B = 1)
+    assert _prefill_noalloc(B=0) == E.KDA_OK
+    assert _prefill_noalloc(n_tok=0) == E.KDA_OK
+    assert _prefill_noalloc(dk=96) == E.KDA_ERR_UNSUPPORTED
+    assert _prefill_noalloc(n_tok=-1) == E.KDA_ERR_INVALID
+    assert _prefill_noalloc(B=1, H=32, slot_stride=32 * 128 * 128, n_tok=fits + 32) == E.KDA_ERR_TOO_LARGE
+    assert _prefill_noalloc(B=1, H=32, slot_stride=32 * 128 * 128, n_tok=1 << 30) == E.KDA_ERR_TOO_LARGE
+    # within the limit every host check passes; without a device the scratch lookup fails
+    assert _prefill_noalloc(B=1, H=32, slot_stride=32 * 128 * 128, n_tok=fits) == E.KDA_ERR_HIP
+    assert fits >= 3600
 
 
 def _pack(**over):
