@@ -428,14 +428,15 @@ int kda_verify_chunk(float *cache, int64_t num_slots, int64_t slot_stride, const
   const bool chunk_fits = mode == KDA_REPLAY && !t1_inplace && epi == nullptr && !a.raw && !a.out_bf16;
   if (form == KDA_VERIFY_CHUNKED && (!chunk_fits || (opts && opts->tile_w != 0))) return KDA_ERR_UNSUPPORTED;
   // Automatic choice, from graph-timed runs on MI355X at H = 32, d = 128 with every row
-  // holding T tokens: the chunk form is faster from 8 tokens once there are at least 256
-  // (row, head) groups (B = 8, T = 8: 7.9 against 9.3 us; B = 16, T = 8: 11.4 against
-  // 15.6 us; B = 16, T = 16: 17.6 against 26.3 us); with fewer tokens or groups its longer
-  // per-group latency loses (B = 4, T = 8: 7.4 against 6.7 us; B = 32, T = 4: 20.8 against
-  // 17.3 us).
+  // holding T tokens (us, chunk / recurrent): the chunk form wins from 7 tokens at 128 or
+  // more (row, head) groups (T = 8: B = 4 6.2 / 6.7, B = 16 11.1 / 15.5, B = 64 38.2 /
+  // 48.6) and at 5 or 6 tokens from 256 groups (T = 6: B = 8 6.5 / 8.1, B = 64 37.1 /
+  // 40.5); with fewer tokens or groups its per-group latency loses (T = 8, B = 2: 5.9 /
+  // 5.1; T = 4, B = 64: 36.0 / 31.3; T = 2, B = 16: 9.7 / 8.0).
+  const int64_t groups = (int64_t)B * H;
+  const bool auto_chunk = (T_max >= 7 && groups >= 128) || (T_max >= 5 && groups >= 256);
   const bool chunked = form == KDA_VERIFY_CHUNKED ||
-                       (form == KDA_VERIFY_AUTO && chunk_fits && (!opts || opts->tile_w == 0) && T_max >= 8 &&
-                        (int64_t)B * H >= 256);
+                       (form == KDA_VERIFY_AUTO && chunk_fits && (!opts || opts->tile_w == 0) && auto_chunk);
   Launch l;
   if (chunked) {
     l = {dv, dv / 16, 0};

@@ -131,9 +131,9 @@ typedef struct kda_replay_buf {
  *     have no output gate. Outputs agree with the recurrent form to rounding;
  *     replay buffers and committed states are identical.
  *   KDA_VERIFY_AUTO: the faster form on MI355X: the chunk form where it applies,
- *     with tile_w = 0, T_max >= 8 and B * H >= 256; the recurrent form
- *     otherwise (fewer tokens or (row, head) groups leave the chunk form's
- *     per-group latency exposed). */
+ *     with tile_w = 0 and either T_max >= 7 and B * H >= 128 or T_max >= 5 and
+ *     B * H >= 256; the recurrent form otherwise (fewer tokens or (row, head)
+ *     groups leave the chunk form's per-group latency exposed). */
 enum kda_verify_form { KDA_VERIFY_AUTO = 0, KDA_VERIFY_RECURRENT = 1, KDA_VERIFY_CHUNKED = 2 };
 
 /* Option flags (kda_options.flags, OR-ed).

@@ -351,11 +351,13 @@ def test_chunked_form_with_extreme_decays(seqlens):
     assert out_rel(o, ref_out) <= OUT_TOL
 
 
-@pytest.mark.parametrize("B,T,expect", [(16, 8, K.KDA_VERIFY_CHUNKED), (8, 8, K.KDA_VERIFY_CHUNKED),
-                                         (4, 8, K.KDA_VERIFY_RECURRENT), (16, 4, K.KDA_VERIFY_RECURRENT)])
+@pytest.mark.parametrize("B,T,expect", [(16, 8, K.KDA_VERIFY_CHUNKED), (4, 8, K.KDA_VERIFY_CHUNKED),
+                                         (2, 8, K.KDA_VERIFY_RECURRENT), (8, 6, K.KDA_VERIFY_CHUNKED),
+                                         (4, 6, K.KDA_VERIFY_RECURRENT), (16, 4, K.KDA_VERIFY_RECURRENT)])
 def test_auto_form_choice(B, T, expect):
-    """The automatic form is the chunk form from 8 tokens and 256 (row, head) groups,
-    the recurrent form below (both are deterministic, so the outputs match bit for bit)."""
+    """The automatic form is the chunk form from 7 tokens at 128 (row, head) groups and from 5
+    tokens at 256 groups, the recurrent form otherwise (both are deterministic, so the outputs
+    match bit for bit)."""
     w = synth.make(B, 32, 128, 128, seqlens=[T] * B, num_slots=B, state_std=0.05, seed=60 + B + T)
     outs = {}
     for form in (K.KDA_VERIFY_AUTO, expect):
