@@ -10,8 +10,11 @@ streamed through the 256 MB Infinity Cache: the state comes from HBM.
 Prints one JSON line on stdout:
   value         decode steps per second (K steps bracketed by synchronizations)
   roofline      HBM bytes the step must move per launch / the kernel's average
-                duration (HIP events around each launch, on its stream) vs 8 TB/s
-  cpu_baseline  the CPU oracle on this host's cores, on a bounded sample
+                duration (HIP events on its stream, median of 3 timed regions) vs
+                8 TB/s; beside it the rate of a plain in-place read-modify-write of
+                the same state bytes (the ceiling probe, libkda_ceiling.so)
+  cpu_baseline  the CPU oracle on this host's cores (all of them, and one), on a
+                bounded sample, median of 3
   breakdown     the batch sweep, the B=1 1024-step latency path (plain launches and
                 one captured HIP graph), the speculative verify + commit in both
                 buffer modes and the mixed gated batch, each with its own
@@ -149,7 +152,8 @@ def per_launch_ms(D, launch, n):
 
 
 def graph_ms(D, launch, n, replays=3):
-    """Average GPU time per launch: n launches captured once in a HIP graph, replayed."""
+    """GPU time per launch: n launches captured once in a HIP graph, replayed; the median of
+    3 timed sets of `replays` replays."""
     torch = D.torch
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
@@ -161,13 +165,16 @@ def graph_ms(D, launch, n, replays=3):
     torch.cuda.current_stream().wait_stream(stream)
     graph.replay()
     D.sync()
-    a, b = D.event(), D.event()
-    a.record()
-    for _ in range(replays):
-        graph.replay()
-    b.record()
-    D.sync()
-    return a.elapsed_time(b) / (n * replays)
+    times = []
+    for _ in range(3):
+        a, b = D.event(), D.event()
+        a.record()
+        for _ in range(replays):
+            graph.replay()
+        b.record()
+        D.sync()
+        times.append(a.elapsed_time(b) / (n * replays))
+    return float(np.median(times))
 
 
 # ----------------------------------------------------------------------------- workloads
@@ -194,17 +201,19 @@ def headline(D, K, synth, steps, warmup):
     for i in range(warmup):
         launch(i)
     D.sync()
-    total_ms = timed_region(D, launch, steps)
-    ms_step = total_ms / steps
-    # the K launches above run back to back on one stream with no other work, so the
-    # region's average is the kernel's average duration (rocprofv3 agrees to ~1%)
+    # three timed regions of K launches each; the median region gives the figure
+    regions = [timed_region(D, launch, steps) / steps for _ in range(3)]
+    ms_step = float(np.median(regions))
+    # the K launches of a region run back to back on one stream with no other work, so
+    # the region's average is the kernel's average duration (rocprofv3 agrees to ~1%)
     kernel_ms = ms_step
     pairs_ms = per_launch_ms(D, launch, min(steps, 200))
     hot_ms = timed_region(D, lambda i: launch(i, hot=True), min(steps, 200)) / min(steps, 200)
-    log(f"headline: {ms_step * 1e3:.2f} us/step ({nbytes / kernel_ms / 1e6:.1f} GB/s); "
+    log(f"headline: regions {', '.join(f'{r * 1e3:.2f}' for r in regions)} us/step; median "
+        f"{ms_step * 1e3:.2f} us/step ({nbytes / kernel_ms / 1e6:.1f} GB/s); "
         f"event pair per launch {pairs_ms * 1e3:.2f} us; same table every step (cache-resident) {hot_ms * 1e3:.2f} us")
     return dict(w=w, ms_step=ms_step, kernel_ms=kernel_ms, pairs_ms=pairs_ms, hot_ms=hot_ms, bytes=nbytes,
-                tile=K.kda_query_variant(B, 32, 128, 128))
+                regions_ms=regions, tile=K.kda_query_variant(B, 32, 128, 128))
 
 
 def batch_sweep(D, K, synth, reps):
@@ -514,37 +523,134 @@ def state_transfer(D, K, synth, reps):
     return res
 
 
-def copy_calibration(D, nbytes=256 << 20, reps=5):
-    """A plain device copy of known size (for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)."""
-    src = D.torch.empty(nbytes // 4, dtype=D.torch.float32, device=D.dev).normal_()
-    dst = D.torch.empty_like(src)
+def _ceiling_lib():
+    import ctypes
+
+    from gated_delta_rule_98_amd import build
+
+    if not os.path.exists(build.CEILING_LIB):
+        raise RuntimeError(f"{build.CEILING_LIB} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(build.CEILING_LIB)
+    P, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.kda_ceiling_rmw.argtypes = [P, i64, P]
+    lib.kda_ceiling_copy.argtypes = [P, P, i64, P]
+    lib.kda_ceiling_read.argtypes = [P, i64, P, P]
+    for fn in (lib.kda_ceiling_rmw, lib.kda_ceiling_copy, lib.kda_ceiling_read):
+        fn.restype = ctypes.c_int
+    return lib
+
+
+def ceiling(D, reps=200):
+    """The HBM rate of plain streams with the single-token step's state access shape (one
+    128-bit access per lane, one wave per workgroup, non-temporal): an in-place
+    read-modify-write of 128 MiB (the B=64 step's state bytes, read and written), a 128 MiB
+    copy and a 128 MiB read, each rotating over the four 128 MiB regions of a 512 MiB buffer
+    so that the data comes from HBM. Median of 3 timed regions of `reps` launches."""
+    lib = _ceiling_lib()
+    torch = D.torch
+    region = (128 << 20) // 4
+    buf = torch.ones(4 * region, device=D.dev)
+    sink = torch.zeros(64, device=D.dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    base = buf.data_ptr()
+
+    def rmw(i):
+        assert lib.kda_ceiling_rmw(base + (i % 4) * region * 4, region, stream) == 0
+
+    def copy(i):
+        assert lib.kda_ceiling_copy(base + (i % 4) * region * 4, base + ((i + 2) % 4) * region * 4, region,
+                                    stream) == 0
+
+    def read(i):
+        assert lib.kda_ceiling_read(base + (i % 4) * region * 4, region, sink.data_ptr(), stream) == 0
+
+    res = {}
+    for name, fn, moved in (("rmw_in_place", rmw, 2 * region * 4), ("copy", copy, 2 * region * 4),
+                            ("read", read, region * 4)):
+        for i in range(20):
+            fn(i)
+        ms = float(np.median([timed_region(D, fn, reps) / reps for _ in range(3)]))
+        res[name] = dict(us=round(ms * 1e3, 3), bytes=moved, gbs=round(moved / ms / 1e6, 1))
+        log(f"ceiling {name}: {ms * 1e3:.2f} us for {moved} B ({moved / ms / 1e6:.0f} GB/s)")
+    del buf
+    return res
+
+
+def copy_calibration(D, reps=5):
+    """Plain device copies of known size, 256 MiB read and 256 MiB written each (the ceiling
+    probe's copy_kernel), for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE."""
+    lib = _ceiling_lib()
+    n = (256 << 20) // 4
+    buf = D.torch.ones(2 * n, device=D.dev)
+    stream = D.torch.cuda.current_stream().cuda_stream
     for _ in range(reps):
-        dst.copy_(src)
+        assert lib.kda_ceiling_copy(buf.data_ptr(), buf.data_ptr() + n * 4, n, stream) == 0
     D.sync()
-    log(f"copy calibration: {reps} copies of {nbytes} bytes")
+    log(f"copy calibration: {reps} copies of {n * 4} bytes (copy_kernel)")
 
 
 # ----------------------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(w, budget_s=12.0, max_steps=2000):
-    """The CPU oracle (as it stands) on the headline workload, rotating the same slot tables."""
-    import oracle
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    threads = max(1, min(len(os.sched_getaffinity(0)), 16))
-    cache = w.cache.copy()
+
+def _rate(fn, seconds, max_calls=100000):
+    """Calls of fn per second over at least one call and about `seconds` of wall time."""
     n = 0
     t0 = time.perf_counter()
-    while n < max_steps:
-        table = w.slot_tables[n % len(w.slot_tables)]
-        oracle.decode(cache, table, w.q[0], w.k[0], w.v[0], w.alpha[0], w.beta[0], nthreads=threads)
+    while n < max_calls:
+        fn(n)
         n += 1
-        if time.perf_counter() - t0 >= budget_s:
+        if time.perf_counter() - t0 >= seconds:
             break
-    el = time.perf_counter() - t0
-    log(f"cpu baseline: {n} oracle steps in {el:.1f} s on {threads} threads")
-    return dict(value=round(n / el, 3), unit="steps/s", cores=threads, kind="oracle",
-                sample=f"{n} single-token steps of the B=64 H=32 d=128 workload (4 rotating slot tables), "
-                       f"{el:.1f} s wall; fp64 arithmetic with fp32 state")
+    return n / (time.perf_counter() - t0), n
+
+
+def cpu_baseline(w, seconds_scale=1.0):
+    """The CPU oracle (as it stands: fp64 arithmetic, fp32 state, one thread per (row, head)
+    item list) on this host: the B=64 H=32 d=128 single-token step on every core this process
+    may use and on one core, and the B=1 H=32 d=128 step (the 1024-step latency path's unit
+    of work) on every core and on one. Each figure is the median of 3 samples; about 20 s of
+    CPU time in all."""
+    import oracle
+    import synth
+
+    cores = len(os.sched_getaffinity(0))
+    b1 = synth.make(1, 32, 128, 128, num_slots=1, seed=5, name="b1")
+    res = {}
+    for key, work, threads, seconds in (("b64_all_cores", w, cores, 3.0), ("b64_one_core", w, 1, 2.0),
+                                        ("b1_all_cores", b1, cores, 1.0), ("b1_one_core", b1, 1, 1.0)):
+        cache = work.cache.copy()
+
+        def step(n, work=work, cache=cache, threads=threads):
+            table = work.slot_tables[n % len(work.slot_tables)]
+            oracle.decode(cache, table, work.q[0], work.k[0], work.v[0], work.alpha[0], work.beta[0],
+                          nthreads=threads)
+
+        samples = [_rate(step, seconds * seconds_scale) for _ in range(3)]
+        rates = [r for r, _ in samples]
+        res[key] = dict(steps_per_s=round(float(np.median(rates)), 3),
+                        us_per_step=round(1e6 / float(np.median(rates)), 1),
+                        samples_steps_per_s=[round(r, 3) for r in rates], threads=threads,
+                        steps_per_sample=[n for _, n in samples])
+        log(f"cpu baseline {key}: {', '.join(f'{r:.2f}' for r in rates)} steps/s on {threads} thread(s)")
+    nbytes = decode_bytes(64, 32, 128, 128)
+    main = res["b64_all_cores"]
+    return dict(value=main["steps_per_s"], unit="steps/s", cores=cores, kind="oracle",
+                sample="median of 3 samples of ~3 s each: single-token steps of the B=64 H=32 d=128 workload "
+                       "(4 rotating slot tables) on every core this process may use; fp64 arithmetic with "
+                       "fp32 state",
+                gbs=round(nbytes * main["steps_per_s"] / 1e9, 3), cpu_count=os.cpu_count(), affinity_cores=cores,
+                cpu_model=_cpu_model(), one_core_steps_per_s=res["b64_one_core"]["steps_per_s"],
+                b1_us_per_step_all_cores=res["b1_all_cores"]["us_per_step"],
+                b1_us_per_step_one_core=res["b1_one_core"]["us_per_step"], detail=res)
 
 
 # ----------------------------------------------------------------------------- counters
@@ -581,7 +687,7 @@ def main():
     ap.add_argument("--no-breakdown", action="store_true", help="headline only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run plain device copies of 256 MiB (for counter scaling)")
+                    help="also run plain device copies of 256 MiB (copy_kernel, for counter scaling)")
     ap.add_argument("--only", default="",
                     help="comma-separated breakdown parts to run (default: all), e.g. spec_verify,mixed")
     args = ap.parse_args()
@@ -618,6 +724,7 @@ def main():
             prefill_8k_checkpoint_chunked=lambda: prefill_8k(D, K, synth, reps=5, chunked=True),
             state_transfer_64x32_heads=lambda: state_transfer(D, K, synth, reps=100),
             raw_inputs_decode=lambda: raw_inputs_decode(D, K, synth, reps=200),
+            hbm_ceiling=lambda: ceiling(D),
         )
         only = [p for p in args.only.split(",") if p]
         unknown = [p for p in only if not any(name.startswith(p) for name in parts)]
@@ -628,6 +735,7 @@ def main():
         breakdown["headline_same_table_kernel_us"] = round(h["hot_ms"] * 1e3, 3)
     if args.copy_calibration:
         copy_calibration(D)
+    ceil = breakdown["hbm_ceiling"] if breakdown and "hbm_ceiling" in breakdown else ceiling(D)
     cpu = None if args.no_cpu_baseline else cpu_baseline(h["w"])
 
     achieved = h["bytes"] / h["kernel_ms"] / 1e6
@@ -652,7 +760,12 @@ def main():
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": stored_traffic(h["tile"]),
                      "algorithmic_bytes_per_launch": h["bytes"],
                      "kernel_us": round(h["kernel_ms"] * 1e3, 3),
-                     "kernel_us_event_pair_per_launch": round(h["pairs_ms"] * 1e3, 3)},
+                     "kernel_us_regions": [round(r * 1e3, 3) for r in h["regions_ms"]],
+                     "kernel_us_event_pair_per_launch": round(h["pairs_ms"] * 1e3, 3),
+                     "ceiling_gbs": ceil["rmw_in_place"]["gbs"],
+                     "ceiling_kernel": "in-place read-modify-write of the same 256 MiB of state traffic "
+                                       "(libkda_ceiling.so rmw_kernel), median of 3 regions",
+                     "frac_of_ceiling": round(achieved / ceil["rmw_in_place"]["gbs"], 4)},
         "cpu_baseline": cpu,
         "breakdown": breakdown,
     }

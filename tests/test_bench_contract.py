@@ -76,7 +76,12 @@ def test_traffic_only_for_the_counted_source_and_shape(monkeypatch):
 
 def test_cpu_baseline_leg_runs_the_oracle():
     w = synth.make(1, 4, 64, 64, num_slots=4, state_std=0.02, seed=3, name="tiny")
-    r = bench.cpu_baseline(w, budget_s=0.2, max_steps=3)
+    r = bench.cpu_baseline(w, seconds_scale=0.01)
     assert r["kind"] == "oracle" and r["unit"] == "steps/s"
-    assert r["cores"] >= 1 and r["value"] > 0
-    assert "steps" in r["sample"]
+    assert r["cores"] == len(os.sched_getaffinity(0)) and r["value"] > 0
+    assert r["cpu_count"] == os.cpu_count() and r["cpu_model"]
+    assert r["one_core_steps_per_s"] > 0 and r["b1_us_per_step_all_cores"] > 0 and r["b1_us_per_step_one_core"] > 0
+    for part in r["detail"].values():
+        assert len(part["samples_steps_per_s"]) == 3
+        assert part["steps_per_s"] == round(sorted(part["samples_steps_per_s"])[1], 3)
+    assert "steps" in r["sample"] and "median of 3" in r["sample"]
