@@ -6,6 +6,7 @@ torch-facing binding of that library.
 """
 
 from .kda import (  # noqa: F401
+    KDA_CHECK_SLOTS,
     KDA_DEVERR_ACCEPTED,
     KDA_DEVERR_CKPT,
     KDA_DEVERR_SEQLEN,

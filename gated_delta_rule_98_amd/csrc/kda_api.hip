@@ -167,9 +167,23 @@ int check_inputs(const uint16_t *q, const uint16_t *k, const uint16_t *v, const 
 // op acts on (the others it accepts and ignores).
 int read_flags(const kda_options *opts, int32_t used, Args &a) {
   const int32_t f = opts ? opts->flags : 0;
-  if (f & ~(int32_t)(KDA_RAW_INPUTS | KDA_OUT_BF16)) return KDA_ERR_INVALID;
+  if (f & ~(int32_t)(KDA_RAW_INPUTS | KDA_OUT_BF16 | KDA_CHECK_SLOTS)) return KDA_ERR_INVALID;
   a.raw = (f & used & KDA_RAW_INPUTS) ? 1 : 0;
   a.out_bf16 = (f & used & KDA_OUT_BF16) ? 1 : 0;
+  return KDA_OK;
+}
+
+// KDA_CHECK_SLOTS: read the slot table on the host (the caller has put it in
+// host-readable memory) and reject a batch in which two rows name the same
+// slot. Quadratic in B and allocation-free; padding rows (< 0) are exempt.
+int check_slots(const kda_options *opts, const int32_t *slot_ids, int32_t B) {
+  if (!opts || !(opts->flags & KDA_CHECK_SLOTS)) return KDA_OK;
+  for (int32_t i = 1; i < B; ++i) {
+    const int32_t s = slot_ids[i];
+    if (s < 0) continue;
+    for (int32_t j = 0; j < i; ++j)
+      if (slot_ids[j] == s) return KDA_ERR_INVALID;
+  }
   return KDA_OK;
 }
 
@@ -243,6 +257,7 @@ int kda_prefill_chunked(float *cache, int64_t num_slots, int64_t slot_stride, co
   if (opts && opts->tile_w != 0 && opts->tile_w != 16) return KDA_ERR_UNSUPPORTED;
   if (B == 0 || (n_tok == 0 && !ckpt_pos)) return KDA_OK;
   if (!slot_ids || !cu_seqlens) return KDA_ERR_INVALID;
+  KDA_TRY(check_slots(opts, slot_ids, B));
   KDA_TRY(check_cache(cache, num_slots, slot_stride, H, dk, dv));
   if (n_tok > 0) KDA_TRY(check_inputs(q, k, v, alpha, beta, out, true, f.out_bf16));
   if (ckpt_pos) {
@@ -301,6 +316,8 @@ int kda_prefill_chunked_noalloc(float *cache, int64_t num_slots, int64_t slot_st
   KDA_TRY(kda_prefill_chunked_workspace(B, n_tok, H, dk, dv, &need));
   if (B == 0 || (n_tok == 0 && !ckpt_pos)) return KDA_OK;
   if (need > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_TOO_LARGE;
+  if (!slot_ids || !cu_seqlens) return KDA_ERR_INVALID;
+  KDA_TRY(check_slots(opts, slot_ids, B));
   void *ws = nullptr;
   KDA_TRY(scratch_for_current_device(&ws));
   return kda_prefill_chunked(cache, num_slots, slot_stride, slot_ids, cu_seqlens, B, n_tok, H, dk, dv, q, k, v,
@@ -319,6 +336,7 @@ int kda_prefill(float *cache, int64_t num_slots, int64_t slot_stride, const int3
   if (!dims_supported(dk, dv)) return KDA_ERR_UNSUPPORTED;
   if (B == 0 || (n_tok == 0 && !ckpt_pos)) return KDA_OK;
   if (!slot_ids || !cu_seqlens) return KDA_ERR_INVALID;
+  KDA_TRY(check_slots(opts, slot_ids, B));
   KDA_TRY(check_cache(cache, num_slots, slot_stride, H, dk, dv));
   if (n_tok > 0) KDA_TRY(check_inputs(q, k, v, alpha, beta, out, true, a.out_bf16));
   if (ckpt_pos) {
@@ -367,6 +385,7 @@ int kda_decode_step(float *cache, int64_t num_slots, int64_t slot_stride, const 
   if (!dims_supported(dk, dv)) return KDA_ERR_UNSUPPORTED;
   if (B == 0) return KDA_OK;
   if (!slot_ids) return KDA_ERR_INVALID;
+  KDA_TRY(check_slots(opts, slot_ids, B));
   KDA_TRY(check_cache(cache, num_slots, slot_stride, H, dk, dv));
   KDA_TRY(check_inputs(q, k, v, alpha, beta, out, true, a.out_bf16));
   KDA_TRY(check_gate(epi));
@@ -413,6 +432,7 @@ int kda_verify_chunk(float *cache, int64_t num_slots, int64_t slot_stride, const
   if (!dims_supported(dk, dv) || T_max < 1 || T_max > kMaxT) return KDA_ERR_UNSUPPORTED;
   if (B == 0 || n_tok == 0) return KDA_OK;  // no tokens: nothing to read or write
   if (!slot_ids || !cu_seqlens) return KDA_ERR_INVALID;
+  KDA_TRY(check_slots(opts, slot_ids, B));
   KDA_TRY(check_cache(cache, num_slots, slot_stride, H, dk, dv));
   KDA_TRY(check_inputs(q, k, v, alpha, beta, out, true, a.out_bf16));
   KDA_TRY(check_gate(epi));
@@ -498,6 +518,7 @@ int kda_replay_commit(float *cache, int64_t num_slots, int64_t slot_stride, cons
   if (!dims_supported(dk, dv) || T_max < 1 || T_max > kMaxT) return KDA_ERR_UNSUPPORTED;
   if (B == 0) return KDA_OK;
   if (!slot_ids || !accepted_len) return KDA_ERR_INVALID;
+  KDA_TRY(check_slots(opts, slot_ids, B));
   KDA_TRY(check_cache(cache, num_slots, slot_stride, H, dk, dv));
   if (mode == KDA_REPLAY) KDA_TRY(check_replay_buf(rb));
   if (mode == KDA_PER_POSITION) {

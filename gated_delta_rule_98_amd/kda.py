@@ -47,6 +47,7 @@ KDA_DEVERR_CKPT = 8
 
 KDA_RAW_INPUTS = 1
 KDA_OUT_BF16 = 2
+KDA_CHECK_SLOTS = 4
 
 
 class KdaError(RuntimeError):

@@ -38,8 +38,8 @@
  * synchronizes: each call validates its arguments on the host, enqueues its
  * kernels on `stream` (a hipStream_t; NULL = the null stream) and returns.
  * Buffers must stay valid until the stream has passed the call. Calls are
- * reentrant. Within one call, slot ids must be distinct, and no output buffer
- * may overlap an input or another output.
+ * reentrant. Within one call, slot ids must be distinct (KDA_CHECK_SLOTS checks
+ * it on the host), and no output buffer may overlap an input or another output.
  *
  * Rows and slots. slot_ids[b] < 0 marks a padding row: its state is neither
  * read nor written and its output rows keep their contents (its inputs may
@@ -152,10 +152,18 @@ enum kda_verify_form { KDA_VERIFY_AUTO = 0, KDA_VERIFY_RECURRENT = 1, KDA_VERIFY
  *     kda_replay_commit in KDA_REPLAY mode must get the flag when the verify did.
  *   KDA_OUT_BF16: out is bf16 [rows][H][dv] (2-byte aligned), each output rounded
  *     to nearest even from the fp32 value the call computes otherwise.
+ *   KDA_CHECK_SLOTS: a debug check of the rule that slot ids are distinct within
+ *     one call. slot_ids must then be host-readable memory that the device can
+ *     also read (pinned host memory, hipHostMalloc): before anything is
+ *     enqueued the library reads it on the host and returns KDA_ERR_INVALID if
+ *     two rows name the same slot (padding rows, < 0, are exempt). The check
+ *     takes O(B^2) host time and allocates nothing. Any entry point that takes
+ *     kda_options accepts it.
  * kda_replay_commit ignores KDA_OUT_BF16 (it has no output) and, in
  * KDA_PER_POSITION mode, KDA_RAW_INPUTS. The chunk form of verify takes neither
- * (KDA_ERR_UNSUPPORTED). Other bits are KDA_ERR_INVALID. */
-enum kda_flag { KDA_RAW_INPUTS = 1, KDA_OUT_BF16 = 2 };
+ * KDA_RAW_INPUTS nor KDA_OUT_BF16 (KDA_ERR_UNSUPPORTED). Other bits are
+ * KDA_ERR_INVALID. */
+enum kda_flag { KDA_RAW_INPUTS = 1, KDA_OUT_BF16 = 2, KDA_CHECK_SLOTS = 4 };
 
 /* Launch options (host struct, may be NULL = all zero). */
 typedef struct kda_options {

@@ -183,7 +183,7 @@ def test_decode_host_checks():
     ok_gate = kda.kda_epilogue(A, None, 1e-6)
     assert _decode(epi=ctypes.byref(ok_gate), opts=ctypes.byref(kda.kda_options(64, 0))) == E.KDA_ERR_UNSUPPORTED
     # option flags: unknown bits are rejected; a bf16 output needs 2-byte alignment only
-    assert _decode(opts=ctypes.byref(kda.kda_options(0, 0, 4))) == E.KDA_ERR_INVALID
+    assert _decode(opts=ctypes.byref(kda.kda_options(0, 0, 8))) == E.KDA_ERR_INVALID
     assert _decode(out=A + 2) == E.KDA_ERR_ALIGN
     assert _decode(out=A + 1, opts=ctypes.byref(kda.kda_options(0, 0, E.KDA_OUT_BF16))) == E.KDA_ERR_ALIGN
     # passes every host check: only the launch itself fails without a device
@@ -255,7 +255,7 @@ def test_prefill_host_checks():
     assert _prefill(dk=96) == E.KDA_ERR_UNSUPPORTED
     assert _prefill(opts=ctypes.byref(kda.kda_options(64, 0))) == E.KDA_ERR_UNSUPPORTED
     assert _prefill(alpha=A + 4) == E.KDA_ERR_ALIGN
-    assert _prefill(opts=ctypes.byref(kda.kda_options(0, 0, 4))) == E.KDA_ERR_INVALID
+    assert _prefill(opts=ctypes.byref(kda.kda_options(0, 0, 8))) == E.KDA_ERR_INVALID
     assert _prefill(out=A + 2) == E.KDA_ERR_ALIGN
     assert _prefill(out=A + 2, opts=ctypes.byref(kda.kda_options(0, 0, E.KDA_OUT_BF16))) == E.KDA_ERR_HIP
 
@@ -287,7 +287,7 @@ def test_prefill_chunked_host_checks():
     assert _prefill_chunked(cu=None) == E.KDA_ERR_INVALID
     assert _prefill_chunked(dk=96) == E.KDA_ERR_UNSUPPORTED
     assert _prefill_chunked(opts=ctypes.byref(kda.kda_options(32, 0, 0))) == E.KDA_ERR_UNSUPPORTED
-    assert _prefill_chunked(opts=ctypes.byref(kda.kda_options(0, 0, 4))) == E.KDA_ERR_INVALID
+    assert _prefill_chunked(opts=ctypes.byref(kda.kda_options(0, 0, 8))) == E.KDA_ERR_INVALID
     assert _prefill_chunked(ckpt_pos=A, ckpt=None) == E.KDA_ERR_INVALID
     assert _prefill_chunked(out=A + 2) == E.KDA_ERR_ALIGN
     # passes every host check: only the launch fails without a device
@@ -319,6 +319,26 @@ def test_prefill_chunked_noalloc_host_checks():
     # within the limit every host check passes; without a device the scratch lookup fails
     assert _prefill_noalloc(B=1, H=32, slot_stride=32 * 128 * 128, n_tok=fits) == E.KDA_ERR_HIP
     assert fits >= 3600
+
+
+@needs_no_gpu
+def test_duplicate_slot_check():
+    """KDA_CHECK_SLOTS reads a host-readable slot table before anything is enqueued and
+    rejects two rows naming the same slot; padding rows may repeat. Without the flag the
+    table is never read on the host (a fake device address passes)."""
+    import numpy as np
+    E = kda
+    dup = np.array([3, 1, -1, 3], np.int32)
+    pad = np.array([3, -1, 1, -1], np.int32)
+    chk = ctypes.byref(kda.kda_options(0, 0, E.KDA_CHECK_SLOTS))
+    for call in (lambda **kw: _decode(**kw), lambda **kw: _verify(mode=1, draft=A, **kw),
+                 lambda **kw: _commit(mode=1, draft=A, **kw),
+                 lambda **kw: _prefill(**kw), lambda **kw: _prefill_chunked(**kw),
+                 lambda **kw: _prefill_noalloc(**kw)):
+        assert call(slot_ids=dup.ctypes.data, opts=chk) == E.KDA_ERR_INVALID
+        # distinct ids (padding repeated) pass the check; only the launch fails without a device
+        assert call(slot_ids=pad.ctypes.data, opts=chk) == E.KDA_ERR_HIP
+    assert _decode(opts=ctypes.byref(kda.kda_options(0, 0, 8))) == E.KDA_ERR_INVALID   # unknown flag bit
 
 
 def _pack(**over):
