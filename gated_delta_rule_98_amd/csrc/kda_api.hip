@@ -235,12 +235,24 @@ int64_t prefill_chunk_bound(int64_t B, int64_t n_tok) {
   return (n_tok + kChunkTokens - 1) / kChunkTokens + 2 * B;
 }
 
+// Workspace of the chunk form: the per-(chunk, head) data, then the chunk map
+// (int32 first chunk of each row [B + 1] and row of each chunk [chunks]),
+// rounded up to 16 bytes.
+size_t prefill_chunk_ws_data_bytes(int64_t B, int64_t n_tok, int H, int dk, int dv) {
+  return (size_t)prefill_chunk_bound(B, n_tok) * (size_t)H * prefill_chunk_ws_floats(dk, dv) * sizeof(float);
+}
+
+size_t prefill_chunk_ws_bytes(int64_t B, int64_t n_tok, int H, int dk, int dv) {
+  const size_t map = ((size_t)B + 1 + (size_t)prefill_chunk_bound(B, n_tok)) * sizeof(int32_t);
+  return (prefill_chunk_ws_data_bytes(B, n_tok, H, dk, dv) + map + 15) / 16 * 16;
+}
+
 extern "C" {
 
 int kda_prefill_chunked_workspace(int32_t B, int32_t n_tok, int32_t H, int32_t dk, int32_t dv, size_t *bytes) {
   if (!bytes || B < 0 || n_tok < 0 || H <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID;
   if (!dims_supported(dk, dv)) return KDA_ERR_UNSUPPORTED;
-  *bytes = (size_t)prefill_chunk_bound(B, n_tok) * (size_t)H * prefill_chunk_ws_floats(dk, dv) * sizeof(float);
+  *bytes = prefill_chunk_ws_bytes(B, n_tok, H, dk, dv);
   return KDA_OK;
 }
 
@@ -266,7 +278,7 @@ int kda_prefill_chunked(float *cache, int64_t num_slots, int64_t slot_stride, co
   }
   if (!aligned(cu_seqlens, 4) || (dev_err && !aligned(dev_err, 4))) return KDA_ERR_ALIGN;
   const int64_t chunks = prefill_chunk_bound(B, n_tok);
-  const size_t need = (size_t)chunks * (size_t)H * prefill_chunk_ws_floats(dk, dv) * sizeof(float);
+  const size_t need = prefill_chunk_ws_bytes(B, n_tok, H, dk, dv);
   if (!workspace || workspace_bytes < need) return KDA_ERR_INVALID;
   if (!aligned(workspace, 16)) return KDA_ERR_ALIGN;
   const int64_t prep_blocks = chunks * H, state_blocks = (int64_t)B * H * (dv / 16);
@@ -288,6 +300,9 @@ int kda_prefill_chunked(float *cache, int64_t num_slots, int64_t slot_stride, co
   a.out = static_cast<float *>(out);
   a.ckpt = ckpt;
   a.ws = static_cast<float *>(workspace);
+  a.cbase = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) +
+                                        prefill_chunk_ws_data_bytes(B, n_tok, H, dk, dv));
+  a.crow = a.cbase + B + 1;
   a.dev_err = dev_err;
   a.B = B;
   a.H = H;
@@ -297,6 +312,11 @@ int kda_prefill_chunked(float *cache, int64_t num_slots, int64_t slot_stride, co
   a.raw = f.raw;
   a.out_bf16 = f.out_bf16;
   void *args[] = {&a};
+  {
+    const hipError_t e = hipLaunchKernel(prefill_chunk_map_kernel(), dim3(1), dim3(kChunkMapThreads), args, 0,
+                                         (hipStream_t)stream);
+    if (e != hipSuccess) return KDA_ERR_HIP;
+  }
   if (n_tok > 0) {
     const hipError_t e = hipLaunchKernel(prefill_chunk_prep_kernel_for(dk, dv), dim3((unsigned)prep_blocks),
                                          dim3(kChunkPrepThreads), args, 0, (hipStream_t)stream);

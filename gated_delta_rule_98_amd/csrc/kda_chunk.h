@@ -23,13 +23,18 @@ struct ChunkArgs {
   float *out;  // fp32, or bf16 when out_bf16
   float *ckpt;
   float *ws;
+  int32_t *cbase;  // [B + 1] first chunk of each row (workspace tail; the map kernel writes it)
+  int32_t *crow;   // [ws_chunks] row of each chunk, -1 past the last (likewise)
   int32_t *dev_err;
   int32_t B, H, n_tok, ws_chunks, ntile, raw, out_bf16;
 };
 
 // Floats of workspace per (chunk, head).
 size_t prefill_chunk_ws_floats(int dk, int dv);
-// Kernel handles: the per-chunk precompute and the sequential pass over chunks.
+// Kernel handles: the chunk map, the per-chunk precompute and the sequential
+// pass over chunks.
+const void *prefill_chunk_map_kernel();
+constexpr int kChunkMapThreads = 1024;
 const void *prefill_chunk_prep_kernel_for(int dk, int dv);
 const void *prefill_chunk_state_kernel_for(int dk, int dv);
 

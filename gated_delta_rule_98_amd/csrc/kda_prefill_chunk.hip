@@ -83,6 +83,45 @@ __device__ __forceinline__ ChunkRow chunk_row(const ChunkArgs &a, int b) {
   return r;
 }
 
+// ----------------------------------------------------------------------------
+// Chunk map, one workgroup: the first chunk of every row (an exclusive prefix
+// sum of the rows' chunk counts) and the row of every chunk, so that each
+// precompute workgroup finds its row and each state-pass workgroup its first
+// chunk with one lookup. Chunks past the last row's map to -1.
+// ----------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kChunkMapThreads) void chunk_map_kernel(ChunkArgs a) {
+  __shared__ int32_t part[kChunkMapThreads];
+  __shared__ int32_t run;
+  const int tid = threadIdx.x;
+  if (tid == 0) run = 0;
+  __syncthreads();
+  for (int b0 = 0; b0 < a.B; b0 += kChunkMapThreads) {
+    const int b = b0 + tid;
+    const int n = b < a.B ? chunk_row(a, b).nch : 0;
+    part[tid] = n;
+    __syncthreads();
+    // inclusive scan of the tile (Hillis-Steele over LDS)
+    for (int d = 1; d < kChunkMapThreads; d <<= 1) {
+      const int add = tid >= d ? part[tid - d] : 0;
+      __syncthreads();
+      part[tid] += add;
+      __syncthreads();
+    }
+    const int first = run + part[tid] - n;
+    if (b < a.B) a.cbase[b] = first;
+    // fill the row's entries of the chunk -> row table
+    for (int j = 0; j < n; ++j)
+      if (first + j < a.ws_chunks) a.crow[first + j] = b;
+    __syncthreads();
+    if (tid == kChunkMapThreads - 1) run += part[tid];
+    __syncthreads();
+  }
+  const int total = run;
+  if (tid == 0) a.cbase[a.B] = total;
+  for (int c = total + tid; c < a.ws_chunks; c += kChunkMapThreads) a.crow[c] = -1;
+}
+
 // Token range [t0, t0 + n) of chunk j of a row.
 __device__ __forceinline__ void chunk_tokens(const ChunkRow &r, int j, int &t0, int &n) {
   if (j < r.n1) {
@@ -145,15 +184,11 @@ __global__ __launch_bounds__(kChunkPrepThreads) void prefill_chunk_prep_kernel(C
   __shared__ float gb[2 * DK];           // product of each sub-block's decays
 
   const int c = blockIdx.x / a.H, h = blockIdx.x % a.H;
-  // the row and chunk this workgroup prepares
-  int b = 0, jc = c;
-  ChunkRow r = {0, 0, 0, 0};
-  for (; b < a.B; ++b) {
-    r = chunk_row(a, b);
-    if (jc < r.nch) break;
-    jc -= r.nch;
-  }
-  if (b >= a.B) return;
+  // the row and chunk this workgroup prepares, from the chunk map
+  const int b = a.crow[c];
+  if (b < 0) return;
+  const int jc = c - a.cbase[b];
+  const ChunkRow r = chunk_row(a, b);
   int t0, n;
   chunk_tokens(r, jc, t0, n);
   const int64_t row0 = (int64_t)a.cu[b] + t0;
@@ -450,8 +485,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_state_kernel(ChunkArgs a) {
     return;
   }
   const ChunkRow r = chunk_row(a, u.b);
-  int cbase = 0;
-  for (int b = 0; b < u.b; ++b) cbase += chunk_row(a, b).nch;
+  const int cbase = a.cbase[u.b];
   if (cbase + r.nch > a.ws_chunks) {  // only with rows that overlap in cu_seqlens
     report(a.dev_err, u, KDA_DEVERR_SEQLEN);
     return;
@@ -578,6 +612,8 @@ size_t prefill_chunk_ws_floats(int dk, int dv) {
   if (dk == 64) return dv == 64 ? ChunkWs<64, 64>::FLOATS : ChunkWs<64, 128>::FLOATS;
   return dv == 64 ? ChunkWs<128, 64>::FLOATS : ChunkWs<128, 128>::FLOATS;
 }
+
+const void *prefill_chunk_map_kernel() { return (const void *)chunk_map_kernel; }
 
 const void *prefill_chunk_prep_kernel_for(int dk, int dv) {
   if (dk == 64) return dv == 64 ? (const void *)prefill_chunk_prep_kernel<64, 64> : (const void *)prefill_chunk_prep_kernel<64, 128>;

@@ -274,8 +274,10 @@ def test_prefill_chunked_host_checks():
     lib = kda.load_library()
     nbytes = ctypes.c_size_t(0)
     assert lib.kda_prefill_chunked_workspace(4, 90, 2, 128, 128, ctypes.byref(nbytes)) == E.KDA_OK
-    # (ceil(90 / 32) + 2 * 4) chunks x 2 heads x (3 * 32 * 128 + 32 * 128 + 32 * 32 + 128) floats
-    assert nbytes.value == 11 * 2 * (3 * 32 * 128 + 32 * 128 + 32 * 32 + 128) * 4
+    # (ceil(90 / 32) + 2 * 4) chunks x 2 heads x (3 * 32 * 128 + 32 * 128 + 32 * 32 + 128) floats,
+    # then the chunk map: int32 first chunk of each row (B + 1) and row of each chunk (11), to 16 B
+    data = 11 * 2 * (3 * 32 * 128 + 32 * 128 + 32 * 32 + 128) * 4
+    assert nbytes.value == (data + (4 + 1 + 11) * 4 + 15) // 16 * 16
     assert lib.kda_prefill_chunked_workspace(4, 90, 2, 96, 128, ctypes.byref(nbytes)) == E.KDA_ERR_UNSUPPORTED
     assert lib.kda_prefill_chunked_workspace(4, -1, 2, 128, 128, ctypes.byref(nbytes)) == E.KDA_ERR_INVALID
     assert lib.kda_prefill_chunked_workspace(4, 90, 2, 128, 128, None) == E.KDA_ERR_INVALID

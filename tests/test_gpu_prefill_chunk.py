@@ -85,6 +85,29 @@ def test_chunked_prefill_matches_oracle(dk, dv):
     _check(w, slots, pos, out, ckpt, cache_d)
 
 
+def test_chunked_prefill_b64_mixed_lengths():
+    """64 rows of mixed prompt lengths (empty, shorter than a chunk, many chunks) with padding
+    rows and checkpoints absent, at the start, inside a chunk, on a boundary and at the end:
+    every precompute workgroup finds its row through the chunk map. Against the oracle, and the
+    recurrent form to 1e-5."""
+    rng = np.random.Generator(np.random.PCG64(74))
+    seqlens = rng.choice([0, 1, 7, 31, 32, 33, 64, 95, 150, 260], 64).astype(int)
+    w = synth.make(64, 8, 128, 128, seqlens=seqlens, num_slots=80, state_std=0.05, seed=75)
+    slots = w.slot_ids.copy()
+    slots[[5, 40]] = -1
+    pos = np.array([rng.choice([-1, 0, n // 2, (n // 32) * 32, n]) if n else rng.choice([-1, 0])
+                    for n in seqlens], np.int32)
+    cache_c, cache_r = f32(w.cache), f32(w.cache)
+    log(f"chunked prefill B=64, {w.n_tok} tokens, 8 heads")
+    out_c, ckpt_c = _run(w, cache_c, slots=slots, pos=pos)
+    out_r, ckpt_r = _run(w, cache_r, slots=slots, pos=pos, chunked=False)
+    torch.cuda.synchronize()
+    live = np.concatenate([np.arange(w.cu_seqlens[b], w.cu_seqlens[b + 1]) for b in range(64) if slots[b] >= 0])
+    assert out_rel(out_c.cpu().numpy()[live], out_r.cpu().numpy()[live]) <= 1e-5
+    assert state_rel(cache_c.cpu().numpy(), cache_r.cpu().numpy()) <= 1e-5
+    _check(w, slots, pos, out_c, ckpt_c, cache_c)
+
+
 def test_chunked_prefill_without_checkpoints_and_against_recurrent_form():
     seqlens = [300, 31, 65]
     w = synth.make(3, 8, 128, 128, seqlens=seqlens, num_slots=4, state_std=0.05, seed=72)
