@@ -323,7 +323,7 @@ int kda_prefill_chunked(float *cache, int64_t num_slots, int64_t slot_stride, co
     if (e != hipSuccess) return KDA_ERR_HIP;
   }
   const hipError_t e = hipLaunchKernel(prefill_chunk_state_kernel_for(dk, dv), dim3((unsigned)state_blocks),
-                                       dim3(256), args, 0, (hipStream_t)stream);
+                                       dim3(kChunkStateThreads), args, 0, (hipStream_t)stream);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

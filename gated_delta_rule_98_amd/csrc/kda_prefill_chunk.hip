@@ -14,13 +14,15 @@
 // Diag(beta), gives delta = U - W S0 with W = T [Gamma k] and U = T V: every
 // product with the state becomes a dense matrix product.
 //
-// Two kernels. The precompute runs once per (chunk, head), all chunks in
-// parallel, and leaves W, U, [Gamma q], the keys decayed to the chunk end, B
-// and Gamma_L in a caller-provided workspace. The state pass runs per (row,
-// head, 16 value columns) through the row's chunks in order, with the state in
-// MFMA accumulator registers:
+// Three kernels. A one-workgroup map numbers the chunks of all rows. The
+// precompute runs once per (chunk, head), all chunks in parallel, and leaves
+// W, U, [Gamma q], the keys decayed to the chunk end, B and Gamma_L in a
+// caller-provided workspace, each in the order the state pass reads it. The
+// state pass runs per (row, head, 16 value columns) through the row's chunks
+// in order, with the state in MFMA accumulator registers:
 //   delta = U - W S0 ;  o = [Gamma q] S0 + B delta ;  S0 <- Diag(Gamma_L) S0 + Kt^T delta
-// all on v_mfma_f32_16x16x4f32.
+// all on v_mfma_f32_16x16x4f32; the products that feed the next chunk and the
+// output products run on separate waves of the workgroup.
 //
 // Decay products never divide. A chunk is two sub-blocks of 16 tokens. With
 // P_t the product over its own sub-block up to and including t, and R_s the
@@ -51,17 +53,24 @@ struct ChunkWs {
   static constexpr int QD = W + kCL * DK;   // [kCL][DK]  Gamma q
   static constexpr int KT = QD + kCL * DK;  // [kCL][DK]  k_s decayed to the chunk end
   static constexpr int U = KT + kCL * DK;   // [kCL][DV]  T v
-  static constexpr int BM = U + kCL * DV;   // [kCL][4][kCL / 4]  B
+  static constexpr int BM = U + kCL * DV;   // [kCL][kCL]  B
   static constexpr int GL = BM + kCL * kCL; // [DK]  Gamma_L
   static constexpr int FLOATS = GL + DK;
   static_assert(FLOATS % 4 == 0, "float4 alignment of every (chunk, head)");
 };
 
-// BM rows are stored as [4][kCL / 4]: element s of a row sits at
-// (s % 4) * (kCL / 4) + s / 4, so the lane that feeds MFMA steps 0..7 with
-// entries g, 4 + g, ... reads two float4s.
+// Every array but Gamma_L is stored in the order in which the state pass
+// reads it, so that each load instruction of a wave reads one contiguous
+// block (1 KB for float4 loads) instead of a piece of each of 16 rows. With
+// wave w of the state pass holding key channels [w DK/4, (w + 1) DK/4) and
+// lane (j, g) = (lane % 16, lane / 16):
+//   W, [Gamma q]  [rt][ct][w][lane][4]: token 16 rt + j, channels w DK/4 + 16 ct + 4 g .. + 3
+//   Kt            [ct][h][w][lane][4]:  key channel w DK/4 + 16 ct + j, tokens 4 (4 h + e) + g
+//   B             [h][rb][lane][4]:     row 16 rb + j, entries 4 (4 h + e) + g
+//   U             [tile][h][lane][4]:   value column 16 tile + j, tokens 4 (4 h + e) + g
+// (ct < DK / 64, h and rb < 2, e < 4 the float of the float4.)
 
-// Chunks of one row. nch = 0 for a row that does not run (padding, or any
+// Chunks of one row.// Chunks of one row. nch = 0 for a row that does not run (padding, or any
 // device error; the state pass reports those).
 struct ChunkRow {
   int nch, n1, s1, Tb;  // chunks, chunks before the checkpoint cut, the cut, tokens
@@ -110,9 +119,20 @@ __global__ __launch_bounds__(kChunkMapThreads) void chunk_map_kernel(ChunkArgs a
     }
     const int first = run + part[tid] - n;
     if (b < a.B) a.cbase[b] = first;
-    // fill the row's entries of the chunk -> row table
-    for (int j = 0; j < n; ++j)
-      if (first + j < a.ws_chunks) a.crow[first + j] = b;
+    // the chunk -> row table for this tile's rows: chunk run + c belongs to the
+    // first row whose inclusive sum exceeds c (a binary search in LDS)
+    const int tile_total = part[kChunkMapThreads - 1];
+    for (int c = tid; c < tile_total; c += kChunkMapThreads) {
+      int lo = 0, hi = kChunkMapThreads - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (part[mid] > c)
+          hi = mid;
+        else
+          lo = mid + 1;
+      }
+      if (run + c < a.ws_chunks) a.crow[run + c] = b0 + lo;
+    }
     __syncthreads();
     if (tid == kChunkMapThreads - 1) run += part[tid];
     __syncthreads();
@@ -183,7 +203,11 @@ __global__ __launch_bounds__(kChunkPrepThreads) void prefill_chunk_prep_kernel(C
   __shared__ float Bl[kCL * kCL];        // B, written out in one coalesced pass
   __shared__ float gb[2 * DK];           // product of each sub-block's decays
 
-  const int c = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  // Chunks are prepared last to first: the state pass starts at the first, and
+  // the workspace written last is the part most likely still held in the
+  // memory-side cache when it starts (measured on MI355X: 4% off the state pass
+  // of an 8000-token prompt).
+  const int c = (int)(gridDim.x / a.H) - 1 - (int)(blockIdx.x / a.H), h = blockIdx.x % a.H;
   // the row and chunk this workgroup prepares, from the chunk map
   const int b = a.crow[c];
   if (b < 0) return;
@@ -302,12 +326,32 @@ __global__ __launch_bounds__(kChunkPrepThreads) void prefill_chunk_prep_kernel(C
   }
   __syncthreads();
   // Gamma q = [P q] x (earlier sub-blocks), keys decayed to the chunk end = [R k] x
-  // (later sub-blocks), Gamma_L, to the workspace in coalesced rows
-  for (int idx = threadIdx.x; idx < kCL * DK; idx += blockDim.x) {
-    const int t = idx / DK, i = idx % DK;
-    const float qf = qb[t * PK + i], kt = ab[t * PK + i];
-    ws[WS::QD + idx] = t < kSB ? qf : qf * gb[i];
-    ws[WS::KT + idx] = t < kSB ? kt * gb[DK + i] : kt;
+  // (later sub-blocks), Gamma_L, to the workspace in its read order, one float4 per
+  // thread and step
+  constexpr int CPW = DK / 4, NCT = CPW / 16;
+  for (int d4 = threadIdx.x; d4 < kCL * DK / 4; d4 += blockDim.x) {
+    const int lane = d4 & 63, w = (d4 >> 6) & 3, r2 = d4 >> 8, j = lane & 15, g = lane >> 4;
+    {
+      const int ct = r2 % NCT, t = 16 * (r2 / NCT) + j, i0 = w * CPW + 16 * ct + 4 * g;
+      float4 qf = *reinterpret_cast<const float4 *>(qb + t * PK + i0);
+      if (t >= kSB) {
+        qf.x *= gb[i0];
+        qf.y *= gb[i0 + 1];
+        qf.z *= gb[i0 + 2];
+        qf.w *= gb[i0 + 3];
+      }
+      *reinterpret_cast<float4 *>(ws + WS::QD + 4 * d4) = qf;
+    }
+    {
+      const int h = r2 & 1, i = w * CPW + 16 * (r2 >> 1) + j;
+      float kv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = 4 * (4 * h + e) + g;
+        kv[e] = s < kSB ? ab[s * PK + i] * gb[DK + i] : ab[s * PK + i];
+      }
+      *reinterpret_cast<float4 *>(ws + WS::KT + 4 * d4) = make_float4(kv[0], kv[1], kv[2], kv[3]);
+    }
   }
   if ((int)threadIdx.x < DK) ws[WS::GL + threadIdx.x] = gb[threadIdx.x] * gb[DK + threadIdx.x];
 
@@ -339,10 +383,11 @@ __global__ __launch_bounds__(kChunkPrepThreads) void prefill_chunk_prep_kernel(C
     }
   }
   __syncthreads();
-  // B to the workspace in its row layout, zero above the diagonal
-  for (int idx = threadIdx.x; idx < kCL * kCL; idx += blockDim.x) {
-    const int t = idx / kCL, pc = idx % kCL, s = (pc % (kCL / 4)) * 4 + pc / (kCL / 4);
-    ws[WS::BM + idx] = s > t ? 0.0f : Bl[t * kCL + s];
+  // B to the workspace in its read order, zero above the diagonal
+  for (int d = threadIdx.x; d < kCL * kCL; d += blockDim.x) {
+    const int e = d & 3, lane = (d >> 2) & 63, rb = (d >> 8) & 1, h = d >> 9;
+    const int t = 16 * rb + (lane & 15), s = 4 * (4 * h + e) + (lane >> 4);
+    ws[WS::BM + d] = s > t ? 0.0f : Bl[t * kCL + s];
   }
 
   // X = (I + Diag(beta) A)^-1 by 16 x 16 blocks: the two diagonal blocks by forward
@@ -402,8 +447,9 @@ __global__ __launch_bounds__(kChunkPrepThreads) void prefill_chunk_prep_kernel(C
     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ks = 0; ks < kCL / 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[ks], bv[ks], acc, 0, 0, 0);
+    // W to the rows of [P q], free since the products across sub-blocks
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ws[WS::W + (16 * rt + 4 * g + e) * DK + 16 * ct + m] = acc[e];
+    for (int e = 0; e < 4; ++e) qb[(16 * rt + 4 * g + e) * PK + 16 * ct + m] = acc[e];
   }
   for (int tile = wave; tile < 2 * TU; tile += NWAVES) {
     const int rt = tile & 1, ct = tile >> 1;
@@ -418,7 +464,13 @@ __global__ __launch_bounds__(kChunkPrepThreads) void prefill_chunk_prep_kernel(C
 #pragma unroll
     for (int ks = 0; ks < kCL / 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[ks], bv[ks], acc, 0, 0, 0);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ws[WS::U + (16 * rt + 4 * g + e) * DV + 16 * ct + m] = acc[e];
+    for (int e = 0; e < 4; ++e) ws[WS::U + ct * (kCL * 16) + (rt * 64 + e * 16 + m) * 4 + g] = acc[e];
+  }
+  __syncthreads();
+  for (int d4 = threadIdx.x; d4 < kCL * DK / 4; d4 += blockDim.x) {
+    const int lane = d4 & 63, w = (d4 >> 6) & 3, r2 = d4 >> 8;
+    const int t = 16 * (r2 / NCT) + (lane & 15), i0 = w * CPW + 16 * (r2 % NCT) + 4 * (lane >> 4);
+    *reinterpret_cast<float4 *>(ws + WS::W + 4 * d4) = *reinterpret_cast<const float4 *>(qb + t * PK + i0);
   }
 }
 
@@ -443,29 +495,37 @@ __device__ __forceinline__ const float *chunk_ws(const ChunkArgs &a, int c, int 
   return a.ws + ((int64_t)c * a.H + h) * WS::FLOATS;
 }
 
-// A operands of W S0 and [Gamma q] S0 for one chunk: lane (j, g) supplies token
-// 16 rt + j at channels coff + 16 ct .. + 3.
-template <class WS, int DK, int NCT>
-__device__ __forceinline__ void load_wq(const float *w, int j, int coff, float4 (&wv)[2][NCT],
-                                        float4 (&qv)[2][NCT]) {
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const int off = (16 * rt + j) * DK + coff + 16 * ct;
-      wv[rt][ct] = *reinterpret_cast<const float4 *>(w + WS::W + off);
-      qv[rt][ct] = *reinterpret_cast<const float4 *>(w + WS::QD + off);
-    }
+template <class WS>
+__device__ __forceinline__ float4 ws4(const float *w, int off) {
+  return *reinterpret_cast<const float4 *>(w + off);
 }
 
+// One workgroup per (row, head, 16 value columns), eight waves in two roles.
+// Wave q < 4 carries the recurrence over key channels [q DK/4, (q + 1) DK/4):
+//   W S0 over its channels -> (barrier) -> delta = U - sum of the four partials
+//   -> S0 <- Diag(Gamma_L) S0 + Kt^T delta
+// holding the state in the accumulator layout (lane (j, g) has channels
+// q DK/4 + 16 ct + 4 g .. + 3 of column j). Side wave 4 + q computes [Gamma q] S0
+// over the same channels from a copy of S0 in LDS, and side waves 5 and 6 finish
+// each chunk's outputs, o = [Gamma q] S0 + B delta, one barrier later. A
+// recurrence wave and its side wave share a SIMD: the recurrence waves run at
+// the higher priority, and the side waves' products fill the matrix unit while
+// they wait at the barrier or on LDS. One barrier per chunk; every LDS array is
+// double-buffered by chunk parity, and a buffer is written again only after
+// the barrier that follows its last read.
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void prefill_chunk_state_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(kChunkStateThreads) void prefill_chunk_state_kernel(ChunkArgs a) {
   using WS = ChunkWs<DK, DV>;
   constexpr int CPW = DK / 4;    // key channels per wave
   constexpr int NCT = CPW / 16;  // 16-channel tiles per wave
-  __shared__ float part[4][2][kCL][16];  // per wave: W S0 and [Gamma q] S0 over its channels
-  __shared__ float dl[kCL][16];          // delta
-  __shared__ float o0[kCL][16];          // [Gamma q] S0
+  static_assert(kChunkStateThreads == 512, "four recurrence waves and four side waves");
+  // W S0 partials in the reading lanes' layout: [parity][wave][row block][lane][c]
+  // holds token 4 (4 rb + c) + g, column j of lane (j, g), so that each lane reads
+  // the partials it needs as float4s.
+  __shared__ float4 pdp[2][4][2][64];
+  __shared__ v4f pop[2][4][2][64];        // [Gamma q] S0 partials, accumulator layout
+  __shared__ float4 sx[2][4][NCT][64];    // S0 for the side waves: [parity][wave][ct][lane]
+  __shared__ float4 dlt[2][2][64];        // delta, B-operand layout: [parity][h][lane] holds ks = 4 h + c
 
   const Unit u = unit_of_block_rows(a.ntile, a.H, a.B);
   const int32_t slot = a.slot_ids[u.b];
@@ -492,118 +552,193 @@ __global__ __launch_bounds__(256) void prefill_chunk_state_kernel(ChunkArgs a) {
   }
   if (r.nch == 0 && ck != 0) return;
 
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), q = wave & 3;
   const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
   const int n0 = 16 * u.tile;
-  const int coff = CPW * wave + 4 * g;  // first channel of this lane in tile 0
-  float *S = a.cache + (int64_t)slot * a.slot_stride + ((int64_t)u.h * DV + n0 + j) * DK + coff;
-  float *CK = ck >= 0 ? a.ckpt + (((int64_t)u.b * a.H + u.h) * DV + n0 + j) * DK + coff : nullptr;
-  float4 s[NCT];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) s[ct] = ld4<kVerifyLoadStream>(S + 16 * ct);
-  if (ck == 0) {
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) st4<kVerifyStoreStream>(CK + 16 * ct, s[ct]);
-  }
+  const int coff = CPW * q + 4 * g;  // first channel of this lane in tile 0
+  const int last = r.nch - 1;
 
-  // W and [Gamma q] of the next chunk are read while this one computes; the other
-  // operands of a chunk are issued before its first product. Past the last chunk the
-  // last one is read again, so every load is unconditional and each wait knows how
-  // many loads follow the ones it needs.
-  float4 wv[2][NCT], qv[2][NCT];
-  if (r.nch > 0) load_wq<WS, DK, NCT>(chunk_ws<WS>(a, cbase, u.h), j, coff, wv, qv);
-  for (int jc = 0; jc < r.nch; ++jc) {
-    int t0, n;
-    chunk_tokens(r, jc, t0, n);
-    const float *w = chunk_ws<WS>(a, cbase + jc, u.h);
-    float uu[kCL * 16 / 256];
+  if (wave < 4) {
+    // ---- recurrence waves ----
+    __builtin_amdgcn_s_setprio(2);
+    float *S = a.cache + (int64_t)slot * a.slot_stride + ((int64_t)u.h * DV + n0 + j) * DK + coff;
+    float *CK = ck >= 0 ? a.ckpt + (((int64_t)u.b * a.H + u.h) * DV + n0 + j) * DK + coff : nullptr;
+    float4 s[NCT];
 #pragma unroll
-    for (int k = 0; k < kCL * 16 / 256; ++k) {
-      const int idx = threadIdx.x + 256 * k;
-      uu[k] = w[WS::U + (idx >> 4) * DV + n0 + (idx & 15)];
-    }
-    const float *brow = w + WS::BM + (16 * (wave & 1) + j) * kCL + g * (kCL / 4);
-    const float4 b0 = *reinterpret_cast<const float4 *>(brow);
-    const float4 b1 = *reinterpret_cast<const float4 *>(brow + 4);
-    float kt[NCT][8];
-    float4 gl[NCT];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      gl[ct] = *reinterpret_cast<const float4 *>(w + WS::GL + coff + 16 * ct);
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) kt[ct][ks] = w[WS::KT + (4 * ks + g) * DK + CPW * wave + 16 * ct + j];
-    }
-
-    // W S0 and [Gamma q] S0 over this wave's channels
-    v4f pd[2], po[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      pd[rt] = {0.0f, 0.0f, 0.0f, 0.0f};
-      po[rt] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[rt][ct].x, s[ct].x, pd[rt], 0, 0, 0);
-        po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[rt][ct].x, s[ct].x, po[rt], 0, 0, 0);
-        pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[rt][ct].y, s[ct].y, pd[rt], 0, 0, 0);
-        po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[rt][ct].y, s[ct].y, po[rt], 0, 0, 0);
-        pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[rt][ct].z, s[ct].z, pd[rt], 0, 0, 0);
-        po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[rt][ct].z, s[ct].z, po[rt], 0, 0, 0);
-        pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[rt][ct].w, s[ct].w, pd[rt], 0, 0, 0);
-        po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[rt][ct].w, s[ct].w, po[rt], 0, 0, 0);
-      }
-    }
-    load_wq<WS, DK, NCT>(chunk_ws<WS>(a, cbase + min(jc + 1, r.nch - 1), u.h), j, coff, wv, qv);
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        part[wave][0][16 * rt + 4 * g + e][j] = pd[rt][e];
-        part[wave][1][16 * rt + 4 * g + e][j] = po[rt][e];
-      }
-    __syncthreads();
-
-    // delta = U - W S0, and [Gamma q] S0, summed over the waves in a fixed order
-#pragma unroll
-    for (int k = 0; k < kCL * 16 / 256; ++k) {
-      const int idx = threadIdx.x + 256 * k, t = idx >> 4, col = idx & 15;
-      const float sd = ((part[0][0][t][col] + part[1][0][t][col]) + part[2][0][t][col]) + part[3][0][t][col];
-      const float so = ((part[0][1][t][col] + part[1][1][t][col]) + part[2][1][t][col]) + part[3][1][t][col];
-      dl[t][col] = uu[k] - sd;
-      o0[t][col] = so;
-    }
-    __syncthreads();
-
-    // o = [Gamma q] S0 + B delta: waves 0 and 1, 16 tokens each
-    if (wave < 2) {
-      const int rt = wave;
-      v4f acc = {o0[16 * rt + 4 * g][j], o0[16 * rt + 4 * g + 1][j], o0[16 * rt + 4 * g + 2][j],
-                 o0[16 * rt + 4 * g + 3][j]};
-      const float bm[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bm[ks], dl[4 * ks + g][j], acc, 0, 0, 0);
-      const int64_t obase = ((int64_t)c0 + t0) * a.H + u.h;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int tok = 16 * rt + 4 * g + e;
-        if (tok < n) put_chunk_out(a, (obase + (int64_t)tok * a.H) * DV + n0 + j, acc[e]);
-      }
-    }
-
-    // S0 <- Diag(Gamma_L) S0 + Kt^T delta over this wave's channels
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      v4f acc = {s[ct].x * gl[ct].x, s[ct].y * gl[ct].y, s[ct].z * gl[ct].z, s[ct].w * gl[ct].w};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[ct][ks], dl[4 * ks + g][j], acc, 0, 0, 0);
-      s[ct] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    }
-    if (ck > 0 && t0 + n == ck) {
+    for (int ct = 0; ct < NCT; ++ct) s[ct] = ld4<kVerifyLoadStream>(S + 16 * ct);
+    if (ck == 0) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) st4<kVerifyStoreStream>(CK + 16 * ct, s[ct]);
     }
-  }
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) st4<kVerifyStoreStream>(S + 16 * ct, s[ct]);
+    for (int ct = 0; ct < NCT; ++ct) sx[0][q][ct][lane] = s[ct];
+    // The operands of the next chunk are read while this one computes, in two
+    // batches that each follow a burst of products (a load issue that waits for
+    // queue space then holds up no product): W and Kt behind W S0, Gamma_L and U
+    // behind the update. Two operand sets alternate (the loop body is unrolled
+    // twice), so no register copy waits for a load early. Past the last chunk the
+    // last one is read again, so every load is unconditional.
+    struct Ops {
+      float4 wv[2][NCT], kt[NCT][2], gl[NCT], uv[2];
+    };
+    auto load_wk = [&](Ops &o, const float *w) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) o.wv[rt][ct] = ws4<WS>(w, WS::W + (((rt * NCT + ct) * 4 + q) * 64 + lane) * 4);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) o.kt[ct][h] = ws4<WS>(w, WS::KT + (((ct * 2 + h) * 4 + q) * 64 + lane) * 4);
+    };
+    auto load_gu = [&](Ops &o, const float *w) {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) o.gl[ct] = ws4<WS>(w, WS::GL + coff + 16 * ct);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) o.uv[h] = ws4<WS>(w, WS::U + u.tile * (kCL * 16) + (h * 64 + lane) * 4);
+    };
+    auto step = [&](int jc, const Ops &cur, Ops &nxt) {
+      const int p = jc & 1;
+      // W S0 over this wave's channels
+      v4f pd[2];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        pd[rt] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.wv[rt][ct].x, s[ct].x, pd[rt], 0, 0, 0);
+          pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.wv[rt][ct].y, s[ct].y, pd[rt], 0, 0, 0);
+          pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.wv[rt][ct].z, s[ct].z, pd[rt], 0, 0, 0);
+          pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.wv[rt][ct].w, s[ct].w, pd[rt], 0, 0, 0);
+        }
+      }
+      const float *wn = chunk_ws<WS>(a, cbase + min(jc + 1, last), u.h);
+      load_wk(nxt, wn);
+      // this lane's accumulator element e (token 16 rt + 4 g + e, column j) is element
+      // g of lane (j, e)'s float4
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) reinterpret_cast<float *>(&pdp[p][q][rt][e * 16 + j])[g] = pd[rt][e];
+      __syncthreads();
+
+      // delta = U - W S0 at this lane's B-operand positions (token 4 ks + g, column
+      // j), the partials summed over the waves in a fixed order
+      float4 pv[4][2];
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) pv[w4][h] = pdp[p][w4][h][lane];
+      float dv[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        dv[4 * h] = cur.uv[h].x - (((pv[0][h].x + pv[1][h].x) + pv[2][h].x) + pv[3][h].x);
+        dv[4 * h + 1] = cur.uv[h].y - (((pv[0][h].y + pv[1][h].y) + pv[2][h].y) + pv[3][h].y);
+        dv[4 * h + 2] = cur.uv[h].z - (((pv[0][h].z + pv[1][h].z) + pv[2][h].z) + pv[3][h].z);
+        dv[4 * h + 3] = cur.uv[h].w - (((pv[0][h].w + pv[1][h].w) + pv[2][h].w) + pv[3][h].w);
+      }
+      if (wave == 0) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) dlt[p][h][lane] = make_float4(dv[4 * h], dv[4 * h + 1], dv[4 * h + 2], dv[4 * h + 3]);
+      }
+
+      // S0 <- Diag(Gamma_L) S0 + Kt^T delta over this wave's channels
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        v4f acc = {s[ct].x * cur.gl[ct].x, s[ct].y * cur.gl[ct].y, s[ct].z * cur.gl[ct].z, s[ct].w * cur.gl[ct].w};
+        const float kt[8] = {cur.kt[ct][0].x, cur.kt[ct][0].y, cur.kt[ct][0].z, cur.kt[ct][0].w,
+                             cur.kt[ct][1].x, cur.kt[ct][1].y, cur.kt[ct][1].z, cur.kt[ct][1].w};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[ks], dv[ks], acc, 0, 0, 0);
+        s[ct] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      }
+      load_gu(nxt, wn);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) sx[p ^ 1][q][ct][lane] = s[ct];
+      int t0, n;
+      chunk_tokens(r, jc, t0, n);
+      if (ck > 0 && t0 + n == ck) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) st4<kVerifyStoreStream>(CK + 16 * ct, s[ct]);
+      }
+    };
+    Ops o0, o1;
+    if (r.nch > 0) {
+      load_wk(o0, chunk_ws<WS>(a, cbase, u.h));
+      load_gu(o0, chunk_ws<WS>(a, cbase, u.h));
+    }
+    for (int jc = 0; jc < r.nch; jc += 2) {
+      step(jc, o0, o1);
+      if (jc + 1 < r.nch) step(jc + 1, o1, o0);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) st4<kVerifyStoreStream>(S + 16 * ct, s[ct]);
+    return;
+  }
+
+  // ---- side waves ----
+  // Wave 5 finishes row block 1 (tokens 16..31, B over all 32 deltas) and wave 6
+  // row block 0 (tokens 0..15, whose B has no entries past token 15).
+  const int rb = wave == 6 ? 0 : 1;
+  const bool outw = wave == 5 || wave == 6;
+  float4 qv[2][NCT], bq[2], bprev[2];
+  auto load_q = [&](const float *w) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) qv[rt][ct] = ws4<WS>(w, WS::QD + (((rt * NCT + ct) * 4 + q) * 64 + lane) * 4);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) bq[h] = ws4<WS>(w, WS::BM + ((h * 2 + rb) * 64 + lane) * 4);
+  };
+  // the outputs of chunk jc, after the barrier that follows its side products
+  auto finish = [&](int jc) {
+    const int p = jc & 1;
+    v4f acc = ((pop[p][0][rb][lane] + pop[p][1][rb][lane]) + pop[p][2][rb][lane]) + pop[p][3][rb][lane];
+    const float bm[8] = {bprev[0].x, bprev[0].y, bprev[0].z, bprev[0].w,
+                         bprev[1].x, bprev[1].y, bprev[1].z, bprev[1].w};
+    const float4 d0 = dlt[p][0][lane], d1 = rb == 1 ? dlt[p][1][lane] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    const float dd[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      if (rb == 1 || ks < 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bm[ks], dd[ks], acc, 0, 0, 0);
+    int t0, n;
+    chunk_tokens(r, jc, t0, n);
+    const int64_t obase = ((int64_t)c0 + t0) * a.H + u.h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int tok = 16 * rb + 4 * g + e;
+      if (tok < n) put_chunk_out(a, (obase + (int64_t)tok * a.H) * DV + n0 + j, acc[e]);
+    }
+  };
+  if (r.nch > 0) load_q(chunk_ws<WS>(a, cbase, u.h));
+  for (int jc = 0; jc < r.nch; ++jc) {
+    const int p = jc & 1;
+    __syncthreads();
+    if (outw && jc > 0) finish(jc - 1);
+    float4 sq[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) sq[ct] = sx[p][q][ct][lane];
+    v4f po[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      po[rt] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[rt][ct].x, sq[ct].x, po[rt], 0, 0, 0);
+        po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[rt][ct].y, sq[ct].y, po[rt], 0, 0, 0);
+        po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[rt][ct].z, sq[ct].z, po[rt], 0, 0, 0);
+        po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[rt][ct].w, sq[ct].w, po[rt], 0, 0, 0);
+      }
+    }
+    bprev[0] = bq[0];
+    bprev[1] = bq[1];
+    load_q(chunk_ws<WS>(a, cbase + min(jc + 1, last), u.h));
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) pop[p][q][rt][lane] = po[rt];
+  }
+  __syncthreads();
+  if (outw && r.nch > 0) finish(last);
 }
 
 }  // namespace
