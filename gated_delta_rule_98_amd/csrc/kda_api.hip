@@ -53,10 +53,17 @@ bool dims_supported(int dk, int dv) { return (dk == 64 || dk == 128) && (dv == 6
 //    at exactly 512 heads of 128 columns, 128-column tiles (two per CU);
 //  * verify (T tokens per row, VALU-heavy): 32 columns while that gives at
 //    least 256 workgroups, 16 below that, then 8;
-//  * replay commit: 32 columns from 2048 workgroups up, 16 columns down to 256
-//    workgroups, then 8;
+//  * replay commit (accepted lengths uniform in 1..T): 32 columns at 512 to 767
+//    heads (B = 16, T = 8: 12.6 us against 13.9 us for 16 columns), 16 columns
+//    from 768 heads (B = 64, T = 8: 47.9 us against 49.4 us for 32) and below
+//    512 heads while that gives 256 workgroups, then 8; a batch whose tokens
+//    fill under 3/4 of B x T_max (rows mostly short or empty, as a mixed batch
+//    whose single-token rows were committed in place) takes one workgroup per
+//    head: fewer workgroups that only find nothing to do (the 64-row mixed
+//    batch: 17.4 us against 19.7 us for 32 columns);
 //  * per-position copy commit: 16 columns.
-int choose_width(Kind kind, int64_t rows, int H, int dk, int dv, bool gate, int requested, Launch *l) {
+int choose_width(Kind kind, int64_t rows, int H, int dk, int dv, bool gate, int requested, Launch *l,
+                 bool sparse_rows = false) {
   if (gate) {
     // the gate's RMS norm spans the whole head: one workgroup owns all dv columns,
     // with two slabs per lane (1024 threads at dv = 128) to keep registers low
@@ -103,9 +110,13 @@ int choose_width(Kind kind, int64_t rows, int H, int dk, int dv, bool gate, int 
       break;
     case KIND_COMMIT_REPLAY:
       W = 8;
-      if (32 <= dv && heads * (dv / 32) >= 2048)
+      if (sparse_rows)
+        W = dv;
+      else if (heads >= 768)
+        W = 16;
+      else if (heads * (dv / 32) >= 2048)
         W = 32;
-      else if (16 <= dv && heads * (dv / 16) >= 256)
+      else if (heads * (dv / 16) >= 256)
         W = 16;
       break;
     case KIND_COMMIT_COPY:
@@ -549,8 +560,10 @@ int kda_replay_commit(float *cache, int64_t num_slots, int64_t slot_stride, cons
       (dev_err && !aligned(dev_err, 4)))
     return KDA_ERR_ALIGN;
   Launch l;
+  // rows mostly short or empty: the packed tokens fill under 3/4 of B x T_max
+  const bool sparse_rows = cu_seqlens && 4 * (int64_t)n_tok < 3 * (int64_t)B * T_max;
   KDA_TRY(choose_width(mode == KDA_REPLAY ? KIND_COMMIT_REPLAY : KIND_COMMIT_COPY, B, H, dk, dv, false,
-                       opts ? opts->tile_w : 0, &l));
+                       opts ? opts->tile_w : 0, &l, sparse_rows));
 
   a.cache = cache;
   a.num_slots = num_slots;

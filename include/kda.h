@@ -345,7 +345,10 @@ int kda_state_unpack(float *cache, int64_t num_slots, int64_t slot_stride,
  * in vLLM", section "Finding time between operators"). For KDA_OP_VERIFY it is
  * the shape of the recurrent form; where the automatic choice takes the chunk
  * form instead (see kda_verify_form), that kernel runs dv columns and 4 * dv
- * threads per workgroup. Returns KDA_ERR_UNSUPPORTED for shapes the library
+ * threads per workgroup. For KDA_OP_COMMIT_REPLAY it assumes full rows:
+ * kda_replay_commit with cu_seqlens whose n_tok is under 3/4 of B * T_max
+ * (rows mostly short or empty) runs one workgroup of dv columns per head
+ * instead. Returns KDA_ERR_UNSUPPORTED for shapes the library
  * does not run, KDA_ERR_INVALID for an unknown op or non-positive sizes.
  */
 int kda_query_variant(int32_t op, int32_t B, int32_t H, int32_t dk, int32_t dv, int32_t T_max,

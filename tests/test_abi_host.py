@@ -74,6 +74,8 @@ def test_query_variant_launch_shapes():
     # verify / replay commit: 32 columns while >= 512 workgroups
     assert q(16, 32, 128, 128, T_max=8, op=V) == (32, 256)
     assert q(16, 32, 128, 128, T_max=8, op=CR) == (32, 256)
+    assert q(24, 32, 128, 128, T_max=8, op=CR) == (16, 256)   # from 768 heads: 16 columns
+    assert q(64, 32, 128, 128, T_max=8, op=CR) == (16, 256)
     assert q(2, 32, 128, 128, T_max=8, op=V) == (32, 256)
     assert q(1, 32, 128, 128, T_max=8, op=V) == (16, 256)
     assert q(8, 32, 128, 128, T_max=8, op=CR) == (16, 256)
