@@ -572,6 +572,26 @@ def ceiling(D, reps=200):
         ms = float(np.median([timed_region(D, fn, reps) / reps for _ in range(3)]))
         res[name] = dict(us=round(ms * 1e3, 3), bytes=moved, gbs=round(moved / ms / 1e6, 1))
         log(f"ceiling {name}: {ms * 1e3:.2f} us for {moved} B ({moved / ms / 1e6:.0f} GB/s)")
+    # the same read-modify-write at the state sizes of the smaller configurations, timed like
+    # them (HIP-graph replays): the B=16 step's 32 MiB and the 48 MiB the mixed batch commits
+    # (24 rows x 32 heads); a single round of workgroups reads, then writes, so the
+    # attainable rate falls with the size
+    for mib in (32, 48):
+        sub = (mib << 20) // 4
+        nreg = 4 * region // sub
+
+        def rmw_sub(i, sub=sub, nreg=nreg):
+            # the stream current at the call: a graph capture runs on its own stream
+            cur = torch.cuda.current_stream().cuda_stream
+            assert lib.kda_ceiling_rmw(base + (i % nreg) * sub * 4, sub, cur) == 0
+
+        for i in range(20):
+            rmw_sub(i)
+        ms = graph_ms(D, rmw_sub, reps)
+        res[f"rmw_in_place_{mib}mib"] = dict(us=round(ms * 1e3, 3), bytes=2 * sub * 4,
+                                             gbs=round(2 * sub * 4 / ms / 1e6, 1))
+        log(f"ceiling rmw_in_place_{mib}mib: {ms * 1e3:.2f} us for {2 * sub * 4} B "
+            f"({2 * sub * 4 / ms / 1e6:.0f} GB/s)")
     del buf
     return res
 
@@ -675,6 +695,18 @@ def stored_traffic(tile):
         return None
 
 
+def size_ceiling_fracs(breakdown):
+    """The B=16 replay commit and the mixed batch's commit against the in-place
+    read-modify-write ceiling measured at their own state sizes."""
+    c = breakdown.get("hbm_ceiling") or {}
+    sv = (breakdown.get("spec_verify_b16_t8") or {}).get("replay")
+    if sv and "rmw_in_place_32mib" in c:
+        sv["commit_frac_of_size_ceiling"] = round(sv["commit_gbs"] / c["rmw_in_place_32mib"]["gbs"], 4)
+    mx = breakdown.get("mixed_b64_gated")
+    if mx and "rmw_in_place_48mib" in c:
+        mx["commit_frac_of_size_ceiling"] = round(mx["commit_gbs"] / c["rmw_in_place_48mib"]["gbs"], 4)
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -733,6 +765,7 @@ def main():
             sys.exit(2)
         breakdown = {name: fn() for name, fn in parts.items() if not only or any(name.startswith(p) for p in only)}
         breakdown["headline_same_table_kernel_us"] = round(h["hot_ms"] * 1e3, 3)
+        size_ceiling_fracs(breakdown)
     if args.copy_calibration:
         copy_calibration(D)
     ceil = breakdown["hbm_ceiling"] if breakdown and "hbm_ceiling" in breakdown else ceiling(D)
