@@ -675,9 +675,11 @@ def cpu_baseline(w, seconds_scale=1.0):
 
 # ----------------------------------------------------------------------------- counters
 
-def stored_traffic(tile):
+def stored_traffic(tile, key="hbm_bytes_per_launch"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
-    the current decode kernel source and the same launch shape."""
+    the current decode kernel source and the same launch shape: FETCH_SIZE + WRITE_SIZE scaled
+    by a plain copy's counts (hbm_bytes_per_launch), or the TCC_EA0 read and write request
+    counts times their sizes (request_bytes_per_launch)."""
     if not os.path.exists(COUNTERS_FILE):
         return None
     fields = {}
@@ -690,7 +692,7 @@ def stored_traffic(tile):
     if fields.get("launch") != f"tile_w {tile[0]}, threads {tile[1]}":
         return None
     try:
-        return int(float(fields["hbm_bytes_per_launch"]))
+        return int(float(fields[key]))
     except (KeyError, ValueError):
         return None
 
@@ -718,6 +720,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--no-breakdown", action="store_true", help="headline only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the ceiling probe (ceiling fields null), for short profiling runs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain device copies of 256 MiB (copy_kernel, for counter scaling)")
     ap.add_argument("--only", default="",
@@ -768,7 +772,10 @@ def main():
         size_ceiling_fracs(breakdown)
     if args.copy_calibration:
         copy_calibration(D)
-    ceil = breakdown["hbm_ceiling"] if breakdown and "hbm_ceiling" in breakdown else ceiling(D)
+    if breakdown and "hbm_ceiling" in breakdown:
+        ceil = breakdown["hbm_ceiling"]
+    else:
+        ceil = None if args.no_ceiling else ceiling(D)
     cpu = None if args.no_cpu_baseline else cpu_baseline(h["w"])
 
     achieved = h["bytes"] / h["kernel_ms"] / 1e6
@@ -791,14 +798,15 @@ def main():
                    "threads": h["tile"][1], "tokens_per_s": round(64 * 1e3 / h["ms_step"], 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": stored_traffic(h["tile"]),
+                     "traffic_from_requests": stored_traffic(h["tile"], "request_bytes_per_launch"),
                      "algorithmic_bytes_per_launch": h["bytes"],
                      "kernel_us": round(h["kernel_ms"] * 1e3, 3),
                      "kernel_us_regions": [round(r * 1e3, 3) for r in h["regions_ms"]],
                      "kernel_us_event_pair_per_launch": round(h["pairs_ms"] * 1e3, 3),
-                     "ceiling_gbs": ceil["rmw_in_place"]["gbs"],
+                     "ceiling_gbs": ceil["rmw_in_place"]["gbs"] if ceil else None,
                      "ceiling_kernel": "in-place read-modify-write of the same 256 MiB of state traffic "
                                        "(libkda_ceiling.so rmw_kernel), median of 3 regions",
-                     "frac_of_ceiling": round(achieved / ceil["rmw_in_place"]["gbs"], 4)},
+                     "frac_of_ceiling": round(achieved / ceil["rmw_in_place"]["gbs"], 4) if ceil else None},
         "cpu_baseline": cpu,
         "breakdown": breakdown,
     }
