@@ -685,8 +685,8 @@ def stored_traffic(tile, key="hbm_bytes_per_launch"):
     fields = {}
     for line in open(COUNTERS_FILE):
         if ":" in line and not line.startswith("#"):
-            key, val = line.split(":", 1)
-            fields[key.strip()] = val.strip()
+            name, val = line.split(":", 1)
+            fields[name.strip()] = val.strip()
     if fields.get("kernel_source_sha256") != kernel_source_sha256():
         return None
     if fields.get("launch") != f"tile_w {tile[0]}, threads {tile[1]}":
