@@ -265,9 +265,15 @@ __global__ __launch_bounds__(kChunkPrepThreads) void prefill_chunk_prep_kernel(C
 
   // inside each sub-block: A and B by running products. Row (s, 16 lanes) of
   // sub-block o carries D(t, s) over its lane's channels cl + 16 e as t advances
-  // and sums over the row; the 32 rows of 16 lanes cover both sub-blocks.
+  // and sums over the row; the 32 rows of 16 lanes cover both sub-blocks. A wave
+  // starts at the first token past its rows (the steps before it only fed
+  // discarded sums), and the second sub-block's rows run in reverse order, so
+  // that the two waves on a SIMD (w and w + 4) need 18 steps together instead of
+  // up to 30: this pass is bound by VALU issue.
   if ((int)threadIdx.x < 2 * kSB * 16) {
-    const int o = (threadIdx.x >> 8) * kSB, s = (threadIdx.x >> 4) & 15, cl = threadIdx.x & 15;
+    const int o = (threadIdx.x >> 8) * kSB, r = (threadIdx.x >> 4) & 15, cl = threadIdx.x & 15;
+    const int s = o == 0 ? r : kSB - 1 - r;
+    const int s_min = __builtin_amdgcn_readfirstlane(o == 0 ? (r & ~3) : kSB - 1 - (r | 3));
     float d[CPT];
     float pd = 0.0f;
 #pragma unroll
@@ -278,8 +284,7 @@ __global__ __launch_bounds__(kChunkPrepThreads) void prefill_chunk_prep_kernel(C
     }
     pd = row16_sum(pd);
     if (cl == 0) Bl[(o + s) * kCL + o + s] = pd;
-#pragma unroll
-    for (int t = 1; t < kSB; ++t) {
+    for (int t = s_min + 1; t < kSB; ++t) {
       const bool after = t > s;  // D(t, s) starts at k_s and takes alpha_t only past s
       float pa = 0.0f, pb = 0.0f;
 #pragma unroll
