@@ -264,35 +264,49 @@ __global__ __launch_bounds__(kChunkPrepThreads) void prefill_chunk_prep_kernel(C
   }
 
   // inside each sub-block: A and B by running products. Row (s, 16 lanes) of
-  // sub-block o carries D(t, s) over its lane's channels cl + 16 e as t advances
-  // and sums over the row; the 32 rows of 16 lanes cover both sub-blocks. A wave
-  // starts at the first token past its rows (the steps before it only fed
+  // sub-block o carries D(t, s) over its lane's channels 4 cl + 64 e4 .. + 3 as t
+  // advances and sums over the row; the 32 rows of 16 lanes cover both sub-blocks.
+  // A wave starts at the first token past its rows (the steps before it only fed
   // discarded sums), and the second sub-block's rows run in reverse order, so
   // that the two waves on a SIMD (w and w + 4) need 18 steps together instead of
-  // up to 30: this pass is bound by VALU issue.
+  // up to 30: this pass is bound by VALU issue. Each step reads token t's k, q and
+  // alpha with 128-bit LDS reads before any arithmetic and applies alpha_t as a
+  // factor (1 up to s, exact), so no read waits behind a per-lane branch.
   if ((int)threadIdx.x < 2 * kSB * 16) {
+    static_assert(CPT % 4 == 0, "whole float4 per lane");
     const int o = (threadIdx.x >> 8) * kSB, r = (threadIdx.x >> 4) & 15, cl = threadIdx.x & 15;
     const int s = o == 0 ? r : kSB - 1 - r;
     const int s_min = __builtin_amdgcn_readfirstlane(o == 0 ? (r & ~3) : kSB - 1 - (r | 3));
-    float d[CPT];
+    auto ld_row = [&](const float *x, int t, float (&y)[CPT]) {
+#pragma unroll
+      for (int e4 = 0; e4 < CPT / 4; ++e4) {
+        const float4 v = *reinterpret_cast<const float4 *>(x + (o + t) * PK + 4 * cl + 64 * e4);
+        y[4 * e4] = v.x;
+        y[4 * e4 + 1] = v.y;
+        y[4 * e4 + 2] = v.z;
+        y[4 * e4 + 3] = v.w;
+      }
+    };
+    float d[CPT], qs[CPT];
+    ld_row(kb, s, d);
+    ld_row(qb, s, qs);
     float pd = 0.0f;
 #pragma unroll
-    for (int e = 0; e < CPT; ++e) {
-      const int c0 = (o + s) * PK + cl + 16 * e;
-      d[e] = kb[c0];
-      pd = __builtin_fmaf(qb[c0], d[e], pd);
-    }
+    for (int e = 0; e < CPT; ++e) pd = __builtin_fmaf(qs[e], d[e], pd);
     pd = row16_sum(pd);
     if (cl == 0) Bl[(o + s) * kCL + o + s] = pd;
     for (int t = s_min + 1; t < kSB; ++t) {
       const bool after = t > s;  // D(t, s) starts at k_s and takes alpha_t only past s
+      float kt[CPT], qt[CPT], at[CPT];
+      ld_row(kb, t, kt);
+      ld_row(qb, t, qt);
+      ld_row(ab, t, at);
       float pa = 0.0f, pb = 0.0f;
 #pragma unroll
       for (int e = 0; e < CPT; ++e) {
-        const int c0 = (o + t) * PK + cl + 16 * e;
-        d[e] = after ? d[e] * ab[c0] : d[e];
-        pa = __builtin_fmaf(kb[c0], d[e], pa);
-        pb = __builtin_fmaf(qb[c0], d[e], pb);
+        d[e] = d[e] * (after ? at[e] : 1.0f);
+        pa = __builtin_fmaf(kt[e], d[e], pa);
+        pb = __builtin_fmaf(qt[e], d[e], pb);
       }
       pa = row16_sum(pa);
       pb = row16_sum(pb);
