@@ -414,13 +414,25 @@ __global__ __launch_bounds__(kChunkPrepThreads) void prefill_chunk_prep_kernel(C
   // T = X Diag(beta) goes to Tm.
   if ((int)threadIdx.x < 2 * kSB) {
     const int J = threadIdx.x / kSB, col = threadIdx.x % kSB, o = J * kSB;
-    float x[kSB];
+    // Every row's sum is formed and the entries above and on the diagonal are
+    // selected afterwards, so no read waits behind a per-lane branch; row t + 1
+    // of A is read while row t is summed.
+    float x[kSB], arow[kSB], nrow[kSB];
 #pragma unroll
     for (int t = 0; t < kSB; ++t) {
+      if (t + 1 < kSB) {
+#pragma unroll
+        for (int s2 = 0; s2 <= t; ++s2) nrow[s2] = Am[(o + t + 1) * kCL + o + s2];
+      }
+      const float bt = bet[o + t];
       float acc = 0.0f;
 #pragma unroll
-      for (int s2 = 0; s2 < t; ++s2) acc = __builtin_fmaf(Am[(o + t) * kCL + o + s2], x[s2], acc);
-      x[t] = t == col ? 1.0f : (t < col ? 0.0f : -bet[o + t] * acc);
+      for (int s2 = 0; s2 < t; ++s2) acc = __builtin_fmaf(arow[s2], x[s2], acc);
+      float xt = -bt * acc;
+      asm volatile("" : "+v"(xt));  // computed here, not sunk into a branch of the select
+      x[t] = t == col ? 1.0f : (t < col ? 0.0f : xt);
+#pragma unroll
+      for (int s2 = 0; s2 <= t; ++s2) arow[s2] = nrow[s2];
     }
 #pragma unroll
     for (int t = 0; t < kSB; ++t) Tm[(o + t) * (kCL + 1) + o + col] = x[t];
