@@ -533,17 +533,17 @@ __device__ __forceinline__ float4 ws4(const float *w, int off) {
 
 // One workgroup per (row, head, 16 value columns), eight waves in two roles.
 // Wave q < 4 carries the recurrence over key channels [q DK/4, (q + 1) DK/4):
-//   W S0 over its channels -> (barrier) -> delta = U - sum of the four partials
+//   W S0 and [Gamma q] S0 over its channels -> (barrier)
+//   -> delta = U - sum of the four W S0 partials
 //   -> S0 <- Diag(Gamma_L) S0 + Kt^T delta
 // holding the state in the accumulator layout (lane (j, g) has channels
-// q DK/4 + 16 ct + 4 g .. + 3 of column j). Side wave 4 + q computes [Gamma q] S0
-// over the same channels from a copy of S0 in LDS, and side waves 5 and 6 finish
-// each chunk's outputs, o = [Gamma q] S0 + B delta, one barrier later. A
-// recurrence wave and its side wave share a SIMD: the recurrence waves run at
-// the higher priority, and the side waves' products fill the matrix unit while
-// they wait at the barrier or on LDS. One barrier per chunk; every LDS array is
-// double-buffered by chunk parity, and a buffer is written again only after
-// the barrier that follows its last read.
+// q DK/4 + 16 ct + 4 g .. + 3 of column j), at the higher priority. Side waves 5
+// and 6 finish each chunk's outputs, o = [Gamma q] S0 + B delta, one barrier
+// later; waves 4 and 7 only keep the barrier count. (With the [Gamma q] S0
+// products on side waves sharing the SIMDs, the side waves' path was the longer
+// one: measured on MI355X, 8000 tokens 735 -> 710 us with them moved here.) One
+// barrier per chunk; a buffer is written again only after the barrier that
+// follows its last read.
 template <int DK, int DV>
 __global__ __launch_bounds__(kChunkStateThreads) void prefill_chunk_state_kernel(ChunkArgs a) {
   using WS = ChunkWs<DK, DV>;
@@ -554,8 +554,11 @@ __global__ __launch_bounds__(kChunkStateThreads) void prefill_chunk_state_kernel
   // holds token 4 (4 rb + c) + g, column j of lane (j, g), so that each lane reads
   // the partials it needs as float4s.
   __shared__ float4 pdp[2][4][2][64];
-  __shared__ v4f pop[2][4][2][64];        // [Gamma q] S0 partials, accumulator layout
-  __shared__ float4 sx[2][4][NCT][64];    // S0 for the side waves: [parity][wave][ct][lane]
+  // [Gamma q] S0 partials, accumulator layout, by chunk index mod 3: written
+  // before barrier jc and read by the output finish after barrier jc + 1, while
+  // the recurrence waves already write those of chunk jc + 1 (the chunk loop is
+  // unrolled three times, so the index is static there)
+  __shared__ v4f pop[3][4][2][64];
   __shared__ float4 dlt[2][2][64];        // delta, B-operand layout: [parity][h][lane] holds ks = 4 h + c
 
   const Unit u = unit_of_block_rows(a.ntile, a.H, a.B);
@@ -601,8 +604,6 @@ __global__ __launch_bounds__(kChunkStateThreads) void prefill_chunk_state_kernel
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) st4<kVerifyStoreStream>(CK + 16 * ct, s[ct]);
     }
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) sx[0][q][ct][lane] = s[ct];
     // The operands of the chunk two ahead are read while this one computes, in
     // two batches that each follow a burst of products (a load issue that waits
     // for queue space then holds up no product): W and Kt behind W S0, Gamma_L and
@@ -613,7 +614,7 @@ __global__ __launch_bounds__(kChunkStateThreads) void prefill_chunk_state_kernel
     // Past the last chunk the last one is read again, so every load is
     // unconditional.
     struct Ops {
-      float4 wv[2][NCT], kt[NCT][2], gl[NCT], uv[2];
+      float4 wv[2][NCT], qv[2][NCT], kt[NCT][2], gl[NCT], uv[2];
     };
     auto load_wk = [&](Ops &o, const float *w) {
 #pragma unroll
@@ -627,11 +628,15 @@ __global__ __launch_bounds__(kChunkStateThreads) void prefill_chunk_state_kernel
     };
     auto load_gu = [&](Ops &o, const float *w) {
 #pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) o.qv[rt][ct] = ws4<WS>(w, WS::QD + (((rt * NCT + ct) * 4 + q) * 64 + lane) * 4);
+#pragma unroll
       for (int ct = 0; ct < NCT; ++ct) o.gl[ct] = ws4<WS>(w, WS::GL + coff + 16 * ct);
 #pragma unroll
       for (int h = 0; h < 2; ++h) o.uv[h] = ws4<WS>(w, WS::U + u.tile * (kCL * 16) + (h * 64 + lane) * 4);
     };
-    auto step = [&](int jc, const Ops &cur, Ops &nxt) {
+    auto step = [&](int jc, int ps, const Ops &cur, Ops &nxt) {
       const int p = jc & 1;
       // W S0 over this wave's channels
       v4f pd[2];
@@ -646,6 +651,20 @@ __global__ __launch_bounds__(kChunkStateThreads) void prefill_chunk_state_kernel
           pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.wv[rt][ct].w, s[ct].w, pd[rt], 0, 0, 0);
         }
       }
+      // [Gamma q] S0 over this wave's channels, from the same S0 (the same product
+      // order as W S0), for the output finish one barrier later
+      v4f po[2];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        po[rt] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.qv[rt][ct].x, s[ct].x, po[rt], 0, 0, 0);
+          po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.qv[rt][ct].y, s[ct].y, po[rt], 0, 0, 0);
+          po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.qv[rt][ct].z, s[ct].z, po[rt], 0, 0, 0);
+          po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.qv[rt][ct].w, s[ct].w, po[rt], 0, 0, 0);
+        }
+      }
       const float *wn = chunk_ws<WS>(a, cbase + min(jc + 2, last), u.h);
       load_wk(nxt, wn);
       // this lane's accumulator element e (token 16 rt + 4 g + e, column j) is element
@@ -654,6 +673,8 @@ __global__ __launch_bounds__(kChunkStateThreads) void prefill_chunk_state_kernel
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) reinterpret_cast<float *>(&pdp[p][q][rt][e * 16 + j])[g] = pd[rt][e];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) pop[ps][q][rt][lane] = po[rt];
       __syncthreads();
 
       // delta = U - W S0 at this lane's B-operand positions (token 4 ks + g, column
@@ -687,8 +708,6 @@ __global__ __launch_bounds__(kChunkStateThreads) void prefill_chunk_state_kernel
         s[ct] = make_float4(acc[0], acc[1], acc[2], acc[3]);
       }
       load_gu(nxt, wn);
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) sx[p ^ 1][q][ct][lane] = s[ct];
       int t0, n;
       chunk_tokens(r, jc, t0, n);
       if (ck > 0 && t0 + n == ck) {
@@ -704,9 +723,9 @@ __global__ __launch_bounds__(kChunkStateThreads) void prefill_chunk_state_kernel
       load_gu(o1, chunk_ws<WS>(a, cbase + min(1, last), u.h));
     }
     for (int jc = 0; jc < r.nch; jc += 3) {
-      step(jc, o0, o2);
-      if (jc + 1 < r.nch) step(jc + 1, o1, o0);
-      if (jc + 2 < r.nch) step(jc + 2, o2, o1);
+      step(jc, 0, o0, o2);
+      if (jc + 1 < r.nch) step(jc + 1, 1, o1, o0);
+      if (jc + 2 < r.nch) step(jc + 2, 2, o2, o1);
     }
     __syncthreads();
 #pragma unroll
@@ -716,27 +735,23 @@ __global__ __launch_bounds__(kChunkStateThreads) void prefill_chunk_state_kernel
 
   // ---- side waves ----
   // Wave 5 finishes row block 1 (tokens 16..31, B over all 32 deltas) and wave 6
-  // row block 0 (tokens 0..15, whose B has no entries past token 15).
+  // row block 0 (tokens 0..15, whose B has no entries past token 15); waves 4 and
+  // 7 only keep the barrier count.
   const int rb = wave == 6 ? 0 : 1;
   const bool outw = wave == 5 || wave == 6;
-  // [Gamma q] and B of the chunk two ahead are read while this one computes
-  // (three sets rotate, as on the recurrence waves)
-  struct QOps {
-    float4 qv[2][NCT], bq[2];
+  // B of the chunk two ahead is read while this one finishes (three sets rotate)
+  struct BOps {
+    float4 bq[2];
   };
   float4 bprev[2];
-  auto load_q = [&](QOps &o, const float *w) {
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) o.qv[rt][ct] = ws4<WS>(w, WS::QD + (((rt * NCT + ct) * 4 + q) * 64 + lane) * 4);
+  auto load_b = [&](BOps &o, const float *w) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) o.bq[h] = ws4<WS>(w, WS::BM + ((h * 2 + rb) * 64 + lane) * 4);
   };
-  // the outputs of chunk jc, after the barrier that follows its side products
+  // the outputs of chunk jc, after the barrier that follows its delta
   auto finish = [&](int jc) {
-    const int p = jc & 1;
-    v4f acc = ((pop[p][0][rb][lane] + pop[p][1][rb][lane]) + pop[p][2][rb][lane]) + pop[p][3][rb][lane];
+    const int p = jc & 1, ps = jc % 3;
+    v4f acc = ((pop[ps][0][rb][lane] + pop[ps][1][rb][lane]) + pop[ps][2][rb][lane]) + pop[ps][3][rb][lane];
     const float bm[8] = {bprev[0].x, bprev[0].y, bprev[0].z, bprev[0].w,
                          bprev[1].x, bprev[1].y, bprev[1].z, bprev[1].w};
     const float4 d0 = dlt[p][0][lane];
@@ -764,40 +779,22 @@ __global__ __launch_bounds__(kChunkStateThreads) void prefill_chunk_state_kernel
         if (tok0 + e < n) put_chunk_out(a, o0 + e * row_stride, acc[e]);
     }
   };
-  auto side_step = [&](int jc, const QOps &cur, QOps &nxt) {
-    const int p = jc & 1;
+  auto side_step = [&](int jc, const BOps &cur, BOps &nxt) {
     __syncthreads();
     if (outw && jc > 0) finish(jc - 1);
-    float4 sq[NCT];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) sq[ct] = sx[p][q][ct][lane];
-    v4f po[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      po[rt] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.qv[rt][ct].x, sq[ct].x, po[rt], 0, 0, 0);
-        po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.qv[rt][ct].y, sq[ct].y, po[rt], 0, 0, 0);
-        po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.qv[rt][ct].z, sq[ct].z, po[rt], 0, 0, 0);
-        po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.qv[rt][ct].w, sq[ct].w, po[rt], 0, 0, 0);
-      }
-    }
     bprev[0] = cur.bq[0];
     bprev[1] = cur.bq[1];
-    load_q(nxt, chunk_ws<WS>(a, cbase + min(jc + 2, last), u.h));
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) pop[p][q][rt][lane] = po[rt];
+    if (outw) load_b(nxt, chunk_ws<WS>(a, cbase + min(jc + 2, last), u.h));
   };
-  QOps q0, q1, q2;
-  if (r.nch > 0) {
-    load_q(q0, chunk_ws<WS>(a, cbase, u.h));
-    load_q(q1, chunk_ws<WS>(a, cbase + min(1, last), u.h));
+  BOps b0, b1, b2;
+  if (outw && r.nch > 0) {
+    load_b(b0, chunk_ws<WS>(a, cbase, u.h));
+    load_b(b1, chunk_ws<WS>(a, cbase + min(1, last), u.h));
   }
   for (int jc = 0; jc < r.nch; jc += 3) {
-    side_step(jc, q0, q2);
-    if (jc + 1 < r.nch) side_step(jc + 1, q1, q0);
-    if (jc + 2 < r.nch) side_step(jc + 2, q2, q1);
+    side_step(jc, b0, b2);
+    if (jc + 1 < r.nch) side_step(jc + 1, b1, b0);
+    if (jc + 2 < r.nch) side_step(jc + 2, b2, b1);
   }
   __syncthreads();
   if (outw && r.nch > 0) finish(last);
