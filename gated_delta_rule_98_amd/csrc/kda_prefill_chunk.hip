@@ -21,8 +21,8 @@
 // state pass runs per (row, head, 16 value columns) through the row's chunks
 // in order, with the state in MFMA accumulator registers:
 //   delta = U - W S0 ;  o = [Gamma q] S0 + B delta ;  S0 <- Diag(Gamma_L) S0 + Kt^T delta
-// all on v_mfma_f32_16x16x4f32; the products that feed the next chunk and the
-// output products run on separate waves of the workgroup.
+// all on v_mfma_f32_16x16x4f32; the products with the state run on four waves
+// split by key channel, and two other waves finish the outputs a barrier later.
 //
 // Decay products never divide. A chunk is two sub-blocks of 16 tokens. With
 // P_t the product over its own sub-block up to and including t, and R_s the
@@ -531,15 +531,15 @@ __device__ __forceinline__ float4 ws4(const float *w, int off) {
   return *reinterpret_cast<const float4 *>(w + off);
 }
 
-// One workgroup per (row, head, 16 value columns), eight waves in two roles.
+// One workgroup per (row, head, 16 value columns), six waves in two roles.
 // Wave q < 4 carries the recurrence over key channels [q DK/4, (q + 1) DK/4):
 //   W S0 and [Gamma q] S0 over its channels -> (barrier)
 //   -> delta = U - sum of the four W S0 partials
 //   -> S0 <- Diag(Gamma_L) S0 + Kt^T delta
 // holding the state in the accumulator layout (lane (j, g) has channels
-// q DK/4 + 16 ct + 4 g .. + 3 of column j), at the higher priority. Side waves 5
-// and 6 finish each chunk's outputs, o = [Gamma q] S0 + B delta, one barrier
-// later; waves 4 and 7 only keep the barrier count. (With the [Gamma q] S0
+// q DK/4 + 16 ct + 4 g .. + 3 of column j), at the higher priority. Waves 4
+// and 5 finish each chunk's outputs, o = [Gamma q] S0 + B delta, one barrier
+// later. (With the [Gamma q] S0
 // products on side waves sharing the SIMDs, the side waves' path was the longer
 // one: measured on MI355X, 8000 tokens 735 -> 710 us with them moved here.) One
 // barrier per chunk; a buffer is written again only after the barrier that
@@ -549,7 +549,7 @@ __global__ __launch_bounds__(kChunkStateThreads) void prefill_chunk_state_kernel
   using WS = ChunkWs<DK, DV>;
   constexpr int CPW = DK / 4;    // key channels per wave
   constexpr int NCT = CPW / 16;  // 16-channel tiles per wave
-  static_assert(kChunkStateThreads == 512, "four recurrence waves and four side waves");
+  static_assert(kChunkStateThreads == 384, "four recurrence waves and two finishing waves");
   // W S0 partials in the reading lanes' layout: [parity][wave][row block][lane][c]
   // holds token 4 (4 rb + c) + g, column j of lane (j, g), so that each lane reads
   // the partials it needs as float4s.
@@ -606,11 +606,12 @@ __global__ __launch_bounds__(kChunkStateThreads) void prefill_chunk_state_kernel
     }
     // The operands of the chunk two ahead are read while this one computes, in
     // two batches that each follow a burst of products (a load issue that waits
-    // for queue space then holds up no product): W and Kt behind W S0, Gamma_L and
-    // U behind the update. Three operand sets rotate (the loop body is unrolled
-    // three times), so no register copy waits for a load early; one chunk ahead,
-    // the loads' latency still reached the products (measured on MI355X: 8000
-    // tokens 790 -> 740 us, with the side waves' operands likewise two ahead).
+    // for queue space then holds up no product): W and Kt behind the products
+    // with S0, [Gamma q], Gamma_L and U behind the update (other splits measured
+    // slower). Three operand sets rotate (the loop body is unrolled three times),
+    // so no register copy waits for a load early; one chunk ahead, the loads'
+    // latency still reached the products (measured on MI355X: 8000 tokens 790 ->
+    // 740 us).
     // Past the last chunk the last one is read again, so every load is
     // unconditional.
     struct Ops {
@@ -733,12 +734,10 @@ __global__ __launch_bounds__(kChunkStateThreads) void prefill_chunk_state_kernel
     return;
   }
 
-  // ---- side waves ----
-  // Wave 5 finishes row block 1 (tokens 16..31, B over all 32 deltas) and wave 6
-  // row block 0 (tokens 0..15, whose B has no entries past token 15); waves 4 and
-  // 7 only keep the barrier count.
-  const int rb = wave == 6 ? 0 : 1;
-  const bool outw = wave == 5 || wave == 6;
+  // ---- finishing waves ----
+  // Wave 4 finishes row block 1 (tokens 16..31, B over all 32 deltas) and wave 5
+  // row block 0 (tokens 0..15, whose B has no entries past token 15).
+  const int rb = wave == 5 ? 0 : 1;
   // B of the chunk two ahead is read while this one finishes (three sets rotate)
   struct BOps {
     float4 bq[2];
@@ -781,13 +780,13 @@ __global__ __launch_bounds__(kChunkStateThreads) void prefill_chunk_state_kernel
   };
   auto side_step = [&](int jc, const BOps &cur, BOps &nxt) {
     __syncthreads();
-    if (outw && jc > 0) finish(jc - 1);
+    if (jc > 0) finish(jc - 1);
     bprev[0] = cur.bq[0];
     bprev[1] = cur.bq[1];
-    if (outw) load_b(nxt, chunk_ws<WS>(a, cbase + min(jc + 2, last), u.h));
+    load_b(nxt, chunk_ws<WS>(a, cbase + min(jc + 2, last), u.h));
   };
   BOps b0, b1, b2;
-  if (outw && r.nch > 0) {
+  if (r.nch > 0) {
     load_b(b0, chunk_ws<WS>(a, cbase, u.h));
     load_b(b1, chunk_ws<WS>(a, cbase + min(1, last), u.h));
   }
@@ -797,7 +796,7 @@ __global__ __launch_bounds__(kChunkStateThreads) void prefill_chunk_state_kernel
     if (jc + 2 < r.nch) side_step(jc + 2, b2, b1);
   }
   __syncthreads();
-  if (outw && r.nch > 0) finish(last);
+  if (r.nch > 0) finish(last);
 }
 
 }  // namespace
