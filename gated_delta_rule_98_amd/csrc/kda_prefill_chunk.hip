@@ -410,8 +410,8 @@ __global__ __launch_bounds__(kChunkPrepThreads) void prefill_chunk_prep_kernel(C
   }
 
   // X = (I + Diag(beta) A)^-1 by 16 x 16 blocks: the two diagonal blocks by forward
-  // substitution (one column per thread), then X10 = -X11 (Diag(beta) A)10 X00.
-  // T = X Diag(beta) goes to Tm.
+  // substitution (one column per thread), then X10 = -X11 (Diag(beta) A)10 X00,
+  // into Tm; the products below read T = X Diag(beta) as X_ts beta_s.
   if ((int)threadIdx.x < 2 * kSB) {
     const int J = threadIdx.x / kSB, col = threadIdx.x % kSB, o = J * kSB;
     // Every row's sum is formed and the entries above and on the diagonal are
@@ -456,12 +456,6 @@ __global__ __launch_bounds__(kChunkPrepThreads) void prefill_chunk_prep_kernel(C
     Tm[t * (kCL + 1) + kSB + col] = 0.0f;
   }
   __syncthreads();
-  // T = X Diag(beta)
-  for (int idx = threadIdx.x; idx < kCL * kCL; idx += blockDim.x) {
-    const int t = idx / kCL, col = idx % kCL;
-    Tm[t * (kCL + 1) + col] *= bet[col];
-  }
-  __syncthreads();
 
   // W = T [Gamma k] and U = T V: 16 x 16 output tiles spread over the waves
   constexpr int TW = DK / 16, TU = DV / 16;
@@ -471,7 +465,7 @@ __global__ __launch_bounds__(kChunkPrepThreads) void prefill_chunk_prep_kernel(C
 #pragma unroll
     for (int ks = 0; ks < kCL / 4; ++ks) {
       const int tok = 4 * ks + g;
-      av[ks] = Tm[(16 * rt + m) * (kCL + 1) + tok];
+      av[ks] = Tm[(16 * rt + m) * (kCL + 1) + tok] * bet[tok];
       // [Gamma k] = [P k] times the product of the earlier sub-blocks (one for block 0)
       bv[ks] = ks < kSB / 4 ? kb[tok * PK + 16 * ct + m] : kb[tok * PK + 16 * ct + m] * gb[16 * ct + m];
     }
@@ -488,7 +482,7 @@ __global__ __launch_bounds__(kChunkPrepThreads) void prefill_chunk_prep_kernel(C
 #pragma unroll
     for (int ks = 0; ks < kCL / 4; ++ks) {
       const int tok = 4 * ks + g;
-      av[ks] = Tm[(16 * rt + m) * (kCL + 1) + tok];
+      av[ks] = Tm[(16 * rt + m) * (kCL + 1) + tok] * bet[tok];
       bv[ks] = vb[tok * DV + 16 * ct + m];
     }
     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
