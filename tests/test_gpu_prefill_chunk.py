@@ -108,6 +108,29 @@ def test_chunked_prefill_b64_mixed_lengths():
     _check(w, slots, pos, out_c, ckpt_c, cache_c)
 
 
+def test_chunked_prefill_more_rows_than_one_map_tile():
+    """1,300 rows, more than the chunk map's workgroup of 1,024 threads scans at once, so its
+    prefix sum carries across tiles and chunks of the second tile map to rows past 1,024. Short
+    mixed prompts (empty, one token, one chunk, just past one), padding rows and checkpoints;
+    against the oracle and the recurrent form."""
+    rng = np.random.Generator(np.random.PCG64(76))
+    B = 1300
+    seqlens = rng.choice([0, 1, 3, 17, 32, 33, 40], B).astype(int)
+    w = synth.make(B, 2, 64, 64, seqlens=seqlens, num_slots=B + 17, state_std=0.05, seed=77)
+    slots = w.slot_ids.copy()
+    slots[[3, 1030, 1299]] = -1
+    pos = np.array([rng.choice([-1, 0, n // 2, n]) if n else -1 for n in seqlens], np.int32)
+    cache_c, cache_r = f32(w.cache), f32(w.cache)
+    log(f"chunked prefill B={B}, {w.n_tok} tokens, 2 heads, d=64")
+    out_c, ckpt_c = _run(w, cache_c, slots=slots, pos=pos)
+    out_r, ckpt_r = _run(w, cache_r, slots=slots, pos=pos, chunked=False)
+    torch.cuda.synchronize()
+    live = np.concatenate([np.arange(w.cu_seqlens[b], w.cu_seqlens[b + 1]) for b in range(B) if slots[b] >= 0])
+    assert out_rel(out_c.cpu().numpy()[live], out_r.cpu().numpy()[live]) <= 1e-5
+    assert state_rel(cache_c.cpu().numpy(), cache_r.cpu().numpy()) <= 1e-5
+    _check(w, slots, pos, out_c, ckpt_c, cache_c)
+
+
 def test_chunked_prefill_without_checkpoints_and_against_recurrent_form():
     seqlens = [300, 31, 65]
     w = synth.make(3, 8, 128, 128, seqlens=seqlens, num_slots=4, state_std=0.05, seed=72)
