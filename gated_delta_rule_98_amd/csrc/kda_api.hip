@@ -626,7 +626,9 @@ static int state_copy(bool pack, float *cache, int64_t num_slots, int64_t slot_s
   if (!slot_ids || !buf) return KDA_ERR_INVALID;
   KDA_TRY(check_cache(cache, num_slots, slot_stride, H, dk, dv));
   if (!aligned(buf, 16) || (dev_err && !aligned(dev_err, 4))) return KDA_ERR_ALIGN;
-  const int64_t blocks = (int64_t)B * nheads;
+  const int lanes = state_copy_lanes();
+  const int parts = (ncols * dk / 4 + lanes - 1) / lanes;
+  const int64_t blocks = (int64_t)B * nheads * parts;
   if (blocks > 0x7fffffff) return KDA_ERR_UNSUPPORTED;
   PackArgs p;
   p.cache = cache;
@@ -642,9 +644,10 @@ static int state_copy(bool pack, float *cache, int64_t num_slots, int64_t slot_s
   p.nheads = nheads;
   p.col0 = col0;
   p.ncols = ncols;
+  p.parts = parts;
   void *args[] = {&p};
   const void *fn = state_copy_kernel_for(pack);
-  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(256), args, 0, (hipStream_t)stream);
+  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(lanes), args, 0, (hipStream_t)stream);
   return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

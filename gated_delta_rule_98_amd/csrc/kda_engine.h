@@ -567,6 +567,7 @@ struct PackArgs {
   float *buf;
   int32_t *dev_err;
   int32_t H, dk, dv, head0, nheads, col0, ncols;
+  int32_t parts;  // workgroups per (row, head) span
 };
 
 // ----------------------------------------------------------------------------
@@ -596,6 +597,7 @@ const void *commit_replay_kernel_for(int dk, int C, bool inputs_first);  // kda_
 const void *commit_copy_kernel_for(int dk, int C);                  // kda_verify.hip
 const void *prefill_kernel_for(int dk, int C, int io);              // kda_prefill.hip
 const void *state_copy_kernel_for(bool pack);                       // kda_state.hip
+int state_copy_lanes();                                             // kda_state.hip: lanes per workgroup
 
 // Dynamic LDS bytes of the kernels that take it.
 size_t staged_bytes(int dk, int T_max, int W, bool gate);           // verify, replay commit
