@@ -21,8 +21,23 @@
 // state pass runs per (row, head, 16 value columns) through the row's chunks
 // in order, with the state in MFMA accumulator registers:
 //   delta = U - W S0 ;  o = [Gamma q] S0 + B delta ;  S0 <- Diag(Gamma_L) S0 + Kt^T delta
-// all on v_mfma_f32_16x16x4f32; the products with the state run on four waves
-// split by key channel, and two other waves finish the outputs a barrier later.
+// The products with the state run on four waves split by key channel, and two
+// other waves finish the outputs a barrier later.
+//
+// Products with the state on the bfloat16 matrix cores. gfx950 has no
+// reduced-precision fp32 (xf32) MFMA, and its fp32 one, v_mfma_f32_16x16x4f32,
+// issues every 32 cycles for 1,024 multiply-adds, while v_mfma_f32_16x16x32_bf16
+// issues every 16 cycles for 8,192 (both measured on MI355X). Each fp32 operand
+// x is split into bfloat16 parts, hi = RNE(x) and lo = RNE(x - hi) (x - hi is
+// exact), so that x = hi + lo to within 2^-18 |x|, and a product is taken as
+// a_lo b_hi + a_hi b_lo + a_hi b_hi with fp32 accumulation: each term is exact
+// in fp32 and the dropped a_lo b_lo is below 2^-18 |a b|, so a product is off
+// by at most about 3 2^-18 (1.2e-5) of |a b|, where fp32 products are off by
+// 2^-24. The state itself stays fp32 in the accumulators. The precompute writes
+// W, [Gamma q] and Kt already split; the state pass splits S0 and delta (three
+// bfloat16 products replace eight fp32 ones per 16 x 16 x 32 block; measured on
+// MI355X, 8000-token prefill 704-726 -> 613-620 us). The output finish (B delta)
+// stays on fp32 MFMA.
 //
 // Decay products never divide. A chunk is two sub-blocks of 16 tokens. With
 // P_t the product over its own sub-block up to and including t, and R_s the
@@ -46,6 +61,44 @@ constexpr int kCL = kChunkTokens;  // tokens per chunk
 constexpr int kSB = 16;            // sub-block: the MFMA row block
 static_assert(kCL == 2 * kSB, "the chunk is two sub-blocks");
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// (x0, x1) to packed bfloat16 pairs: hi = RNE(x) and lo = RNE(x - hi), element
+// 0 in the low half of each word
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t &hi, uint32_t &lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x0, x1}, bf16x2));
+  const float r0 = x0 - __builtin_bit_cast(float, hi << 16);
+  const float r1 = x1 - __builtin_bit_cast(float, hi & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){r0, r1}, bf16x2));
+}
+
+// The split of N floats as N/2 hi words then N/2 lo words
+template <int N>
+__device__ __forceinline__ void split_n(const float (&x)[N], uint32_t (&w)[N]) {
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) split_pair(x[2 * i], x[2 * i + 1], w[i], w[N / 2 + i]);
+}
+
+// 16-byte slot s of the split of N floats (N = 8: s = 0 the hi, 1 the lo parts;
+// N = 4: s = 0, hi then lo)
+template <int N>
+__device__ __forceinline__ float4 split_slot(const float (&x)[N], int s) {
+  uint32_t w[N];
+  split_n<N>(x, w);
+  if constexpr (N == 8) {
+    return s == 0 ? make_float4(__builtin_bit_cast(float, w[0]), __builtin_bit_cast(float, w[1]),
+                                __builtin_bit_cast(float, w[2]), __builtin_bit_cast(float, w[3]))
+                  : make_float4(__builtin_bit_cast(float, w[N / 2]), __builtin_bit_cast(float, w[N / 2 + 1]),
+                                __builtin_bit_cast(float, w[N / 2 + 2]), __builtin_bit_cast(float, w[N / 2 + 3]));
+  } else {
+    return make_float4(__builtin_bit_cast(float, w[0]), __builtin_bit_cast(float, w[1]),
+                       __builtin_bit_cast(float, w[2]), __builtin_bit_cast(float, w[3]));
+  }
+}
+
 // Workspace of one (chunk, head), in floats.
 template <int DK, int DV>
 struct ChunkWs {
@@ -61,14 +114,18 @@ struct ChunkWs {
 
 // Every array but Gamma_L is stored in the order in which the state pass
 // reads it, so that each load instruction of a wave reads one contiguous
-// block (1 KB for float4 loads) instead of a piece of each of 16 rows. With
+// block (1 KB for 16-byte loads) instead of a piece of each of 16 rows. With
 // wave w of the state pass holding key channels [w DK/4, (w + 1) DK/4) and
 // lane (j, g) = (lane % 16, lane / 16):
-//   W, [Gamma q]  [rt][ct][w][lane][4]: token 16 rt + j, channels w DK/4 + 16 ct + 4 g .. + 3
-//   Kt            [ct][h][w][lane][4]:  key channel w DK/4 + 16 ct + j, tokens 4 (4 h + e) + g
-//   B             [h][rb][lane][4]:     row 16 rb + j, entries 4 (4 h + e) + g
-//   U             [tile][h][lane][4]:   value column 16 tile + j, tokens 4 (4 h + e) + g
-// (ct < DK / 64, h and rb < 2, e < 4 the float of the float4.)
+//   W, [Gamma q]  [rt][s][w][lane]: token 16 rt + j at the lane's channels
+//                 w DK/4 + 16 (i / 4) + 4 g + i % 4, i < DK / 16
+//   Kt            [ct][s][w][lane]: key channel w DK/4 + 16 ct + j at tokens 4 i + g, i < 8
+//   B             [h][rb][lane][4]: row 16 rb + j, entries 4 (4 h + e) + g (fp32)
+//   U             [tile][h][lane][4]: value column 16 tile + j, tokens 4 (4 h + e) + g (fp32)
+// W, [Gamma q] and Kt hold the bfloat16 split of their n = 8 (n = 4 for W and
+// [Gamma q] at DK = 64) values per lane: the n hi parts, then the n lo parts,
+// each pair packed low half first, 16 bytes per slot s (ct < DK / 64, h and rb
+// < 2, e < 4 the float of the float4).
 
 // Chunks of one row.// Chunks of one row. nch = 0 for a row that does not run (padding, or any
 // device error; the state pass reports those).
@@ -345,31 +402,42 @@ __global__ __launch_bounds__(kChunkPrepThreads) void prefill_chunk_prep_kernel(C
   }
   __syncthreads();
   // Gamma q = [P q] x (earlier sub-blocks), keys decayed to the chunk end = [R k] x
-  // (later sub-blocks), Gamma_L, to the workspace in its read order, one float4 per
-  // thread and step
+  // (later sub-blocks), both split to bfloat16 parts, and Gamma_L, to the workspace
+  // in its read order, one 16-byte slot per thread and step
   constexpr int CPW = DK / 4, NCT = CPW / 16;
   for (int d4 = threadIdx.x; d4 < kCL * DK / 4; d4 += blockDim.x) {
     const int lane = d4 & 63, w = (d4 >> 6) & 3, r2 = d4 >> 8, j = lane & 15, g = lane >> 4;
     {
-      const int ct = r2 % NCT, t = 16 * (r2 / NCT) + j, i0 = w * CPW + 16 * ct + 4 * g;
-      float4 qf = *reinterpret_cast<const float4 *>(qb + t * PK + i0);
-      if (t >= kSB) {
-        qf.x *= gb[i0];
-        qf.y *= gb[i0 + 1];
-        qf.z *= gb[i0 + 2];
-        qf.w *= gb[i0 + 3];
+      const int t = 16 * (r2 / NCT) + j;
+      float x[4 * NCT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const int i0 = w * CPW + 16 * ct + 4 * g;
+        float4 qf = *reinterpret_cast<const float4 *>(qb + t * PK + i0);
+        if (t >= kSB) {  // uniform over the wave
+          qf.x *= gb[i0];
+          qf.y *= gb[i0 + 1];
+          qf.z *= gb[i0 + 2];
+          qf.w *= gb[i0 + 3];
+        }
+        x[4 * ct] = qf.x;
+        x[4 * ct + 1] = qf.y;
+        x[4 * ct + 2] = qf.z;
+        x[4 * ct + 3] = qf.w;
       }
-      *reinterpret_cast<float4 *>(ws + WS::QD + 4 * d4) = qf;
+      *reinterpret_cast<float4 *>(ws + WS::QD + 4 * d4) = split_slot<4 * NCT>(x, r2 % NCT);
     }
     {
-      const int h = r2 & 1, i = w * CPW + 16 * (r2 >> 1) + j;
-      float kv[4];
+      const int i = w * CPW + 16 * (r2 >> 1) + j;
+      const float gk = gb[DK + i];
+      float kv[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int s = 4 * (4 * h + e) + g;
-        kv[e] = s < kSB ? ab[s * PK + i] * gb[DK + i] : ab[s * PK + i];
+      for (int e = 0; e < 8; ++e) {
+        const int tok = 4 * e + g;
+        const float y = ab[tok * PK + i];
+        kv[e] = tok < kSB ? y * gk : y;
       }
-      *reinterpret_cast<float4 *>(ws + WS::KT + 4 * d4) = make_float4(kv[0], kv[1], kv[2], kv[3]);
+      *reinterpret_cast<float4 *>(ws + WS::KT + 4 * d4) = split_slot<8>(kv, r2 & 1);
     }
   }
   if ((int)threadIdx.x < DK) ws[WS::GL + threadIdx.x] = gb[threadIdx.x] * gb[DK + threadIdx.x];
@@ -494,8 +562,17 @@ __global__ __launch_bounds__(kChunkPrepThreads) void prefill_chunk_prep_kernel(C
   __syncthreads();
   for (int d4 = threadIdx.x; d4 < kCL * DK / 4; d4 += blockDim.x) {
     const int lane = d4 & 63, w = (d4 >> 6) & 3, r2 = d4 >> 8;
-    const int t = 16 * (r2 / NCT) + (lane & 15), i0 = w * CPW + 16 * (r2 % NCT) + 4 * (lane >> 4);
-    *reinterpret_cast<float4 *>(ws + WS::W + 4 * d4) = *reinterpret_cast<const float4 *>(qb + t * PK + i0);
+    const int t = 16 * (r2 / NCT) + (lane & 15);
+    float x[4 * NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const float4 v = *reinterpret_cast<const float4 *>(qb + t * PK + w * CPW + 16 * ct + 4 * (lane >> 4));
+      x[4 * ct] = v.x;
+      x[4 * ct + 1] = v.y;
+      x[4 * ct + 2] = v.z;
+      x[4 * ct + 3] = v.w;
+    }
+    *reinterpret_cast<float4 *>(ws + WS::W + 4 * d4) = split_slot<4 * NCT>(x, r2 % NCT);
   }
 }
 
@@ -513,6 +590,46 @@ __device__ __forceinline__ void put_chunk_out(const ChunkArgs &a, int64_t idx, f
     reinterpret_cast<uint16_t *>(a.out)[idx] = f32_to_bf16(y);
   else
     a.out[idx] = y;
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(float4 v) {
+  return __builtin_bit_cast(bf16x8, (u32x4){__builtin_bit_cast(uint32_t, v.x), __builtin_bit_cast(uint32_t, v.y),
+                                            __builtin_bit_cast(uint32_t, v.z), __builtin_bit_cast(uint32_t, v.w)});
+}
+
+// acc + A B over K = 32 (the bfloat16 parts of A in two 16-byte slots, hi then
+// lo; B as split_n words), small terms first
+__device__ __forceinline__ v4f split_mma32(float4 a_hi, float4 a_lo, const uint32_t (&b)[8], v4f acc) {
+  const bf16x8 ah = as_bf16x8(a_hi), al = as_bf16x8(a_lo);
+  const bf16x8 bh = __builtin_bit_cast(bf16x8, (u32x4){b[0], b[1], b[2], b[3]});
+  const bf16x8 bl = __builtin_bit_cast(bf16x8, (u32x4){b[4], b[5], b[6], b[7]});
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+}
+
+// the same over K = 16, A's hi and lo parts in one slot
+__device__ __forceinline__ v4f split_mma16(float4 a, const uint32_t (&b)[4], v4f acc) {
+  const s16x4 ah = __builtin_bit_cast(s16x4, (u32x2){__builtin_bit_cast(uint32_t, a.x), __builtin_bit_cast(uint32_t, a.y)});
+  const s16x4 al = __builtin_bit_cast(s16x4, (u32x2){__builtin_bit_cast(uint32_t, a.z), __builtin_bit_cast(uint32_t, a.w)});
+  const s16x4 bh = __builtin_bit_cast(s16x4, (u32x2){b[0], b[1]});
+  const s16x4 bl = __builtin_bit_cast(s16x4, (u32x2){b[2], b[3]});
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, acc, 0, 0, 0);
+}
+
+// A S0 over a wave's NCT 16-channel tiles (A one row block of W or [Gamma q])
+template <int NCT>
+__device__ __forceinline__ v4f state_mma(const float4 (&a)[NCT], const uint32_t (&sw)[4 * NCT]) {
+  const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (NCT == 2)
+    return split_mma32(a[0], a[1], sw, z);
+  else
+    return split_mma16(a[0], sw, z);
 }
 
 template <class WS>
@@ -633,33 +750,25 @@ __global__ __launch_bounds__(kChunkStateThreads) void prefill_chunk_state_kernel
     };
     auto step = [&](int jc, int ps, const Ops &cur, Ops &nxt) {
       const int p = jc & 1;
-      // W S0 over this wave's channels
-      v4f pd[2];
+      // S0 split to the B operand of the products over this wave's channels: slot i
+      // of lane (j, g) is channel 16 (i / 4) + 4 g + i % 4 of the quarter, where the
+      // accumulator layout already has it (no data moves between lanes)
+      float sv[4 * NCT];
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        pd[rt] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.wv[rt][ct].x, s[ct].x, pd[rt], 0, 0, 0);
-          pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.wv[rt][ct].y, s[ct].y, pd[rt], 0, 0, 0);
-          pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.wv[rt][ct].z, s[ct].z, pd[rt], 0, 0, 0);
-          pd[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.wv[rt][ct].w, s[ct].w, pd[rt], 0, 0, 0);
-        }
+      for (int ct = 0; ct < NCT; ++ct) {
+        sv[4 * ct] = s[ct].x;
+        sv[4 * ct + 1] = s[ct].y;
+        sv[4 * ct + 2] = s[ct].z;
+        sv[4 * ct + 3] = s[ct].w;
       }
-      // [Gamma q] S0 over this wave's channels, from the same S0 (the same product
-      // order as W S0), for the output finish one barrier later
-      v4f po[2];
+      uint32_t sw[4 * NCT];
+      split_n<4 * NCT>(sv, sw);
+      // W S0, then [Gamma q] S0 (for the output finish one barrier later)
+      v4f pd[2], po[2];
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        po[rt] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int rt = 0; rt < 2; ++rt) pd[rt] = state_mma<NCT>(cur.wv[rt], sw);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.qv[rt][ct].x, s[ct].x, po[rt], 0, 0, 0);
-          po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.qv[rt][ct].y, s[ct].y, po[rt], 0, 0, 0);
-          po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.qv[rt][ct].z, s[ct].z, po[rt], 0, 0, 0);
-          po[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.qv[rt][ct].w, s[ct].w, po[rt], 0, 0, 0);
-        }
-      }
+      for (int rt = 0; rt < 2; ++rt) po[rt] = state_mma<NCT>(cur.qv[rt], sw);
       const float *wn = chunk_ws<WS>(a, cbase + min(jc + 2, last), u.h);
       load_wk(nxt, wn);
       // this lane's accumulator element e (token 16 rt + 4 g + e, column j) is element
@@ -692,14 +801,14 @@ __global__ __launch_bounds__(kChunkStateThreads) void prefill_chunk_state_kernel
         for (int h = 0; h < 2; ++h) dlt[p][h][lane] = make_float4(dv[4 * h], dv[4 * h + 1], dv[4 * h + 2], dv[4 * h + 3]);
       }
 
-      // S0 <- Diag(Gamma_L) S0 + Kt^T delta over this wave's channels
+      // S0 <- Diag(Gamma_L) S0 + Kt^T delta over this wave's channels (delta split:
+      // slot i of lane (j, g) is token 4 i + g, where dv already has it)
+      uint32_t dw[8];
+      split_n<8>(dv, dw);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         v4f acc = {s[ct].x * cur.gl[ct].x, s[ct].y * cur.gl[ct].y, s[ct].z * cur.gl[ct].z, s[ct].w * cur.gl[ct].w};
-        const float kt[8] = {cur.kt[ct][0].x, cur.kt[ct][0].y, cur.kt[ct][0].z, cur.kt[ct][0].w,
-                             cur.kt[ct][1].x, cur.kt[ct][1].y, cur.kt[ct][1].z, cur.kt[ct][1].w};
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kt[ks], dv[ks], acc, 0, 0, 0);
+        acc = split_mma32(cur.kt[ct][0], cur.kt[ct][1], dw, acc);
         s[ct] = make_float4(acc[0], acc[1], acc[2], acc[3]);
       }
       load_gu(nxt, wn);

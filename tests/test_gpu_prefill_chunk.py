@@ -5,7 +5,11 @@ within 1e-3 relative Frobenius; slot handling and device errors bit-exact. The
 rows cover empty prompts, prompts shorter than, equal to and just past one
 32-token chunk, long prompts, checkpoints before the prompt, inside a chunk,
 on a chunk boundary and at the end, padding rows and extreme decays. The chunk
-form also agrees with kda_prefill (the recurrent form) to 1e-5.
+form also agrees with kda_prefill (the recurrent form, fp32 products) to
+REC_OUT_TOL in outputs and REC_STATE_TOL in states: its products with the
+state are taken as three bfloat16 products of split fp32 operands, each off
+by at most about 3 * 2^-18 (1.2e-5) of |a b|, and the two forms differ by
+that error.
 """
 
 import numpy as np
@@ -22,6 +26,8 @@ pytestmark = pytest.mark.gpu
 
 OUT_TOL = 1e-4
 STATE_TOL = 1e-3
+REC_OUT_TOL = 1e-4
+REC_STATE_TOL = 2e-5
 
 
 def _run(w, cache_d, *, slots=None, pos=None, dev_err=None, raw=False, out_dtype=torch.float32, chunked=True,
@@ -88,8 +94,8 @@ def test_chunked_prefill_matches_oracle(dk, dv):
 def test_chunked_prefill_b64_mixed_lengths():
     """64 rows of mixed prompt lengths (empty, shorter than a chunk, many chunks) with padding
     rows and checkpoints absent, at the start, inside a chunk, on a boundary and at the end:
-    every precompute workgroup finds its row through the chunk map. Against the oracle, and the
-    recurrent form to 1e-5."""
+    every precompute workgroup finds its row through the chunk map. Against the oracle and the
+    recurrent form."""
     rng = np.random.Generator(np.random.PCG64(74))
     seqlens = rng.choice([0, 1, 7, 31, 32, 33, 64, 95, 150, 260], 64).astype(int)
     w = synth.make(64, 8, 128, 128, seqlens=seqlens, num_slots=80, state_std=0.05, seed=75)
@@ -103,8 +109,8 @@ def test_chunked_prefill_b64_mixed_lengths():
     out_r, ckpt_r = _run(w, cache_r, slots=slots, pos=pos, chunked=False)
     torch.cuda.synchronize()
     live = np.concatenate([np.arange(w.cu_seqlens[b], w.cu_seqlens[b + 1]) for b in range(64) if slots[b] >= 0])
-    assert out_rel(out_c.cpu().numpy()[live], out_r.cpu().numpy()[live]) <= 1e-5
-    assert state_rel(cache_c.cpu().numpy(), cache_r.cpu().numpy()) <= 1e-5
+    assert out_rel(out_c.cpu().numpy()[live], out_r.cpu().numpy()[live], "outputs vs recurrent form") <= REC_OUT_TOL
+    assert state_rel(cache_c.cpu().numpy(), cache_r.cpu().numpy(), "states vs recurrent form") <= REC_STATE_TOL
     _check(w, slots, pos, out_c, ckpt_c, cache_c)
 
 
@@ -126,8 +132,8 @@ def test_chunked_prefill_more_rows_than_one_map_tile():
     out_r, ckpt_r = _run(w, cache_r, slots=slots, pos=pos, chunked=False)
     torch.cuda.synchronize()
     live = np.concatenate([np.arange(w.cu_seqlens[b], w.cu_seqlens[b + 1]) for b in range(B) if slots[b] >= 0])
-    assert out_rel(out_c.cpu().numpy()[live], out_r.cpu().numpy()[live]) <= 1e-5
-    assert state_rel(cache_c.cpu().numpy(), cache_r.cpu().numpy()) <= 1e-5
+    assert out_rel(out_c.cpu().numpy()[live], out_r.cpu().numpy()[live], "outputs vs recurrent form") <= REC_OUT_TOL
+    assert state_rel(cache_c.cpu().numpy(), cache_r.cpu().numpy(), "states vs recurrent form") <= REC_STATE_TOL
     _check(w, slots, pos, out_c, ckpt_c, cache_c)
 
 
@@ -139,8 +145,8 @@ def test_chunked_prefill_without_checkpoints_and_against_recurrent_form():
     out_c, _ = _run(w, cache_c)
     out_r, _ = _run(w, cache_r, chunked=False)
     torch.cuda.synchronize()
-    assert out_rel(out_c.cpu().numpy(), out_r.cpu().numpy()) <= 1e-5
-    assert state_rel(cache_c.cpu().numpy(), cache_r.cpu().numpy()) <= 1e-5
+    assert out_rel(out_c.cpu().numpy(), out_r.cpu().numpy(), "outputs vs recurrent form") <= REC_OUT_TOL
+    assert state_rel(cache_c.cpu().numpy(), cache_r.cpu().numpy(), "states vs recurrent form") <= REC_STATE_TOL
     _check(w, w.slot_ids, np.full(3, -1, np.int32), out_c, None, cache_c)
 
 
