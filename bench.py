@@ -494,6 +494,8 @@ def prefill_8k(D, K, synth, reps, tile_w=0, chunked=False):
                tflops=round(flops / ms / 1e9, 3), checkpoint_at=7680)
     if chunked:
         res["workspace_bytes"] = ws_bytes
+        # fp32 state; its products with W, [Gamma q] and Kt on bfloat16 MFMA, three per fp32 product
+        res["state_products"] = "bf16 MFMA, split fp32 operands (hi*hi + hi*lo + lo*hi)"
     else:
         res["tile_w"] = K.kda_query_variant(1, H, d, d, T_max=n, op=K.KDA_OP_PREFILL, tile_w=tile_w)[0]
     return res
