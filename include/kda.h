@@ -264,8 +264,14 @@ int kda_prefill(float *cache, int64_t num_slots, int64_t slot_stride,
  * chunk, the lower-triangular system of the delta rule solved once per chunk,
  * and the matrices that turn the chunk's effect on the state into dense
  * products. A second kernel runs each (row, head, 16 value columns) through its
- * chunks in order with those products on MFMA. Outputs and states agree with
- * kda_prefill to rounding (not bit for bit). Arguments, layouts, flags and
+ * chunks in order with those products on MFMA. The state is fp32 throughout,
+ * but its products with the chunk matrices are taken on the bfloat16 matrix
+ * cores as three products of split fp32 operands (hi = RNE(x), lo = RNE(x -
+ * hi)), each within about 1.2e-5 of |a||b|: outputs stay within 1e-4 relative
+ * L2 per (token, head) of the exact recurrence and states far within 1e-3
+ * relative Frobenius, where kda_prefill's products are fp32. Outputs and states
+ * therefore agree with kda_prefill to that accuracy (not bit for bit).
+ * Arguments, layouts, flags and
  * device errors are kda_prefill's; kda_options.tile_w may be 0 or 16.
  * workspace: device memory of at least kda_prefill_chunked_workspace() bytes,
  * 16-byte aligned, owned by the caller; its contents need no initialization
