@@ -323,7 +323,7 @@ int kda_prefill_chunked(float *cache, int64_t num_slots, int64_t slot_stride, co
   a.raw = f.raw;
   a.out_bf16 = f.out_bf16;
   void *args[] = {&a};
-  {
+  if (B > 1) {  // one row's chunks are numbered from 0 without the map
     const hipError_t e = hipLaunchKernel(prefill_chunk_map_kernel(), dim3(1), dim3(kChunkMapThreads), args, 0,
                                          (hipStream_t)stream);
     if (e != hipSuccess) return KDA_ERR_HIP;

@@ -265,11 +265,16 @@ __global__ __launch_bounds__(kChunkPrepThreads) void prefill_chunk_prep_kernel(C
   // memory-side cache when it starts (measured on MI355X: 4% off the state pass
   // of an 8000-token prompt).
   const int c = (int)(gridDim.x / a.H) - 1 - (int)(blockIdx.x / a.H), h = blockIdx.x % a.H;
-  // the row and chunk this workgroup prepares, from the chunk map
-  const int b = a.crow[c];
-  if (b < 0) return;
-  const int jc = c - a.cbase[b];
+  // the row and chunk this workgroup prepares, from the chunk map (a single row
+  // needs none: its chunks are numbered from 0)
+  int b = 0, jc = c;
+  if (a.B > 1) {
+    b = a.crow[c];
+    if (b < 0) return;
+    jc = c - a.cbase[b];
+  }
   const ChunkRow r = chunk_row(a, b);
+  if (jc >= r.nch) return;
   int t0, n;
   chunk_tokens(r, jc, t0, n);
   const int64_t row0 = (int64_t)a.cu[b] + t0;
@@ -690,7 +695,7 @@ __global__ __launch_bounds__(kChunkStateThreads) void prefill_chunk_state_kernel
     return;
   }
   const ChunkRow r = chunk_row(a, u.b);
-  const int cbase = a.cbase[u.b];
+  const int cbase = a.B > 1 ? a.cbase[u.b] : 0;
   if (cbase + r.nch > a.ws_chunks) {  // only with rows that overlap in cu_seqlens
     report(a.dev_err, u, KDA_DEVERR_SEQLEN);
     return;
