@@ -91,6 +91,24 @@ def test_chunked_prefill_matches_oracle(dk, dv):
     _check(w, slots, pos, out, ckpt, cache_d)
 
 
+@pytest.mark.parametrize("seed,B", [(81, 1), (82, 1), (83, 2), (84, 3)])
+def test_chunked_prefill_random_single_and_few_rows(seed, B):
+    """Seeded random shapes: one row (no chunk map launch) or a few rows of random lengths
+    around chunk multiples, random checkpoints (none, 0, inside, on a boundary, at the end),
+    random (dk, dv), against the oracle."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dk, dv = (int(x) for x in rng.choice([(128, 128), (64, 64), (64, 128), (128, 64)]))
+    lengths = [33, 63, 64, 65, 97, 200] if B == 1 else [1, 31, 32, 33, 63, 64, 65, 97, 200]
+    seqlens = [int(rng.choice(lengths)) for _ in range(B)]
+    w = synth.make(B, 2, dk, dv, seqlens=seqlens, num_slots=B + 1, state_std=0.05, seed=seed)
+    pos = np.array([int(rng.choice([-1, 0, n // 3, (n // 32) * 32, n])) for n in seqlens], np.int32)
+    cache_d = f32(w.cache)
+    log(f"chunked prefill seed {seed}: B={B} dk={dk} dv={dv} lengths {seqlens} checkpoints {pos.tolist()}")
+    out, ckpt = _run(w, cache_d, pos=pos)
+    torch.cuda.synchronize()
+    _check(w, w.slot_ids, pos, out, ckpt, cache_d)
+
+
 def test_chunked_prefill_b64_mixed_lengths():
     """64 rows of mixed prompt lengths (empty, shorter than a chunk, many chunks) with padding
     rows and checkpoints absent, at the start, inside a chunk, on a boundary and at the end:
